@@ -1,0 +1,37 @@
+"""CPU oracle for the DFlash draft step.
+
+TEST INFRASTRUCTURE ONLY.  This package is a plain, slow float64 NumPy
+restatement of what the draft step computes.  It exists to check the HIP path
+and shares no code with it.  Only the test suite, the smoke check in
+`__graft_entry__.py` and the CPU-baseline leg of `bench.py` may import it; the
+product path never does.
+
+Sources (web pages on the method; cited by page title and section):
+  * "DFlash 投机解码：块扩散草稿与 KV 注入" (caijizhuo.github.io): notation table,
+    section 二 "注意力模式", section 三 (KV injection, fusion equation),
+    section 四 (inference pseudocode; engineering note on cached projected KV).
+  * "DFlow 完全拆解" (pinghaoyang.com.cn): the fusion equation in the section on
+    DFlash's recomputation window; the accept/reject split in the opening section.
+  * DFlash system/training/deployment notes (blog.hotdry.top), section 2.
+
+Where the pages leave a step open, the reading taken is stated at the function.
+
+Parity status: every function here is pinned by tests under tests/ (closed
+forms, invariants, library-routine special cases, brute force on tiny inputs,
+and the worked examples stored under tests/golden/).  Forward values at the
+full model shapes are pinned only through those properties: the pages print no
+output values for any input.
+"""
+from .dflash import (  # noqa: F401
+    ContextCache,
+    OracleDrafter,
+    accept,
+    block_attention,
+    draft_block,
+    fuse_context,
+    project_context_kv,
+    rms_norm,
+    rope,
+    swiglu_ffn,
+    topk,
+)

@@ -1,0 +1,194 @@
+"""Seeded generators: weights, verifier hidden states, anchors, target tokens.
+
+Every tensor is filled in chunks of 2**20 elements; chunk c of tensor t draws
+standard normals (float32) from PCG64(SeedSequence([seed, t, c])).  Chunks are
+independent streams, so filling runs on a thread pool and the values do not
+depend on the thread count.  Weights and the mask embedding are N(0, 0.02);
+RMSNorm gains are 1 + N(0, 0.02); verifier features are N(0, 1).  bf16 storage
+rounds each float32 draw to nearest-even.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List, Sequence
+
+import numpy as np
+
+from .configs import Dims, GEOM_P_MEAN_6_5
+
+CHUNK = 1 << 20
+_HIDDEN_ROWS_PER_BLOCK = 64
+_POOL = None
+
+
+def _pool() -> ThreadPoolExecutor:
+    global _POOL
+    if _POOL is None:
+        n = min(16, os.cpu_count() or 1)
+        _POOL = ThreadPoolExecutor(max_workers=n)
+    return _POOL
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest-even), returned as uint16 bits."""
+    v = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).copy()
+    r = (v >> 16) & 1
+    r += 0x7FFF
+    v += r
+    v >>= 16
+    return v.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Exact upcast of bf16 bits to float32."""
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _fill(shape, keys: Sequence[int], scale: float, offset: float, dtype: str) -> np.ndarray:
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16 if dtype == "bf16" else np.float32)
+
+    def work(c):
+        s = c * CHUNK
+        e = min(n, s + CHUNK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(keys) + [c])))
+        x = rng.standard_normal(e - s, dtype=np.float32)
+        x *= np.float32(scale)
+        if offset:
+            x += np.float32(offset)
+        if dtype == "bf16":
+            v = x.view(np.uint32)
+            r = (v >> 16) & 1
+            r += 0x7FFF
+            v += r
+            v >>= 16
+            out[s:e] = v
+        else:
+            out[s:e] = x
+
+    nch = (n + CHUNK - 1) // CHUNK
+    if nch <= 2:
+        for c in range(nch):
+            work(c)
+    else:
+        list(_pool().map(work, range(nch)))
+    return out.reshape(shape)
+
+
+LAYER_KEYS = ("g_attn", "w_q", "w_kb", "w_vb", "w_kc", "w_vc", "w_o",
+              "g_ffn", "w_gate", "w_up", "w_down")
+
+
+def layer_shapes(d: Dims) -> Dict[str, tuple]:
+    return {
+        "g_attn": (d.D,),
+        "w_q": (d.Hq * d.hd, d.D),
+        "w_kb": (d.Hkv * d.hd, d.D),
+        "w_vb": (d.Hkv * d.hd, d.D),
+        "w_kc": (d.Hkv * d.hd, d.D),
+        "w_vc": (d.Hkv * d.hd, d.D),
+        "w_o": (d.D, d.Hq * d.hd),
+        "g_ffn": (d.D,),
+        "w_gate": (d.I, d.D),
+        "w_up": (d.I, d.D),
+        "w_down": (d.D, d.I),
+    }
+
+
+def make_weights(d: Dims, seed: int) -> dict:
+    """Synthetic drafter weights in storage dtype (fp32 arrays or bf16 bits).
+
+    Tensor order (the tensor index t in the chunk seed): w_c, g_c, embed,
+    e_mask, g_final, then for each layer the LAYER_KEYS order.  The LM head is
+    tied to the embedding.
+    """
+    s = 1000 + seed
+    t = [0]
+
+    def nxt(shape, gain=False):
+        a = _fill(shape, [s, t[0]], 0.02, 1.0 if gain else 0.0, d.dtype)
+        t[0] += 1
+        return a
+
+    w = {}
+    w["w_c"] = nxt((d.D, d.L * d.Dt))
+    w["g_c"] = nxt((d.D,), gain=True)
+    w["embed"] = nxt((d.V, d.D))
+    w["e_mask"] = nxt((d.D,))
+    w["g_final"] = nxt((d.D,), gain=True)
+    w["w_lm"] = w["embed"]
+    shapes = layer_shapes(d)
+    layers = []
+    for _ in range(d.N):
+        lw = {}
+        for k in LAYER_KEYS:
+            lw[k] = nxt(shapes[k], gain=k.startswith("g_"))
+        layers.append(lw)
+    w["layers"] = layers
+    return w
+
+
+def weights_as_f32(w: dict) -> dict:
+    """Exact float32 view of the stored weights (bf16 bits are upcast)."""
+    def cv(a):
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+    out = {k: cv(v) for k, v in w.items() if k not in ("layers", "w_lm")}
+    out["w_lm"] = out["embed"] if w["w_lm"] is w["embed"] else cv(w["w_lm"])
+    out["layers"] = [{k: cv(v) for k, v in lw.items()} for lw in w["layers"]]
+    return out
+
+
+def make_hidden(d: Dims, seed: int, req: int, start: int, n: int) -> List[np.ndarray]:
+    """Verifier hidden states of request `req`, rows start..start+n-1, one array
+    [n, Dt] per tapped layer.  Row values depend only on (seed, req, layer, row)."""
+    out = []
+    R = _HIDDEN_ROWS_PER_BLOCK
+    for l in range(d.L):
+        rows = []
+        b0, b1 = start // R, (start + n + R - 1) // R
+        for b in range(b0, b1):
+            blk = _fill((R, d.Dt), [2000 + seed, 77, req, l, b], 1.0, 0.0, d.dtype)
+            lo = max(start, b * R) - b * R
+            hi = min(start + n, (b + 1) * R) - b * R
+            rows.append(blk[lo:hi])
+        arr = np.concatenate(rows, axis=0) if rows else np.zeros((0, d.Dt),
+                                                                  np.uint16 if d.dtype == "bf16" else np.float32)
+        out.append(np.ascontiguousarray(arr))
+    return out
+
+
+def make_anchors(d: Dims, seed: int, bs: int) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([2000 + seed, 5])))
+    return rng.integers(0, d.V, size=bs).astype(np.int32)
+
+
+def draw_first_mismatch(kind: str, bs: int, B: int, seed: int) -> np.ndarray:
+    """First mismatch position m per request, m in 0..B-1 (tau = m + 1).
+
+    kind "uniform": m ~ U{0..B-1}; kind "geometric": tau = min(Geom(p), B)
+    with p chosen so the clamped mean is 6.5."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([3000 + seed, 1])))
+    if kind == "uniform":
+        return rng.integers(0, B, size=bs).astype(np.int32)
+    if kind == "geometric":
+        tau = np.minimum(rng.geometric(GEOM_P_MEAN_6_5, size=bs), B)
+        return (tau - 1).astype(np.int32)
+    raise KeyError(kind)
+
+
+def make_targets(cand: np.ndarray, m: np.ndarray, V: int, seed: int) -> np.ndarray:
+    """Verifier argmax tokens t [bs, B] built so the first mismatch with the
+    candidates c [bs, B-1] sits at m: t_j = c_{j+1} for j < m, t_m differs from
+    c_{m+1} (when m < B-1), all other entries uniform."""
+    bs, Bm1 = cand.shape
+    B = Bm1 + 1
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([3000 + seed, 2])))
+    t = rng.integers(0, V, size=(bs, B)).astype(np.int64)
+    shift = rng.integers(0, V - 1, size=bs)
+    for r in range(bs):
+        mr = int(m[r])
+        t[r, :mr] = cand[r, :mr]
+        if mr < B - 1:
+            t[r, mr] = (int(cand[r, mr]) + 1 + int(shift[r])) % V
+    return t.astype(np.int32)

@@ -1,0 +1,201 @@
+"""Python binding of libdflash_fuse.so, the MI355X (gfx950) DFlash draft step.
+
+Argument marshalling only: every step of the draft runs in the HIP kernels of
+the shared library.  PyTorch provides device memory and the stream.  The names
+mirror the C ABI in include/dflash_fuse.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdflash_fuse.so")
+
+DFLASH_F32, DFLASH_BF16 = 0, 1
+STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",
+          -3: "DFLASH_ECAPACITY", -4: "DFLASH_EHIP"}
+
+EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fuse_ctx",
+            "dflash_draft_block", "dflash_accept", "dflash_slot_reset", "dflash_slot_len",
+            "dflash_read_cache", "dflash_strerror", "dflash_last_error")
+
+
+class DflashError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({detail})")
+        self.code = code
+
+
+class dflash_dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("dtype", "D", "L", "Dt", "N", "Hq", "Hkv", "hd", "I", "V", "B",
+                 "max_ctx", "max_slots", "max_batch")] + [
+        ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float), ("use_rope", ctypes.c_int32)]
+
+
+LAYER_FIELDS = ("g_attn", "w_q", "w_kb", "w_vb", "w_kc", "w_vc", "w_o", "g_ffn", "w_gate",
+                "w_up", "w_down")
+
+
+class dflash_layer_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
+
+
+class dflash_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w_c", "g_c", "embed", "e_mask", "g_final", "w_lm")] + [
+        ("layers", ctypes.POINTER(dflash_layer_weights))]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; fails loudly when it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or `python block_diffusion_drafter_fuse_amd/build.py`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    P = ctypes.POINTER
+    L.dflash_query_sizes.argtypes = [P(dflash_dims), P(sz), P(sz)]
+    L.dflash_create.argtypes = [P(dflash_dims), P(dflash_weights), vp, sz, vp, sz, P(vp)]
+    L.dflash_destroy.argtypes = [vp]
+    L.dflash_destroy.restype = None
+    L.dflash_fuse_ctx.argtypes = [vp, vp, i32, P(i32), P(i32), P(vp)]
+    L.dflash_draft_block.argtypes = [vp, vp, i32, P(i32), vp, i32, vp, vp, vp]
+    L.dflash_accept.argtypes = [vp, i32, i32, vp, i32, vp, vp, vp]
+    L.dflash_slot_reset.argtypes = [vp, i32, i32]
+    L.dflash_slot_len.argtypes = [vp, i32, P(i32)]
+    L.dflash_read_cache.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    L.dflash_strerror.argtypes = [ctypes.c_int]
+    L.dflash_strerror.restype = ctypes.c_char_p
+    L.dflash_last_error.argtypes = []
+    L.dflash_last_error.restype = ctypes.c_char_p
+    for n in EXPORTED:
+        if n not in ("dflash_destroy", "dflash_strerror", "dflash_last_error"):
+            getattr(L, n).restype = ctypes.c_int
+    _LIB = L
+    return L
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise DflashError(rc, where, lib().dflash_last_error().decode())
+
+
+def make_dims(d, max_ctx: int, max_slots: int, max_batch: int) -> dflash_dims:
+    """C dims from any object with the model fields (D, L, Dt, N, Hq, Hkv, hd, I,
+    V, B, rope_base, rms_eps, use_rope, dtype in {"f32", "bf16"})."""
+    return dflash_dims(DFLASH_BF16 if d.dtype == "bf16" else DFLASH_F32, d.D, d.L, d.Dt, d.N,
+                       d.Hq, d.Hkv, d.hd, d.I, d.V, d.B, max_ctx, max_slots, max_batch,
+                       float(d.rope_base), float(d.rms_eps), int(bool(d.use_rope)))
+
+
+def query_sizes(dims: dflash_dims):
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().dflash_query_sizes(ctypes.byref(dims), ctypes.byref(a), ctypes.byref(b)),
+           "dflash_query_sizes")
+    return a.value, b.value
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    """Upload a storage-dtype array (float32, or uint16 bf16 bits)."""
+    import torch
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _i32(xs: Sequence[int]):
+    arr = (ctypes.c_int32 * max(1, len(xs)))(*[int(x) for x in xs])
+    return arr
+
+
+class Drafter:
+    """One dflash_ctx over caller-owned (torch) device buffers."""
+
+    def __init__(self, d, weights: dict, max_ctx: int, max_slots: int, max_batch: int,
+                 device="cuda"):
+        import torch
+        self.d = d
+        self.device = device
+        self.dims = make_dims(d, max_ctx, max_slots, max_batch)
+        pool_b, ws_b = query_sizes(self.dims)
+        self.pool = torch.empty(pool_b, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(ws_b, dtype=torch.uint8, device=device)
+        self.w = weights  # keep tensors alive
+        layers = (dflash_layer_weights * d.N)()
+        for l in range(d.N):
+            for n in LAYER_FIELDS:
+                setattr(layers[l], n, _ptr(weights["layers"][l][n]))
+        self._layers = layers
+        cw = dflash_weights(_ptr(weights["w_c"]), _ptr(weights["g_c"]), _ptr(weights["embed"]),
+                            _ptr(weights["e_mask"]), _ptr(weights["g_final"]), _ptr(weights["w_lm"]),
+                            layers)
+        h = ctypes.c_void_p()
+        _check(lib().dflash_create(ctypes.byref(self.dims), ctypes.byref(cw), _ptr(self.pool), pool_b,
+                                   _ptr(self.ws), ws_b, ctypes.byref(h)), "dflash_create")
+        self.h = h
+
+    @staticmethod
+    def upload_weights(w_np: dict, device="cuda") -> dict:
+        out = {k: to_device(v, device) for k, v in w_np.items() if k not in ("layers", "w_lm")}
+        out["w_lm"] = out["embed"] if w_np["w_lm"] is w_np["embed"] else to_device(w_np["w_lm"], device)
+        out["layers"] = [{k: to_device(v, device) for k, v in lw.items()} for lw in w_np["layers"]]
+        return out
+
+    def close(self):
+        if getattr(self, "h", None) and self.h.value:
+            lib().dflash_destroy(self.h)
+            self.h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def fuse_ctx(self, slots: Sequence[int], n_new: Sequence[int], hidden: Sequence, stream=None):
+        ptrs = (ctypes.c_void_p * max(1, len(hidden)))(*[_ptr(t) for t in hidden])
+        _check(lib().dflash_fuse_ctx(self.h, _stream(stream), len(slots), _i32(slots), _i32(n_new), ptrs),
+               "dflash_fuse_ctx")
+
+    def draft_block(self, slots: Sequence[int], anchor, top_k: int, out_ids, out_vals=None,
+                    out_logits=None, stream=None):
+        _check(lib().dflash_draft_block(self.h, _stream(stream), len(slots), _i32(slots), _ptr(anchor),
+                                        int(top_k), _ptr(out_ids), _ptr(out_vals), _ptr(out_logits)),
+               "dflash_draft_block")
+
+    def slot_reset(self, slot: int, keep_len: int):
+        _check(lib().dflash_slot_reset(self.h, int(slot), int(keep_len)), "dflash_slot_reset")
+
+    def slot_len(self, slot: int) -> int:
+        v = ctypes.c_int32()
+        _check(lib().dflash_slot_len(self.h, int(slot), ctypes.byref(v)), "dflash_slot_len")
+        return v.value
+
+    def read_cache(self, slot: int, layer: int, pos0: int, n: int, k_out, v_out, stream=None):
+        _check(lib().dflash_read_cache(self.h, _stream(stream), int(slot), int(layer), int(pos0), int(n),
+                                       _ptr(k_out), _ptr(v_out)), "dflash_read_cache")
+
+
+def accept(n_req: int, B: int, cand, cand_stride: int, target, tau, bonus, stream=None):
+    _check(lib().dflash_accept(_stream(stream), int(n_req), int(B), _ptr(cand), int(cand_stride),
+                               _ptr(target), _ptr(tau), _ptr(bonus)), "dflash_accept")

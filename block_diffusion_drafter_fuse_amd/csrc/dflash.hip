@@ -1,0 +1,662 @@
+// Host side of the DFlash draft-step library: argument validation, buffer
+// carving, launch planning and the C ABI declared in include/dflash_fuse.h.
+//
+// One launch sequence per call, all on the caller's stream:
+//   fuse_ctx:   [fusion GEMM -> RMSNorm -> context K/V GEMM with RoPE + cache append] per row chunk
+//   draft:      embed, then per layer {RMSNorm, QKV GEMM (+RoPE), attention,
+//               O GEMM (+residual), RMSNorm, gate/up GEMM (+SwiGLU), down GEMM
+//               (+residual)}, final RMSNorm, LM head with top-k, top-k merge
+//   accept:     one scan kernel
+// Per-call request metadata travels in kernel arguments (no host-to-device
+// copies), so a call sequence can be captured in a HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dflash_fuse.h"
+#include "attention.h"
+#include "common.h"
+#include "gemm.h"
+#include "lmhead.h"
+#include "misc.h"
+
+using namespace dfl;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+constexpr size_t kAlign = 256;
+constexpr int kFuseChunk = 1024;      // rows per fusion GEMM launch
+constexpr int kAttnWorkMax = 4096;    // attention split work items per call
+constexpr int kLmTargetWG = 2048;     // LM-head work-groups aimed for
+constexpr int kLmWV = 4;              // waves per LM-head work-group
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+struct Plan {
+  // pool
+  size_t kv_off, rope_off, ctr_off, pool_bytes;
+  size_t head_stride, kv_stride, layer_stride, slot_stride;  // elements
+  int ctx_pad;
+  // workspace
+  size_t x_off, u_off, q_off, kb_off, vbt_off, o_off, h_off, ufin_off;
+  size_t po_off, pml_off, lmv_off, lmi_off, z_off, hc_off, ws_bytes;
+  int BP;
+  size_t lm_entries;
+  int qf;
+};
+
+int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
+
+int lm_rows_per_wg(int M) { return M <= 16 ? 16 : 64; }
+
+void lm_shape(int M, int V, int* tpw, int* nchunk, int* rowblocks) {
+  const int rpw = lm_rows_per_wg(M);
+  *rowblocks = ceil_div(M, rpw);
+  const int ntiles = V / 16;
+  const int chunks_target = std::max(1, kLmTargetWG / *rowblocks);
+  *tpw = std::max(1, ceil_div(ntiles, kLmWV * chunks_target));
+  *nchunk = ceil_div(ntiles, kLmWV * *tpw);
+}
+
+int validate_dims(const dflash_dims* d) {
+  if (!d) return fail(DFLASH_EINVAL, "dims is NULL");
+  if (d->dtype != DFLASH_F32 && d->dtype != DFLASH_BF16)
+    return fail(DFLASH_EUNSUPPORTED, "dtype must be DFLASH_F32 or DFLASH_BF16");
+  const int vals[] = {d->D, d->L, d->Dt, d->N, d->Hq, d->Hkv, d->hd, d->I, d->V, d->B,
+                      d->max_ctx, d->max_slots, d->max_batch};
+  for (int v : vals)
+    if (v <= 0) return fail(DFLASH_EINVAL, "all dimensions must be positive");
+  if (d->hd != 64 && d->hd != 128) return fail(DFLASH_EUNSUPPORTED, "head dim must be 64 or 128");
+  if (d->B < 2 || d->B > 16) return fail(DFLASH_EUNSUPPORTED, "block size must be in 2..16");
+  if (d->N > kMaxLayers) return fail(DFLASH_EUNSUPPORTED, "at most 16 drafter layers");
+  if (d->L > kMaxKSeg) return fail(DFLASH_EUNSUPPORTED, "at most 16 tapped target layers");
+  if (d->max_batch > kMaxReq) return fail(DFLASH_EUNSUPPORTED, "max_batch must be <= 64");
+  if (d->Hq % d->Hkv) return fail(DFLASH_EINVAL, "Hq must be a multiple of Hkv");
+  if ((d->Hq / d->Hkv) * d->B > 64)
+    return fail(DFLASH_EUNSUPPORTED, "(Hq/Hkv)*B must be <= 64 (query rows per KV head)");
+  if (d->D % 32 || d->Dt % 32 || d->I % 32)
+    return fail(DFLASH_EUNSUPPORTED, "D, Dt and I must be multiples of 32");
+  if (d->V % 16) return fail(DFLASH_EUNSUPPORTED, "V must be a multiple of 16");
+  if (!(d->rms_eps >= 0.f) || !(d->rope_base > 0.f))
+    return fail(DFLASH_EINVAL, "rms_eps must be >= 0 and rope_base > 0");
+  if ((long long)d->max_ctx > (1 << 24)) return fail(DFLASH_EUNSUPPORTED, "max_ctx too large");
+  return DFLASH_OK;
+}
+
+void make_plan(const dflash_dims* d, Plan* p) {
+  const size_t e = elt_size(d->dtype);
+  const int KS = d->dtype == DFLASH_BF16 ? 32 : 16;
+  p->ctx_pad = round_up(d->max_ctx, 64);
+  p->head_stride = (size_t)p->ctx_pad * d->hd;
+  p->kv_stride = p->head_stride * d->Hkv;
+  p->layer_stride = 2 * p->kv_stride;
+  p->slot_stride = p->layer_stride * d->N;
+  size_t off = 0;
+  p->kv_off = off;
+  off = align_up(off + p->slot_stride * d->max_slots * e);
+  p->rope_off = off;
+  off = align_up(off + (size_t)(d->max_ctx + d->B) * (d->hd / 2) * sizeof(float2));
+  p->ctr_off = off;
+  off = align_up(off + (size_t)kMaxReq * d->Hkv * sizeof(int));
+  p->pool_bytes = off;
+
+  const int M = d->max_batch * d->B;
+  const int Mlm = d->max_batch * (d->B - 1);
+  p->BP = round_up(d->B, KS);
+  p->qf = ceil_div((d->Hq / d->Hkv) * d->B, 16);
+  if (p->qf == 3) p->qf = 4;
+  off = 0;
+  p->x_off = off;    off = align_up(off + (size_t)M * d->D * 4);
+  p->u_off = off;    off = align_up(off + (size_t)M * d->D * e);
+  p->q_off = off;    off = align_up(off + (size_t)M * d->Hq * d->hd * e);
+  p->kb_off = off;   off = align_up(off + (size_t)M * d->Hkv * d->hd * e);
+  p->vbt_off = off;  off = align_up(off + (size_t)d->max_batch * d->Hkv * d->hd * p->BP * e);
+  p->o_off = off;    off = align_up(off + (size_t)M * d->Hq * d->hd * e);
+  p->h_off = off;    off = align_up(off + (size_t)M * d->I * e);
+  p->ufin_off = off; off = align_up(off + (size_t)Mlm * d->D * e);
+  const int qr = p->qf * 16;
+  p->po_off = off;   off = align_up(off + (size_t)kAttnWorkMax * qr * d->hd * 4);
+  p->pml_off = off;  off = align_up(off + (size_t)kAttnWorkMax * qr * 2 * 4);
+  size_t lm = 0;
+  for (int m = 1; m <= Mlm; ++m) {
+    int tpw, nchunk, rb;
+    lm_shape(m, d->V, &tpw, &nchunk, &rb);
+    lm = std::max(lm, (size_t)nchunk * m * 16);
+  }
+  p->lm_entries = lm;
+  p->lmv_off = off;  off = align_up(off + lm * 4);
+  p->lmi_off = off;  off = align_up(off + lm * 4);
+  p->z_off = off;    off = align_up(off + (size_t)kFuseChunk * d->D * 4);
+  p->hc_off = off;   off = align_up(off + (size_t)kFuseChunk * d->D * e);
+  p->ws_bytes = off;
+}
+
+bool hip_ok(hipError_t e, const char* what, int* rc) {
+  if (e == hipSuccess) return true;
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  *rc = DFLASH_EHIP;
+  return false;
+}
+
+}  // namespace
+
+struct dflash_ctx {
+  dflash_dims d;
+  dflash_weights w;
+  std::vector<dflash_layer_weights> layers;
+  Plan p;
+  char* pool;
+  char* ws;
+  std::vector<int> len;
+  template <typename T> T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
+};
+
+namespace {
+
+// ------------------------------------------------------------------ launches
+
+template <typename T, class Epi>
+void launch_gemm(const WOperand<T>& w, const AOperand<T>& a, const Epi& epi, hipStream_t st) {
+  if (a.M <= 0 || w.ngroups <= 0) return;
+  if (a.M <= 32) {
+    constexpr int FM = 1, FN = Epi::kPaired ? 2 : 1, WM = 1, WN = 1, WK = 4, U = 8;
+    const int tiles_n = ceil_div(w.ngroups, FN * WN);
+    const int tiles_m = ceil_div(a.M, 16 * FM * WM);
+    hipLaunchKernelGGL((gemm_kernel<T, FM, FN, WM, WN, WK, U, Epi>), dim3(tiles_n * tiles_m),
+                       dim3(64 * WM * WN * WK), 0, st, w, a, epi);
+  } else {
+    constexpr int FM = 4, FN = 4, WM = 2, WN = 2, WK = 1, U = 2;
+    const int tiles_n = ceil_div(w.ngroups, FN * WN);
+    const int tiles_m = ceil_div(a.M, 16 * FM * WM);
+    hipLaunchKernelGGL((gemm_kernel<T, FM, FN, WM, WN, WK, U, Epi>), dim3(tiles_n * tiles_m),
+                       dim3(64 * WM * WN * WK), 0, st, w, a, epi);
+  }
+}
+
+template <typename T>
+WOperand<T> wop(std::initializer_list<std::pair<const void*, int>> segs, int pair) {
+  WOperand<T> w{};
+  int end = 0, n = 0;
+  for (auto& s : segs) {
+    w.ptr[n] = static_cast<const T*>(s.first);
+    end += s.second;
+    w.end[n] = end;
+    ++n;
+  }
+  w.nseg = n;
+  w.pair = pair;
+  w.ngroups = end / 16;
+  return w;
+}
+
+template <typename T>
+AOperand<T> aop(const void* p, int M, int K) {
+  AOperand<T> a{};
+  a.ptr[0] = static_cast<const T*>(p);
+  a.nk = 1;
+  a.kseg = K;
+  a.lda = K;
+  a.M = M;
+  return a;
+}
+
+template <typename T>
+void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, const void* const* hid) {
+  const dflash_dims& d = c->d;
+  const Plan& p = c->p;
+  float* z = c->wsp<float>(p.z_off);
+  T* hc = c->wsp<T>(p.hc_off);
+  T* pool = reinterpret_cast<T*>(c->pool + p.kv_off);
+  const float2* rope = reinterpret_cast<const float2*>(c->pool + p.rope_off);
+
+  WOperand<T> wc = wop<T>({{c->w.w_c, d.D}}, 0);
+  WOperand<T> wkv{};
+  {
+    int end = 0, n = 0;
+    for (int l = 0; l < d.N; ++l) {
+      wkv.ptr[n] = static_cast<const T*>(c->layers[l].w_kc);
+      end += d.Hkv * d.hd;
+      wkv.end[n++] = end;
+      wkv.ptr[n] = static_cast<const T*>(c->layers[l].w_vc);
+      end += d.Hkv * d.hd;
+      wkv.end[n++] = end;
+    }
+    wkv.nseg = n;
+    wkv.pair = d.hd / 2;
+    wkv.ngroups = end / 16;
+  }
+  for (int base = 0; base < total; base += kFuseChunk) {
+    const int rows = std::min(kFuseChunk, total - base);
+    AOperand<T> a{};
+    for (int l = 0; l < d.L; ++l) a.ptr[l] = static_cast<const T*>(hid[l]) + (size_t)base * d.Dt;
+    a.nk = d.L;
+    a.kseg = d.Dt;
+    a.lda = d.Dt;
+    a.M = rows;
+    launch_gemm<T>(wc, a, EpiStoreF32{z, d.D}, st);
+    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(rows), dim3(256), 0, st, z,
+                       static_cast<const T*>(c->w.g_c), hc, d.D, d.rms_eps, 0, d.B);
+    EpiKVAppend<T> epi{};
+    epi.pool = pool;
+    epi.slot_stride = p.slot_stride;
+    epi.layer_stride = p.layer_stride;
+    epi.kv_stride = p.kv_stride;
+    epi.head_stride = p.head_stride;
+    epi.rope = rope;
+    epi.Hkv = d.Hkv;
+    epi.hd = d.hd;
+    epi.ctx_pad = p.ctx_pad;
+    epi.use_rope = d.use_rope;
+    epi.row_base = base;
+    epi.meta = fm;
+    launch_gemm<T>(wkv, aop<T>(hc, rows, d.D), epi, st);
+  }
+}
+
+template <typename T, int HD, int QF>
+void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
+  hipLaunchKernelGGL((attn_kernel<T, HD, QF>), dim3(work), dim3(64), 0, st, a);
+}
+
+template <typename T>
+void attn_dispatch(const AttnArgs<T>& a, int work, int hd, int qf, hipStream_t st) {
+  if (hd == 128) {
+    if (qf == 1) launch_attn<T, 128, 1>(a, work, st);
+    else if (qf == 2) launch_attn<T, 128, 2>(a, work, st);
+    else launch_attn<T, 128, 4>(a, work, st);
+  } else {
+    if (qf == 1) launch_attn<T, 64, 1>(a, work, st);
+    else if (qf == 2) launch_attn<T, 64, 2>(a, work, st);
+    else launch_attn<T, 64, 4>(a, work, st);
+  }
+}
+
+template <typename T, int FM, int KTOP>
+void launch_lm(const LmArgs<T>& a, int nchunk, int rowblocks, hipStream_t st) {
+  constexpr int U = FM == 1 ? 8 : 4;
+  hipLaunchKernelGGL((lmhead_kernel<T, FM, KTOP, kLmWV, U>), dim3(nchunk, rowblocks), dim3(64 * kLmWV),
+                     0, st, a);
+}
+
+struct AttnPlan {
+  int chunk, work;
+  AttnMeta meta;
+};
+
+int plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPlan* ap) {
+  const dflash_dims& d = c->d;
+  long long total = 0;
+  for (int r = 0; r < n_req; ++r) total += c->len[slot[r]];
+  int chunk = round_up((int)std::max<long long>(1, (total * d.Hkv + 1023) / 1024), 32);
+  chunk = std::max(chunk, 256);
+  for (;;) {
+    long long work = 0;
+    for (int r = 0; r < n_req; ++r) work += (long long)d.Hkv * (ceil_div(c->len[slot[r]], chunk) + 1);
+    if (work <= kAttnWorkMax) {
+      ap->chunk = chunk;
+      ap->work = (int)work;
+      break;
+    }
+    chunk *= 2;
+  }
+  AttnMeta& m = ap->meta;
+  memset(&m, 0, sizeof(m));
+  m.n_req = n_req;
+  int w = 0;
+  for (int r = 0; r < n_req; ++r) {
+    m.ctx[r] = c->len[slot[r]];
+    m.slot[r] = slot[r];
+    m.nsplit[r] = ceil_div(m.ctx[r], ap->chunk);
+    m.work0[r] = w;
+    w += d.Hkv * (m.nsplit[r] + 1);
+  }
+  m.work0[n_req] = w;
+  return DFLASH_OK;
+}
+
+template <typename T>
+void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, const int32_t* anchor,
+               int top_k, int32_t* out_ids, float* out_vals, float* out_logits, const AttnPlan& apl) {
+  const dflash_dims& d = c->d;
+  const Plan& p = c->p;
+  const int M = n_req * d.B;
+  const int Mlm = n_req * (d.B - 1);
+  float* x = c->wsp<float>(p.x_off);
+  T* u = c->wsp<T>(p.u_off);
+  T* q = c->wsp<T>(p.q_off);
+  T* kb = c->wsp<T>(p.kb_off);
+  T* vbT = c->wsp<T>(p.vbt_off);
+  T* o = c->wsp<T>(p.o_off);
+  T* h = c->wsp<T>(p.h_off);
+  T* ufin = c->wsp<T>(p.ufin_off);
+  const float2* rope = reinterpret_cast<const float2*>(c->pool + p.rope_off);
+
+  DraftMeta dm{};
+  dm.n_req = n_req;
+  dm.B = d.B;
+  for (int r = 0; r < n_req; ++r) dm.ctx[r] = c->len[slot[r]];
+
+  hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(c->w.embed),
+                     static_cast<const T*>(c->w.e_mask), anchor, d.B, d.D, d.V, x);
+
+  AttnArgs<T> aa{};
+  aa.q = q;
+  aa.kb = kb;
+  aa.vbT = vbT;
+  aa.o = o;
+  aa.pool = reinterpret_cast<const T*>(c->pool + p.kv_off);
+  aa.slot_stride = p.slot_stride;
+  aa.layer_stride = p.layer_stride;
+  aa.kv_stride = p.kv_stride;
+  aa.head_stride = p.head_stride;
+  aa.ctx_pad = p.ctx_pad;
+  aa.Hq = d.Hq;
+  aa.Hkv = d.Hkv;
+  aa.G = d.Hq / d.Hkv;
+  aa.B = d.B;
+  aa.BP = p.BP;
+  aa.chunk = apl.chunk;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.hd));
+  aa.part_o = c->wsp<float>(p.po_off);
+  aa.part_ml = c->wsp<float>(p.pml_off);
+  aa.counters = reinterpret_cast<int*>(c->pool + p.ctr_off);
+  aa.meta = apl.meta;
+
+  const int qd = d.Hq * d.hd, kd = d.Hkv * d.hd;
+  for (int l = 0; l < d.N; ++l) {
+    const dflash_layer_weights& lw = c->layers[l];
+    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
+                       static_cast<const T*>(lw.g_attn), u, d.D, d.rms_eps, 0, d.B);
+    EpiQKV<T> eq{};
+    eq.q = q;
+    eq.kb = kb;
+    eq.vbT = vbT;
+    eq.rope = rope;
+    eq.Hq = d.Hq;
+    eq.Hkv = d.Hkv;
+    eq.hd = d.hd;
+    eq.BP = p.BP;
+    eq.use_rope = d.use_rope;
+    eq.meta = dm;
+    launch_gemm<T>(wop<T>({{lw.w_q, qd}, {lw.w_kb, kd}, {lw.w_vb, kd}}, d.hd / 2), aop<T>(u, M, d.D), eq,
+                   st);
+    aa.layer = l;
+    attn_dispatch<T>(aa, apl.work, d.hd, p.qf, st);
+    launch_gemm<T>(wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), EpiResidual{x, d.D}, st);
+    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
+                       static_cast<const T*>(lw.g_ffn), u, d.D, d.rms_eps, 0, d.B);
+    launch_gemm<T>(wop<T>({{lw.w_gate, d.I}, {lw.w_up, d.I}}, d.I), aop<T>(u, M, d.D),
+                   EpiSwiGLU<T>{h, d.I}, st);
+    launch_gemm<T>(wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), EpiResidual{x, d.D}, st);
+  }
+  hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(Mlm), dim3(256), 0, st, x,
+                     static_cast<const T*>(c->w.g_final), ufin, d.D, d.rms_eps, 1, d.B);
+
+  int tpw, nchunk, rowblocks;
+  lm_shape(Mlm, d.V, &tpw, &nchunk, &rowblocks);
+  LmArgs<T> la{};
+  la.u = ufin;
+  la.w = static_cast<const T*>(c->w.w_lm);
+  la.M = Mlm;
+  la.V = d.V;
+  la.D = d.D;
+  la.tpw = tpw;
+  la.logits = out_logits;
+  la.part_v = c->wsp<float>(p.lmv_off);
+  la.part_i = c->wsp<int>(p.lmi_off);
+  const bool small = lm_rows_per_wg(Mlm) == 16;
+  if (top_k == 1) {
+    if (small) launch_lm<T, 1, 1>(la, nchunk, rowblocks, st);
+    else launch_lm<T, 4, 1>(la, nchunk, rowblocks, st);
+    hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i, nchunk,
+                       Mlm, top_k, out_ids, out_vals);
+  } else {
+    if (small) launch_lm<T, 1, 16>(la, nchunk, rowblocks, st);
+    else launch_lm<T, 4, 16>(la, nchunk, rowblocks, st);
+    hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i,
+                       nchunk, Mlm, top_k, out_ids, out_vals);
+  }
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+
+extern "C" {
+
+const char* dflash_strerror(int status) {
+  switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_EINVAL: return "invalid argument";
+    case DFLASH_EUNSUPPORTED: return "unsupported configuration";
+    case DFLASH_ECAPACITY: return "capacity exceeded";
+    case DFLASH_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* dflash_last_error(void) { return g_last_error.c_str(); }
+
+int dflash_query_sizes(const dflash_dims* dims, size_t* kv_pool_bytes, size_t* workspace_bytes) {
+  g_last_error.clear();
+  int rc = validate_dims(dims);
+  if (rc) return rc;
+  if (!kv_pool_bytes || !workspace_bytes) return fail(DFLASH_EINVAL, "output pointer is NULL");
+  Plan p;
+  make_plan(dims, &p);
+  *kv_pool_bytes = p.pool_bytes;
+  *workspace_bytes = p.ws_bytes;
+  return DFLASH_OK;
+}
+
+int dflash_create(const dflash_dims* dims, const dflash_weights* weights, void* kv_pool,
+                  size_t kv_pool_bytes, void* workspace, size_t workspace_bytes, dflash_ctx** out) {
+  g_last_error.clear();
+  int rc = validate_dims(dims);
+  if (rc) return rc;
+  if (!weights || !out || !kv_pool || !workspace) return fail(DFLASH_EINVAL, "NULL argument");
+  const void* top[] = {weights->w_c, weights->g_c, weights->embed, weights->e_mask, weights->g_final,
+                       weights->w_lm};
+  for (const void* t : top)
+    if (!t) return fail(DFLASH_EINVAL, "a model weight pointer is NULL");
+  if (!weights->layers) return fail(DFLASH_EINVAL, "layers array is NULL");
+  for (int l = 0; l < dims->N; ++l) {
+    const dflash_layer_weights& lw = weights->layers[l];
+    const void* lp[] = {lw.g_attn, lw.w_q, lw.w_kb, lw.w_vb, lw.w_kc, lw.w_vc,
+                        lw.w_o,    lw.g_ffn, lw.w_gate, lw.w_up, lw.w_down};
+    for (const void* t : lp)
+      if (!t) return fail(DFLASH_EINVAL, "a layer weight pointer is NULL (layer " + std::to_string(l) + ")");
+  }
+  if (((uintptr_t)kv_pool % kAlign) || ((uintptr_t)workspace % kAlign))
+    return fail(DFLASH_EINVAL, "kv_pool and workspace must be 256-byte aligned");
+  Plan p;
+  make_plan(dims, &p);
+  if (kv_pool_bytes < p.pool_bytes) return fail(DFLASH_ECAPACITY, "kv_pool smaller than required");
+  if (workspace_bytes < p.ws_bytes) return fail(DFLASH_ECAPACITY, "workspace smaller than required");
+
+  dflash_ctx* c = new dflash_ctx();
+  c->d = *dims;
+  c->w = *weights;
+  c->layers.assign(weights->layers, weights->layers + dims->N);
+  c->w.layers = nullptr;
+  c->p = p;
+  c->pool = static_cast<char*>(kv_pool);
+  c->ws = static_cast<char*>(workspace);
+  c->len.assign(dims->max_slots, 0);
+
+  rc = DFLASH_OK;
+  if (!hip_ok(hipMemsetAsync(kv_pool, 0, p.pool_bytes, nullptr), "hipMemsetAsync(pool)", &rc) ||
+      !hip_ok(hipMemsetAsync(workspace, 0, p.ws_bytes, nullptr), "hipMemsetAsync(workspace)", &rc)) {
+    delete c;
+    return rc;
+  }
+  const int half = dims->hd / 2;
+  const int npos = dims->max_ctx + dims->B;
+  const int total = npos * half;
+  hipLaunchKernelGGL(rope_table_kernel, dim3(ceil_div(total, 256)), dim3(256), 0, nullptr,
+                     reinterpret_cast<float2*>(c->pool + p.rope_off), npos, half, (double)dims->rope_base,
+                     dims->hd);
+  if (!hip_ok(hipGetLastError(), "rope table launch", &rc) ||
+      !hip_ok(hipStreamSynchronize(nullptr), "hipStreamSynchronize", &rc)) {
+    delete c;
+    return rc;
+  }
+  *out = c;
+  return DFLASH_OK;
+}
+
+void dflash_destroy(dflash_ctx* ctx) { delete ctx; }
+
+int dflash_slot_reset(dflash_ctx* ctx, int32_t slot, int32_t keep_len) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  if (slot < 0 || slot >= ctx->d.max_slots) return fail(DFLASH_ECAPACITY, "slot out of range");
+  if (keep_len < 0 || keep_len > ctx->len[slot])
+    return fail(DFLASH_EINVAL, "keep_len must be in 0..current length");
+  ctx->len[slot] = keep_len;
+  return DFLASH_OK;
+}
+
+int dflash_slot_len(const dflash_ctx* ctx, int32_t slot, int32_t* len) {
+  g_last_error.clear();
+  if (!ctx || !len) return fail(DFLASH_EINVAL, "NULL argument");
+  if (slot < 0 || slot >= ctx->d.max_slots) return fail(DFLASH_ECAPACITY, "slot out of range");
+  *len = ctx->len[slot];
+  return DFLASH_OK;
+}
+
+static int check_slots(const dflash_ctx* ctx, int32_t n_req, const int32_t* slot) {
+  if (n_req < 0) return fail(DFLASH_EINVAL, "n_req must be >= 0");
+  if (n_req > ctx->d.max_batch) return fail(DFLASH_ECAPACITY, "n_req exceeds max_batch");
+  if (n_req > 0 && !slot) return fail(DFLASH_EINVAL, "slot is NULL");
+  for (int r = 0; r < n_req; ++r) {
+    if (slot[r] < 0 || slot[r] >= ctx->d.max_slots) return fail(DFLASH_ECAPACITY, "slot out of range");
+    for (int q = 0; q < r; ++q)
+      if (slot[q] == slot[r]) return fail(DFLASH_EINVAL, "slots in one call must be distinct");
+  }
+  return DFLASH_OK;
+}
+
+int dflash_fuse_ctx(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot,
+                    const int32_t* n_new, const void* const* tgt_hidden) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  int rc = check_slots(ctx, n_req, slot);
+  if (rc) return rc;
+  if (n_req > 0 && !n_new) return fail(DFLASH_EINVAL, "n_new is NULL");
+  long long total = 0;
+  for (int r = 0; r < n_req; ++r) {
+    if (n_new[r] < 0) return fail(DFLASH_EINVAL, "n_new must be >= 0");
+    if ((long long)ctx->len[slot[r]] + n_new[r] > ctx->d.max_ctx)
+      return fail(DFLASH_ECAPACITY, "context would exceed max_ctx for slot " + std::to_string(slot[r]));
+    total += n_new[r];
+  }
+  if (total == 0) return DFLASH_OK;
+  if (total > (1LL << 30)) return fail(DFLASH_ECAPACITY, "too many rows in one call");
+  if (!tgt_hidden) return fail(DFLASH_EINVAL, "tgt_hidden is NULL");
+  for (int l = 0; l < ctx->d.L; ++l)
+    if (!tgt_hidden[l]) return fail(DFLASH_EINVAL, "a tgt_hidden layer pointer is NULL");
+
+  FuseMeta fm{};
+  fm.n_req = n_req;
+  int row = 0;
+  for (int r = 0; r < n_req; ++r) {
+    fm.row0[r] = row;
+    fm.pos0[r] = ctx->len[slot[r]];
+    fm.slot[r] = slot[r];
+    row += n_new[r];
+  }
+  fm.row0[n_req] = row;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ctx->d.dtype == DFLASH_BF16) run_fuse<bf16_t>(ctx, st, fm, (int)total, tgt_hidden);
+  else run_fuse<float>(ctx, st, fm, (int)total, tgt_hidden);
+  if (!hip_ok(hipGetLastError(), "fuse launch", &rc)) return rc;
+  for (int r = 0; r < n_req; ++r) ctx->len[slot[r]] += n_new[r];
+  return DFLASH_OK;
+}
+
+int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot,
+                       const int32_t* anchor, int32_t top_k, int32_t* out_ids, float* out_vals,
+                       float* out_logits) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  int rc = check_slots(ctx, n_req, slot);
+  if (rc) return rc;
+  if (top_k < 1 || top_k > 16) return fail(DFLASH_EUNSUPPORTED, "top_k must be in 1..16");
+  if (n_req == 0) return DFLASH_OK;
+  if (!anchor || !out_ids) return fail(DFLASH_EINVAL, "anchor and out_ids must not be NULL");
+  AttnPlan apl;
+  plan_attention(ctx, n_req, slot, &apl);
+  const int Mlm = n_req * (ctx->d.B - 1);
+  int tpw, nchunk, rb;
+  lm_shape(Mlm, ctx->d.V, &tpw, &nchunk, &rb);
+  if ((size_t)nchunk * Mlm * 16 > ctx->p.lm_entries)
+    return fail(DFLASH_ECAPACITY, "LM-head partial buffer too small");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ctx->d.dtype == DFLASH_BF16)
+    run_draft<bf16_t>(ctx, st, n_req, slot, anchor, top_k, out_ids, out_vals, out_logits, apl);
+  else
+    run_draft<float>(ctx, st, n_req, slot, anchor, top_k, out_ids, out_vals, out_logits, apl);
+  if (!hip_ok(hipGetLastError(), "draft launch", &rc)) return rc;
+  return DFLASH_OK;
+}
+
+int dflash_accept(void* stream, int32_t n_req, int32_t B, const int32_t* cand, int32_t cand_stride,
+                  const int32_t* target, int32_t* tau, int32_t* bonus) {
+  g_last_error.clear();
+  if (n_req < 0) return fail(DFLASH_EINVAL, "n_req must be >= 0");
+  if (B < 1) return fail(DFLASH_EINVAL, "B must be >= 1");
+  if (cand_stride < 1) return fail(DFLASH_EINVAL, "cand_stride must be >= 1");
+  if (n_req == 0) return DFLASH_OK;
+  if (!cand || !target || !tau || !bonus) return fail(DFLASH_EINVAL, "NULL argument");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(accept_kernel, dim3(ceil_div(n_req, 64)), dim3(64), 0, st, n_req, B, cand,
+                     cand_stride, target, tau, bonus);
+  int rc = DFLASH_OK;
+  if (!hip_ok(hipGetLastError(), "accept launch", &rc)) return rc;
+  return DFLASH_OK;
+}
+
+int dflash_read_cache(dflash_ctx* ctx, void* stream, int32_t slot, int32_t layer, int32_t pos0, int32_t n,
+                      float* k_out, float* v_out) {
+  g_last_error.clear();
+  if (!ctx || !k_out || !v_out) return fail(DFLASH_EINVAL, "NULL argument");
+  if (slot < 0 || slot >= ctx->d.max_slots) return fail(DFLASH_ECAPACITY, "slot out of range");
+  if (layer < 0 || layer >= ctx->d.N) return fail(DFLASH_EINVAL, "layer out of range");
+  if (pos0 < 0 || n < 0 || pos0 + n > ctx->len[slot]) return fail(DFLASH_EINVAL, "range beyond slot length");
+  if (n == 0) return DFLASH_OK;
+  const Plan& p = ctx->p;
+  const size_t e = elt_size(ctx->d.dtype);
+  const char* base = ctx->pool + p.kv_off + (slot * p.slot_stride + layer * p.layer_stride) * e;
+  const int total = ctx->d.Hkv * n * ctx->d.hd;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ctx->d.dtype == DFLASH_BF16)
+    hipLaunchKernelGGL(read_cache_kernel<bf16_t>, dim3(ceil_div(total, 256)), dim3(256), 0, st,
+                       reinterpret_cast<const bf16_t*>(base),
+                       reinterpret_cast<const bf16_t*>(base + p.kv_stride * e), p.head_stride, p.ctx_pad,
+                       ctx->d.hd, ctx->d.Hkv, pos0, n, k_out, v_out);
+  else
+    hipLaunchKernelGGL(read_cache_kernel<float>, dim3(ceil_div(total, 256)), dim3(256), 0, st,
+                       reinterpret_cast<const float*>(base),
+                       reinterpret_cast<const float*>(base + p.kv_stride * e), p.head_stride, p.ctx_pad,
+                       ctx->d.hd, ctx->d.Hkv, pos0, n, k_out, v_out);
+  int rc = DFLASH_OK;
+  if (!hip_ok(hipGetLastError(), "read_cache launch", &rc)) return rc;
+  return DFLASH_OK;
+}
+
+}  // extern "C"

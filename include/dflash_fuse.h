@@ -1,0 +1,199 @@
+/*
+ * dflash_fuse.h -- C ABI of the DFlash block-diffusion draft step on MI355X
+ * (gfx950).
+ *
+ * The draft step has three parts, each one entry point:
+ *
+ *   dflash_fuse_ctx     target-context fusion H_c = RMSNorm(W_c [H^(l1);...;H^(lL)])
+ *                       followed by the per-layer context projections
+ *                       K_c = RoPE(W_c^K H_c), V_c = W_c^V H_c, appended to a
+ *                       per-request cache ("DFlash 投机解码：块扩散草稿与 KV 注入",
+ *                       section 三 fusion equation; section 二 "注意力模式" for
+ *                       K_c/V_c; section 四 engineering note: the cache holds
+ *                       projected K/V, not raw H_c).
+ *   dflash_draft_block  one forward pass of the N drafter layers over the block
+ *                       [anchor, mask x (B-1)]: queries from the block only,
+ *                       keys/values [K_c; K_b] / [V_c; V_b], no mask, SwiGLU FFN,
+ *                       then the shared LM head with per-position top-k over
+ *                       block offsets 1..B-1 (same page, section 二 and the
+ *                       draft_forward / dflash_cycle pseudocode of section 四).
+ *   dflash_accept       greedy verification: longest prefix of candidates that
+ *                       match the verifier's argmax tokens, plus the bonus token;
+ *                       tau counts the bonus, 1 <= tau <= B (same page, notation
+ *                       table and section 四; "DFlow 完全拆解", opening section).
+ *
+ * Conventions
+ *   - Pointers are device pointers unless marked [host].
+ *   - Storage dtype is DFLASH_F32 (float) or DFLASH_BF16 (uint16_t bit
+ *     patterns, round-to-nearest-even).  Weights, RMSNorm gains and verifier
+ *     hidden states use the storage dtype; accumulation is always fp32 and the
+ *     residual stream is fp32.
+ *   - Every matrix is [out, in] row-major (the input index is contiguous).
+ *   - Ownership: all device memory (weights, the KV pool, the workspace,
+ *     inputs and outputs) belongs to the caller.  The library borrows the
+ *     weight, pool and workspace pointers for the lifetime of a dflash_ctx and
+ *     never allocates or frees device memory.
+ *   - Calls are asynchronous and ordered on the given stream (a hipStream_t
+ *     passed as void*; NULL is the default stream).  Kernel faults surface at
+ *     the caller's next synchronisation.
+ *   - Errors: every argument is validated before the first launch, so a call
+ *     that returns an error has enqueued nothing and changed no state.
+ *   - A dflash_ctx is not thread-safe; calls that share a ctx must be ordered
+ *     on one stream.
+ */
+#ifndef DFLASH_FUSE_H
+#define DFLASH_FUSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum dflash_dtype { DFLASH_F32 = 0, DFLASH_BF16 = 1 };
+
+enum dflash_status {
+  DFLASH_OK = 0,
+  DFLASH_EINVAL = -1,       /* null pointer, bad dimension or argument */
+  DFLASH_EUNSUPPORTED = -2, /* head_dim not 64/128, B > 16, top_k > 16, dtype */
+  DFLASH_ECAPACITY = -3,    /* slot out of range, context overflow, batch or buffer too small */
+  DFLASH_EHIP = -4          /* a HIP runtime call failed; see dflash_last_error() */
+};
+
+/* Model and capacity description. */
+typedef struct dflash_dims {
+  int32_t dtype;      /* enum dflash_dtype */
+  int32_t D;          /* drafter hidden size */
+  int32_t L;          /* number of tapped target layers */
+  int32_t Dt;         /* target hidden size per tapped layer */
+  int32_t N;          /* drafter layers (<= 16) */
+  int32_t Hq;         /* query heads */
+  int32_t Hkv;        /* key/value heads (Hq % Hkv == 0) */
+  int32_t hd;         /* head dim: 64 or 128 */
+  int32_t I;          /* SwiGLU intermediate size */
+  int32_t V;          /* vocabulary size */
+  int32_t B;          /* block size: anchor + (B-1) masks, 2..16 */
+  int32_t max_ctx;    /* context capacity per slot (fused tokens) */
+  int32_t max_slots;  /* number of request slots in the KV pool */
+  int32_t max_batch;  /* requests per call, 1..64 */
+  float rope_base;    /* RoPE base (e.g. 10000) */
+  float rms_eps;      /* RMSNorm epsilon (e.g. 1e-6) */
+  int32_t use_rope;   /* 1: rotate Q and K (rotate-half pairing), 0: no positions */
+} dflash_dims;
+
+/* Per-layer weights.  Shapes ([out, in]):
+ *   g_attn [D], w_q [Hq*hd, D], w_kb [Hkv*hd, D], w_vb [Hkv*hd, D],
+ *   w_kc [Hkv*hd, D], w_vc [Hkv*hd, D], w_o [D, Hq*hd],
+ *   g_ffn [D], w_gate [I, D], w_up [I, D], w_down [D, I].
+ * w_kc / w_vc project the fused context, w_kb / w_vb the block; they may alias. */
+typedef struct dflash_layer_weights {
+  const void* g_attn;
+  const void* w_q;
+  const void* w_kb;
+  const void* w_vb;
+  const void* w_kc;
+  const void* w_vc;
+  const void* w_o;
+  const void* g_ffn;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+} dflash_layer_weights;
+
+/* Model weights.  w_c [D, L*Dt] (fusion projection; the L tapped layers are
+ * concatenated along its input axis), g_c [D], embed [V, D] (token
+ * embedding), e_mask [D] (shared mask embedding), g_final [D], w_lm [V, D]
+ * (shared LM head; may alias embed).  `layers` is a [host] array of N
+ * entries, copied at dflash_create. */
+typedef struct dflash_weights {
+  const void* w_c;
+  const void* g_c;
+  const void* embed;
+  const void* e_mask;
+  const void* g_final;
+  const void* w_lm;
+  const dflash_layer_weights* layers;
+} dflash_weights;
+
+typedef struct dflash_ctx dflash_ctx;
+
+/* Byte sizes of the two caller-allocated device buffers for `dims`: the KV
+ * pool (projected context K/V of every slot, the RoPE table and a few
+ * counters; persistent) and the workspace (per-call scratch).  Pure host
+ * computation.  Returns DFLASH_OK or DFLASH_EINVAL / DFLASH_EUNSUPPORTED. */
+int dflash_query_sizes(const dflash_dims* dims, size_t* kv_pool_bytes, size_t* workspace_bytes);
+
+/* Create a context over caller-owned buffers.  kv_pool and workspace must be
+ * 256-byte aligned and at least the sizes dflash_query_sizes reports.  Clears
+ * both buffers and fills the RoPE table on the default stream, then waits.
+ * All slots start empty (length 0). */
+int dflash_create(const dflash_dims* dims, const dflash_weights* weights, void* kv_pool,
+                  size_t kv_pool_bytes, void* workspace, size_t workspace_bytes,
+                  dflash_ctx** out);
+
+void dflash_destroy(dflash_ctx* ctx);
+
+/* Context fusion and cache append.
+ *   slot [host, n_req]    distinct slot ids in 0..max_slots-1
+ *   n_new [host, n_req]   new verifier rows per request (>= 0)
+ *   tgt_hidden [host, L]  L device pointers, each [sum(n_new), Dt] in the
+ *                         storage dtype; rows grouped by request in `slot` order.
+ * Request r's rows are fused and their K/V written at absolute positions
+ * len(slot[r]) .. len(slot[r]) + n_new[r] - 1; then len(slot[r]) += n_new[r].
+ * ECAPACITY if a slot would exceed max_ctx.  Uses the workspace: calls that
+ * share a ctx must not overlap. */
+int dflash_fuse_ctx(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot,
+                    const int32_t* n_new, const void* const* tgt_hidden);
+
+/* Draft one block per request.
+ *   slot [host, n_req]     slot ids (distinct); the block of request r sits at
+ *                          absolute positions len(slot[r]) .. + B-1
+ *   anchor [n_req] int32   anchor token per request (device)
+ *   top_k                  1..16
+ *   out_ids [n_req, B-1, top_k] int32: per block offset 1..B-1, ids ordered by
+ *                          (logit descending, id ascending)
+ *   out_vals  nullable [n_req, B-1, top_k] float: the matching logits
+ *   out_logits nullable [n_req, B-1, V] float: all logits (debug)
+ * Slot lengths are not changed: the block's own K/V are transient. */
+int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot,
+                       const int32_t* anchor, int32_t top_k, int32_t* out_ids,
+                       float* out_vals, float* out_logits);
+
+/* Greedy acceptance (stateless).
+ *   cand [n_req, B-1] int32 with row stride cand_stride (>= 1) between block
+ *        offsets (pass top_k to read the top-1 column of out_ids)
+ *   target [n_req, B] int32: target[r][j] is the verifier's argmax after block
+ *        offset j (j = 0 is the anchor)
+ *   tau [n_req] int32 out:  n + 1 where n counts leading j with
+ *        cand[r][j] == target[r][j]
+ *   bonus [n_req] int32 out: target[r][n], the next anchor */
+int dflash_accept(void* stream, int32_t n_req, int32_t B, const int32_t* cand,
+                  int32_t cand_stride, const int32_t* target, int32_t* tau, int32_t* bonus);
+
+/* Rewind (or confirm) a slot: set its length to keep_len <= current length.
+ * Host-side bookkeeping only; cached entries past keep_len are ignored and
+ * overwritten by later appends. */
+int dflash_slot_reset(dflash_ctx* ctx, int32_t slot, int32_t keep_len);
+
+/* Current fused length of a slot. */
+int dflash_slot_len(const dflash_ctx* ctx, int32_t slot, int32_t* len);
+
+/* Copy the cached context keys and values of one slot and drafter layer,
+ * positions pos0 .. pos0+n-1 (all < the slot's length), into k_out / v_out,
+ * each [Hkv, n, hd] float (device).  Keys are stored already rotated at
+ * their absolute positions.  For inspection and tests. */
+int dflash_read_cache(dflash_ctx* ctx, void* stream, int32_t slot, int32_t layer, int32_t pos0,
+                      int32_t n, float* k_out, float* v_out);
+
+/* Static text for a status code. */
+const char* dflash_strerror(int status);
+
+/* Detail of the most recent failure on the calling thread ("" if none). */
+const char* dflash_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_FUSE_H */

@@ -15,7 +15,10 @@ F = np.float64
 
 
 def _f64(a) -> np.ndarray:
-    return np.asarray(a, dtype=F)
+    a = np.asarray(a)
+    if not np.issubdtype(a.dtype, np.floating):
+        raise TypeError("oracle inputs must be floating point (decode bf16 bit patterns first)")
+    return a.astype(F, copy=False)
 
 
 # --------------------------------------------------------------------------
@@ -44,7 +47,7 @@ def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     hd = x.shape[-1]
     half = hd // 2
     inv_freq = F(base) ** (-(np.arange(half, dtype=F) * 2.0) / hd)
-    ang = _f64(pos)[:, None] * inv_freq[None, :]          # [T, half]
+    ang = np.asarray(pos, dtype=F)[:, None] * inv_freq[None, :]   # [T, half]
     c, s = np.cos(ang), np.sin(ang)
     x1, x2 = x[..., :half], x[..., half:]
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)

@@ -7,6 +7,7 @@ exactly the arrays produced here.
 """
 from .configs import CONFIGS, Dims, Workload, get_config  # noqa: F401
 from .gen import (  # noqa: F401
+    as_f32,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
     make_anchors,

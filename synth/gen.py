@@ -139,22 +139,36 @@ def weights_as_f32(w: dict) -> dict:
     return out
 
 
+def as_f32(arrays):
+    """Exact float32 values of storage-dtype arrays (bf16 bits are upcast)."""
+    return [bf16_bits_to_f32(a) if a.dtype == np.uint16 else a for a in arrays]
+
+
 def make_hidden(d: Dims, seed: int, req: int, start: int, n: int) -> List[np.ndarray]:
     """Verifier hidden states of request `req`, rows start..start+n-1, one array
-    [n, Dt] per tapped layer.  Row values depend only on (seed, req, layer, row)."""
-    out = []
+    [n, Dt] per tapped layer.  Row values depend only on (seed, req, layer, row):
+    rows come in blocks of 64, block b of layer l drawn from the stream keyed
+    (2000+seed, 77, req, l, b)."""
     R = _HIDDEN_ROWS_PER_BLOCK
-    for l in range(d.L):
-        rows = []
-        b0, b1 = start // R, (start + n + R - 1) // R
-        for b in range(b0, b1):
-            blk = _fill((R, d.Dt), [2000 + seed, 77, req, l, b], 1.0, 0.0, d.dtype)
-            lo = max(start, b * R) - b * R
-            hi = min(start + n, (b + 1) * R) - b * R
-            rows.append(blk[lo:hi])
-        arr = np.concatenate(rows, axis=0) if rows else np.zeros((0, d.Dt),
-                                                                  np.uint16 if d.dtype == "bf16" else np.float32)
-        out.append(np.ascontiguousarray(arr))
+    dt = np.uint16 if d.dtype == "bf16" else np.float32
+    b0, b1 = start // R, (start + n + R - 1) // R
+    out = [np.empty((n, d.Dt), dt) for _ in range(d.L)]
+    if n == 0:
+        return out
+
+    def work(job):
+        l, b = job
+        blk = _fill((R, d.Dt), [2000 + seed, 77, req, l, b], 1.0, 0.0, d.dtype)
+        lo = max(start, b * R)
+        hi = min(start + n, (b + 1) * R)
+        out[l][lo - start:hi - start] = blk[lo - b * R:hi - b * R]
+
+    jobs = [(l, b) for l in range(d.L) for b in range(b0, b1)]
+    if len(jobs) <= 4:
+        for j in jobs:
+            work(j)
+    else:
+        list(_pool().map(work, jobs))
     return out
 
 

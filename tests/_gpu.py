@@ -1,0 +1,101 @@
+"""Helpers for the GPU parity tests: stage a seeded workload through the C ABI
+and run the oracle on the same inputs."""
+import sys
+
+import numpy as np
+
+import oracle
+import synth
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_inf(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def margin_mask(ref_logits, thr=0.05):
+    """Rows whose top-1 minus top-2 logit exceeds thr."""
+    s = np.sort(ref_logits, axis=1)
+    return (s[:, -1] - s[:, -2]) > thr
+
+
+def check_top1(ids_top1, ref_logits, thr=0.05):
+    ref_ids, _ = oracle.topk(ref_logits, 1)
+    mask = margin_mask(ref_logits, thr)
+    bad = np.nonzero(mask & (ids_top1 != ref_ids[:, 0]))[0]
+    return mask, bad
+
+
+def check_topk(ids, ref_logits, thr=0.05):
+    """Rank i is compared where both gaps around it exceed thr."""
+    k = ids.shape[1]
+    ref_ids, ref_vals = oracle.topk(ref_logits, k + 1)
+    gaps = ref_vals[:, :-1] - ref_vals[:, 1:]               # gap after rank i
+    before = np.concatenate([np.full((ids.shape[0], 1), np.inf), gaps[:, :-1]], axis=1)
+    cmp = (before > thr) & (gaps[:, :k] > thr)
+    bad = cmp & (ids != ref_ids[:, :k])
+    return cmp, np.argwhere(bad)
+
+
+def hidden_rows(d, seed, reqs_counts):
+    """Concatenate per-request hidden rows: reqs_counts = [(req, start, n)]."""
+    parts = [synth.make_hidden(d, seed, r, s, n) for r, s, n in reqs_counts]
+    return [np.ascontiguousarray(np.concatenate([p[l] for p in parts], axis=0)) for l in range(d.L)]
+
+
+class GpuDraft:
+    """A drafter over one workload's synthetic weights, driven through the C ABI."""
+
+    def __init__(self, d, w_np, max_ctx, max_slots, max_batch):
+        import torch
+        import block_diffusion_drafter_fuse_amd as dfa
+        self.torch = torch
+        self.dfa = dfa
+        self.d = d
+        self.w_dev = dfa.Drafter.upload_weights(w_np)
+        self.dr = dfa.Drafter(d, self.w_dev, max_ctx, max_slots, max_batch)
+
+    def fuse(self, slots, counts, hidden_np):
+        hid = [self.dfa.to_device(h) for h in hidden_np]
+        self.dr.fuse_ctx(slots, counts, hid)
+        self.torch.cuda.synchronize()
+
+    def draft(self, slots, anchors, top_k=1, logits=False):
+        torch = self.torch
+        n = len(slots)
+        B = self.d.B
+        anc = torch.tensor(np.asarray(anchors, dtype=np.int32), device="cuda")
+        ids = torch.full((n, B - 1, top_k), -1, dtype=torch.int32, device="cuda")
+        vals = torch.zeros((n, B - 1, top_k), dtype=torch.float32, device="cuda")
+        lg = torch.zeros((n, B - 1, self.d.V), dtype=torch.float32, device="cuda") if logits else None
+        self.dr.draft_block(slots, anc, top_k, ids, vals, lg)
+        torch.cuda.synchronize()
+        return (ids.cpu().numpy(), vals.cpu().numpy(), lg.cpu().numpy() if logits else None)
+
+    def read_cache(self, slot, layer, pos0, n):
+        torch = self.torch
+        k = torch.zeros((self.d.Hkv, n, self.d.hd), dtype=torch.float32, device="cuda")
+        v = torch.zeros_like(k)
+        self.dr.read_cache(slot, layer, pos0, n, k, v)
+        torch.cuda.synchronize()
+        return k.cpu().numpy(), v.cpu().numpy()
+
+    def accept(self, cand, cand_stride, target):
+        torch = self.torch
+        n = target.shape[0]
+        c = torch.tensor(np.ascontiguousarray(cand, dtype=np.int32), device="cuda")
+        t = torch.tensor(np.ascontiguousarray(target, dtype=np.int32), device="cuda")
+        tau = torch.zeros(n, dtype=torch.int32, device="cuda")
+        bonus = torch.zeros(n, dtype=torch.int32, device="cuda")
+        self.dfa.accept(n, target.shape[1], c, cand_stride, t, tau, bonus)
+        torch.cuda.synchronize()
+        return tau.cpu().numpy(), bonus.cpu().numpy()
+
+    def close(self):
+        self.dr.close()

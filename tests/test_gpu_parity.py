@@ -1,0 +1,253 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Tolerances: fp32 storage paths rel <= 1e-4 (max-norm); bf16 logits
+max|diff| <= 2e-2 * max|logit|; token ids compared wherever the oracle's
+top-1 minus top-2 logit margin exceeds 0.05; acceptance bit-exact."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.configs import QWEN3_4B, QWEN3_8B
+from tests._gpu import GpuDraft, check_top1, check_topk, hidden_rows, log, margin_mask, rel_inf
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+
+def _oracle_for(d, w_np, seed, reqs):
+    """reqs: list of (req_index, ctx).  Returns OracleDrafter with caches filled."""
+    o = oracle.OracleDrafter(synth.weights_as_f32(w_np), d)
+    for r, ctx in reqs:
+        if ctx:
+            o.fuse(r, synth.as_f32(synth.make_hidden(d, seed, r, 0, ctx)))
+    return o
+
+
+def _compare_request(gl, gids, ref_logits, d, tol_logit, label):
+    if d.dtype == "f32":
+        err = rel_inf(gl, ref_logits)
+        assert err <= 1e-4, f"{label}: logits rel err {err}"
+    else:
+        err = np.abs(gl - ref_logits).max() / np.abs(ref_logits).max()
+        assert err <= tol_logit, f"{label}: logits err {err}"
+    mask, bad = check_top1(gids[:, 0], ref_logits)
+    assert len(bad) == 0, f"{label}: top-1 mismatch at rows {bad} (margin-passing rows {mask.sum()})"
+    return err, mask
+
+
+# ------------------------------------------------------------------ tiny fp32
+
+@pytest.fixture(scope="module")
+def tiny():
+    wl = synth.get_config("tiny")
+    d = wl.dims
+    w_np = synth.make_weights(d, wl.seed)
+    return wl, d, w_np
+
+
+def test_gpu_tiny_full_step(tiny):
+    wl, d, w_np = tiny
+    log(f"case tiny full step: D={d.D} ctx={wl.ctx}")
+    g = GpuDraft(d, w_np, max_ctx=128, max_slots=2, max_batch=1)
+    hid = synth.make_hidden(d, wl.seed, 0, 0, 64)
+    g.fuse([1], [64], hid)
+    o = _oracle_for(d, w_np, wl.seed, [(0, 64)])
+    for l in range(d.N):
+        k, v = g.read_cache(1, l, 0, 64)
+        assert rel_inf(k, o.cache(0).K[l]) <= 1e-4
+        assert rel_inf(v, o.cache(0).V[l]) <= 1e-4
+    anchor = synth.make_anchors(d, wl.seed, 1)
+    ref = o.draft(0, int(anchor[0]))["logits"]
+    ids, vals, lg = g.draft([1], anchor, top_k=1, logits=True)
+    _compare_request(lg[0], ids[0], ref, d, 0, "tiny")
+    np.testing.assert_allclose(vals[0][:, 0], lg[0].max(axis=1), rtol=0, atol=0)
+    ids16, vals16, _ = g.draft([1], anchor, top_k=16)
+    cmp, bad = check_topk(ids16[0], ref)
+    assert len(bad) == 0, bad
+    assert rel_inf(vals16[0], np.take_along_axis(ref, ids16[0].astype(np.int64), 1)) <= 1e-4
+    # acceptance on GPU candidates with targets built from the oracle's
+    m = synth.draw_first_mismatch("uniform", 1, d.B, wl.seed)
+    ref_c, _ = oracle.topk(ref, 1)
+    tgt = synth.make_targets(ref_c[:, 0][None], m, d.V, wl.seed)
+    tau, bonus = g.accept(ids16, 16, tgt)
+    tau_ref, bonus_ref = oracle.accept(ref_c[:, 0], tgt[0])
+    mm = margin_mask(ref)
+    if mm[:min(tau_ref, d.B - 1)].all():
+        assert (tau[0], bonus[0]) == (tau_ref, bonus_ref)
+    g.close()
+
+
+def test_gpu_tiny_ragged_batch_and_rewind(tiny):
+    wl, d, w_np = tiny
+    log("case tiny ragged batch bs=5")
+    ctxs = [0, 1, 17, 64, 100]
+    first = [0, 1, 10, 30, 64]
+    slots = [4, 0, 3, 1, 2]
+    g = GpuDraft(d, w_np, max_ctx=160, max_slots=6, max_batch=5)
+    g.fuse(slots, first, hidden_rows(d, wl.seed, [(r, 0, first[r]) for r in range(5)]))
+    second = [c - f for c, f in zip(ctxs, first)]
+    g.fuse(slots, second, hidden_rows(d, wl.seed, [(r, first[r], second[r]) for r in range(5)]))
+    for r in range(5):
+        assert g.dr.slot_len(slots[r]) == ctxs[r]
+    o = _oracle_for(d, w_np, wl.seed, list(enumerate(ctxs)))
+    anchors = synth.make_anchors(d, wl.seed, 5)
+    ids, vals, lg = g.draft(slots, anchors, top_k=4, logits=True)
+    for r in range(5):
+        ref = o.draft(r, int(anchors[r]))["logits"]
+        _compare_request(lg[r], ids[r], ref, d, 0, f"tiny r{r}")
+        cmp, bad = check_topk(ids[r], ref)
+        assert len(bad) == 0
+        if ctxs[r]:
+            k, v = g.read_cache(slots[r], d.N - 1, 0, ctxs[r])
+            assert rel_inf(k, o.cache(r).K[d.N - 1]) <= 1e-4
+            assert rel_inf(v, o.cache(r).V[d.N - 1]) <= 1e-4
+    # rewind request 4 to 40 tokens and re-append 25 different rows
+    g.dr.slot_reset(slots[4], 40)
+    alt = hidden_rows(d, wl.seed + 100, [(4, 40, 25)])
+    g.fuse([slots[4]], [25], alt)
+    o.reset(4, 40)
+    o.fuse(4, synth.as_f32(alt))
+    ids2, _, lg2 = g.draft([slots[4]], anchors[4:5], top_k=1, logits=True)
+    ref2 = o.draft(4, int(anchors[4]))["logits"]
+    _compare_request(lg2[0], ids2[0], ref2, d, 0, "tiny rewind")
+    g.close()
+
+
+def test_gpu_tiny_deterministic(tiny):
+    wl, d, w_np = tiny
+    log("case tiny determinism")
+    g = GpuDraft(d, w_np, max_ctx=128, max_slots=2, max_batch=2)
+    g.fuse([0, 1], [64, 33], hidden_rows(d, wl.seed, [(0, 0, 64), (1, 0, 33)]))
+    a = synth.make_anchors(d, wl.seed, 2)
+    r1 = g.draft([0, 1], a, top_k=16, logits=True)
+    r2 = g.draft([0, 1], a, top_k=16, logits=True)
+    for x, y in zip(r1, r2):
+        assert np.array_equal(x, y)
+    g.close()
+
+
+def test_gpu_no_rope_identical_mask_outputs(tiny):
+    wl, d, w_np = tiny
+    log("case tiny use_rope=0")
+    d0 = dataclasses.replace(d, use_rope=False)
+    g = GpuDraft(d0, w_np, max_ctx=128, max_slots=1, max_batch=1)
+    g.fuse([0], [40], synth.make_hidden(d0, wl.seed, 0, 0, 40))
+    _, _, lg = g.draft([0], [5], top_k=1, logits=True)
+    for j in range(1, d.B - 1):
+        np.testing.assert_allclose(lg[0][j], lg[0][0], rtol=1e-6, atol=1e-6)
+    o = _oracle_for(d0, w_np, wl.seed, [(0, 40)])
+    assert rel_inf(lg[0], o.draft(0, 5)["logits"]) <= 1e-4
+    g.close()
+
+
+def test_gpu_block_size_two_and_empty_context(tiny):
+    wl, _, _ = tiny
+    d = dataclasses.replace(synth.get_config("tiny").dims, B=2)
+    log("case tiny B=2, ctx=0")
+    w_np = synth.make_weights(d, 9)
+    g = GpuDraft(d, w_np, max_ctx=64, max_slots=1, max_batch=1)
+    ids, _, lg = g.draft([0], [17], top_k=2, logits=True)
+    o = _oracle_for(d, w_np, 9, [])
+    ref = o.draft(0, 17)["logits"]
+    _compare_request(lg[0], ids[0], ref, d, 0, "B=2 ctx=0")
+    g.close()
+
+
+def test_gpu_capacity_errors_leave_state(tiny):
+    import block_diffusion_drafter_fuse_amd as dfa
+    wl, d, w_np = tiny
+    log("case capacity errors")
+    g = GpuDraft(d, w_np, max_ctx=64, max_slots=2, max_batch=1)
+    g.fuse([0], [60], synth.make_hidden(d, wl.seed, 0, 0, 60))
+    with pytest.raises(dfa.DflashError) as e:
+        g.fuse([0], [5], synth.make_hidden(d, wl.seed, 0, 60, 5))
+    assert e.value.code == -3 and g.dr.slot_len(0) == 60
+    with pytest.raises(dfa.DflashError) as e:
+        g.draft([0, 1], [1, 2])
+    assert e.value.code == -3
+    with pytest.raises(dfa.DflashError) as e:
+        g.draft([0], [1], top_k=17)
+    assert e.value.code == -2
+    with pytest.raises(dfa.DflashError):
+        g.dr.slot_reset(0, 61)
+    g.close()
+
+
+def test_gpu_accept_bitexact():
+    log("case accept")
+    rng = np.random.default_rng(0)
+    import block_diffusion_drafter_fuse_amd as dfa
+    for B, V, n in [(16, 5, 64), (8, 2, 33), (2, 3, 7), (16, 151936, 32)]:
+        for k in (1, 3):
+            cand_full = rng.integers(0, V, size=(n, B - 1, k)).astype(np.int32)
+            m = rng.integers(0, B, size=n)
+            tgt = synth.make_targets(cand_full[:, :, 0], m, V, 7)
+            c = torch.tensor(cand_full, device="cuda")
+            t = torch.tensor(tgt, device="cuda")
+            tau = torch.zeros(n, dtype=torch.int32, device="cuda")
+            bonus = torch.zeros(n, dtype=torch.int32, device="cuda")
+            dfa.accept(n, B, c, k, t, tau, bonus)
+            torch.cuda.synchronize()
+            for r in range(n):
+                assert (int(tau[r]), int(bonus[r])) == oracle.accept(cand_full[r, :, 0], tgt[r])
+                assert int(tau[r]) == m[r] + 1
+
+
+# ------------------------------------------------------------------ full size
+
+def _full_size_case(wl, sample_reqs, label):
+    d = wl.dims
+    log(f"case {label}: generating weights")
+    w_np = synth.make_weights(d, wl.seed)
+    bs = wl.bs
+    max_ctx = max(wl.ctx) + 16
+    g = GpuDraft(d, w_np, max_ctx=max_ctx, max_slots=bs, max_batch=bs)
+    slots = list(range(bs))
+    pre = [c - n for c, n in zip(wl.ctx, wl.n_new)]
+    log(f"case {label}: prefill {sum(pre)} rows")
+    for r in range(bs):   # per request keeps host memory bounded
+        if pre[r]:
+            g.fuse([r], [pre[r]], synth.make_hidden(d, wl.seed, r, 0, pre[r]))
+    log(f"case {label}: step fuse {sum(wl.n_new)} rows")
+    g.fuse(slots, wl.n_new, hidden_rows(d, wl.seed, [(r, pre[r], wl.n_new[r]) for r in range(bs)]))
+    anchors = synth.make_anchors(d, wl.seed, bs)
+    ids, vals, lg = g.draft(slots, anchors, top_k=1, logits=True)
+    log(f"case {label}: oracle on requests {sample_reqs}")
+    o = oracle.OracleDrafter(synth.weights_as_f32(w_np), d)
+    worst = 0.0
+    cover = []
+    for r in sample_reqs:
+        o.fuse(r, synth.as_f32(synth.make_hidden(d, wl.seed, r, 0, wl.ctx[r])))
+        for l in (0, d.N - 1):
+            n_chk = min(wl.ctx[r], 64)
+            pos0 = wl.ctx[r] - n_chk
+            k, v = g.read_cache(r, l, pos0, n_chk)
+            assert rel_inf(k, o.cache(r).K[l][:, pos0:]) <= 2e-2
+            assert rel_inf(v, o.cache(r).V[l][:, pos0:]) <= 2e-2
+        ref = o.draft(r, int(anchors[r]))["logits"]
+        err, mask = _compare_request(lg[r], ids[r], ref, d, 2e-2, f"{label} r{r}")
+        worst = max(worst, err)
+        cover.append(mask.mean())
+        o.caches.pop(r)
+    log(f"case {label}: worst logit err {worst:.3e}, margin coverage {np.mean(cover):.2f}")
+    g.close()
+
+
+def test_gpu_qwen3_4b_bs1():
+    _full_size_case(synth.get_config("qwen3_4b_bs1"), [0], "qwen3_4b_bs1")
+
+
+def test_gpu_qwen3_8b_bs1():
+    _full_size_case(synth.get_config("qwen3_8b_bs1"), [0], "qwen3_8b_bs1")
+
+
+def test_gpu_qwen3_8b_bs32_sampled():
+    wl = synth.get_config("qwen3_8b_bs32")
+    order = np.argsort(wl.ctx)
+    _full_size_case(wl, [int(order[0]), int(order[len(order) // 2])], "qwen3_8b_bs32")

@@ -1,0 +1,352 @@
+#!/usr/bin/env python3
+"""Throughput of the DFlash draft step on one MI355X.
+
+One step = dflash_fuse_ctx over the tokens each request committed in the
+previous round + dflash_draft_block (top-1 candidates for block offsets
+1..B-1) + dflash_accept, for every request of the batch, with all inputs
+already resident in HBM.  After each step the slot lengths are rewound on the
+host so every step has the same shape.
+
+Headline workload: Qwen3-8B-shaped drafter, bs 32 ragged (context ~ U{512..8192},
+previous-round tau ~ clamped geometric with mean 6.5), bf16 weights and inputs,
+seeded synthetic data.  The same line carries the bs 1 Qwen3-8B-shaped step
+(context 4096, 7 new tokens) under "bs1".  Metric: drafted tokens/s =
+blocks/s x B.
+
+`roofline` reports the kernel with the largest time share, timed live with HIP
+events recorded by the library on the launch stream during the timed steps;
+its achieved rate is the kernel's algorithmic bytes (HBM-bound kernels) or
+flops (MFMA-bound) per launch divided by its mean launch time.
+`cpu_baseline` times the float64 CPU oracle on one request of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0       # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 (dense MFMA / vector)
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
+def elt(d):
+    return 2 if d.dtype == "bf16" else 4
+
+
+def kernel_work(d, wl):
+    """Algorithmic (bytes, flops) per launch and launches per step, per kernel
+    kind: weights read once, activations read/written once, context K/V read
+    once per layer."""
+    e = elt(d)
+    bs, B = wl.bs, d.B
+    M, Mlm = bs * B, bs * (B - 1)
+    n = sum(wl.n_new)
+    sctx = sum(wl.ctx)
+    qkv = (d.Hq + 2 * d.Hkv) * d.hd
+    w = {}
+    w["fuse_gemm"] = (d.D * d.L * d.Dt * e + n * d.L * d.Dt * e + n * d.D * 4,
+                      2.0 * n * d.D * d.L * d.Dt, 1)
+    w["fuse_norm"] = (n * d.D * (4 + e), 0.0, 1)
+    w["ctx_kv_gemm"] = (d.N * 2 * d.Hkv * d.hd * d.D * e + n * d.D * e + n * d.N * 2 * d.Hkv * d.hd * e,
+                        2.0 * n * d.N * 2 * d.Hkv * d.hd * d.D, 1)
+    w["embed"] = (M * d.D * (4 + e), 0.0, 1)
+    w["norm"] = (M * d.D * (4 + e), 0.0, 2 * d.N + 1)
+    w["qkv_gemm"] = (qkv * d.D * e + M * d.D * e + M * qkv * e, 2.0 * M * qkv * d.D, d.N)
+    w["attention"] = (sctx * 2 * d.Hkv * d.hd * e + M * (2 * d.Hq + 2 * d.Hkv) * d.hd * e,
+                      sum(4.0 * d.Hq * B * (c + B) * d.hd for c in wl.ctx), d.N)
+    w["o_gemm"] = (d.D * d.Hq * d.hd * e + M * d.Hq * d.hd * e + 2 * M * d.D * 4,
+                   2.0 * M * d.D * d.Hq * d.hd, d.N)
+    w["gateup_gemm"] = (2 * d.I * d.D * e + M * d.D * e + M * d.I * e, 2.0 * M * 2 * d.I * d.D, d.N)
+    w["down_gemm"] = (d.D * d.I * e + M * d.I * e + 2 * M * d.D * 4, 2.0 * M * d.D * d.I, d.N)
+    w["lm_head"] = (d.V * d.D * e + Mlm * d.D * e, 2.0 * Mlm * d.V * d.D, 1)
+    return w
+
+
+def step_work(d, wl):
+    """Whole-step algorithmic bytes and flops: every weight once, the context
+    K/V once per layer, the fused rows in and their K/V out."""
+    e = elt(d)
+    n = sum(wl.n_new)
+    weights = (d.D * d.L * d.Dt + d.N * 2 * d.D * d.Hkv * d.hd
+               + d.N * (d.D * d.Hq * d.hd + 2 * d.D * d.Hkv * d.hd + d.Hq * d.hd * d.D + 3 * d.D * d.I)
+               + d.V * d.D)
+    byts = e * weights + sum(wl.ctx) * d.N * 2 * d.Hkv * d.hd * e + n * (d.L * d.Dt + d.N * 2 * d.Hkv * d.hd) * e
+    kw = kernel_work(d, wl)
+    flops = sum(f * c for _, f, c in kw.values())
+    return byts, flops
+
+
+def roof_entry(kind, d, wl, ms_per_launch, traffic):
+    byts, flops, _ = kernel_work(d, wl)[kind]
+    if flops / max(byts, 1) >= RIDGE:
+        ach = flops / (ms_per_launch * 1e-3) / 1e12
+        peak = BF16_PEAK_TFLOPS if d.dtype == "bf16" else FP32_PEAK_TFLOPS
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": traffic, "kernel": kind,
+                "launch_ms": round(ms_per_launch, 5), "algorithmic_flops": flops}
+    ach = byts / (ms_per_launch * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kind,
+            "launch_ms": round(ms_per_launch, 5), "algorithmic_bytes": byts}
+
+
+def source_sha():
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "block_diffusion_drafter_fuse_amd", "csrc")
+    for f in sorted(os.listdir(cdir)):
+        h.update(open(os.path.join(cdir, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kind, workload):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        t = json.load(open(p))
+    except ValueError:
+        return None
+    if t.get("source_sha") != source_sha():
+        return None
+    k = t.get("kernels", {}).get(f"{workload}:{kind}")
+    return None if k is None else k.get("bytes_per_launch")
+
+
+class Workbench:
+    """Drafter + resident inputs for one workload."""
+
+    def __init__(self, wl, w_dev, torch):
+        import block_diffusion_drafter_fuse_amd as dfa
+        import synth
+        self.torch = torch
+        self.wl = wl
+        d = wl.dims
+        self.d = d
+        bs = wl.bs
+        self.slots = list(range(bs))
+        self.dr = dfa.Drafter(d, w_dev, max(wl.ctx) + d.B, bs, bs)
+        self.pre = [c - n for c, n in zip(wl.ctx, wl.n_new)]
+        for r in range(bs):
+            if self.pre[r]:
+                hid = [dfa.to_device(h) for h in synth.make_hidden(d, wl.seed, r, 0, self.pre[r])]
+                self.dr.fuse_ctx([r], [self.pre[r]], hid)
+                del hid
+        rows = [synth.make_hidden(d, wl.seed, r, self.pre[r], wl.n_new[r]) for r in range(bs)]
+        self.hid = [dfa.to_device(np.ascontiguousarray(np.concatenate([x[l] for x in rows], 0)))
+                    for l in range(d.L)]
+        self.anchor = torch.tensor(synth.make_anchors(d, wl.seed, bs), device="cuda")
+        self.ids = torch.zeros((bs, d.B - 1, 1), dtype=torch.int32, device="cuda")
+        m = synth.draw_first_mismatch("geometric", bs, d.B, wl.seed)
+        self.m = m
+        self.target = None
+        self.tau = torch.zeros(bs, dtype=torch.int32, device="cuda")
+        self.bonus = torch.zeros(bs, dtype=torch.int32, device="cuda")
+        self.dfa = dfa
+        torch.cuda.synchronize()
+
+    def step(self):
+        wl = self.wl
+        self.dr.fuse_ctx(self.slots, wl.n_new, self.hid)
+        self.dr.draft_block(self.slots, self.anchor, 1, self.ids)
+        self.dfa.accept(wl.bs, self.d.B, self.ids, 1, self.target, self.tau, self.bonus)
+        for r in self.slots:
+            self.dr.slot_reset(r, self.pre[r])
+
+    def prepare_targets(self):
+        """Targets giving the drawn acceptance lengths on this drafter's own
+        candidates (timing input only; acceptance parity is tested elsewhere)."""
+        import synth
+        self.dr.fuse_ctx(self.slots, self.wl.n_new, self.hid)
+        self.dr.draft_block(self.slots, self.anchor, 1, self.ids)
+        self.torch.cuda.synchronize()
+        cand = self.ids[:, :, 0].cpu().numpy()
+        for r in self.slots:
+            self.dr.slot_reset(r, self.pre[r])
+        tgt = synth.make_targets(cand, self.m, self.d.V, self.wl.seed)
+        self.target = self.torch.tensor(tgt, device="cuda")
+
+    def breakdown(self, steps=3):
+        self.dr.profile_enable(list(self.dfa.KERNEL_KINDS[:-1]), 4096)
+        for _ in range(steps):
+            self.step()
+        res = self.dr.profile_read()
+        self.dr.profile_enable([], 0)
+        return {k: (ms / steps, cnt // steps) for k, (ms, cnt) in res.items()}
+
+    def timed(self, steps, warmup, kind):
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        if kind:
+            self.dr.profile_enable([kind], 64 * (steps + 1))
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for _ in range(steps):
+            self.step()
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = start.elapsed_time(stop) / steps
+        kern = None
+        if kind:
+            res = self.dr.profile_read()
+            self.dr.profile_enable([], 0)
+            tot, cnt = res.get(kind, (0.0, 0))
+            kern = (tot / max(cnt, 1), cnt)
+        return ms, wall / steps * 1e3, kern
+
+
+def measure(wl, w_dev, torch, steps, warmup, label):
+    wb = Workbench(wl, w_dev, torch)
+    wb.prepare_targets()
+    for _ in range(2):
+        wb.step()
+    torch.cuda.synchronize()
+    bd = wb.breakdown()
+    dom = max(bd, key=lambda k: bd[k][0])
+    ms, wall_ms, kern = wb.timed(steps, warmup, dom)
+    d = wl.dims
+    byts, flops = step_work(d, wl)
+    blocks_s = wl.bs / (ms * 1e-3)
+    out = {
+        "workload": label,
+        "ms_per_step": round(ms, 4),
+        "wall_ms_per_step": round(wall_ms, 4),
+        "blocks_per_s": round(blocks_s, 1),
+        "drafted_tokens_per_s": round(blocks_s * d.B, 1),
+        "step_algorithmic_bytes": byts,
+        "step_algorithmic_flops": flops,
+        "step_hbm_roof_frac": round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+        "step_mfma_roof_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+        "breakdown_ms": {k: round(v[0], 4) for k, v in sorted(bd.items(), key=lambda kv: -kv[1][0])},
+        "roofline": roof_entry(dom, d, wl, kern[0], traffic_for(dom, label)),
+    }
+    out["roofline"]["launches_timed"] = kern[1]
+    wb.dr.close()
+    del wb
+    torch.cuda.synchronize()
+    return out
+
+
+def cpu_baseline(wl, w_np, budget_s=20.0):
+    """The float64 oracle, as it stands, on one request of the workload (the
+    one with the shortest context): fuse its new rows, draft its block, accept.
+    Returns blocks/s x B for that single-request stream."""
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    d = wl.dims
+    r = int(np.argmin(wl.ctx))
+    w32 = synth.weights_as_f32(w_np)
+    pre = wl.ctx[r] - wl.n_new[r]
+    new = synth.as_f32(synth.make_hidden(d, wl.seed, r, pre, wl.n_new[r]))
+    anchor = int(synth.make_anchors(d, wl.seed, wl.bs)[r])
+    o = oracle.OracleDrafter(w32, d)
+    if pre:
+        o.fuse(r, synth.as_f32(synth.make_hidden(d, wl.seed, r, 0, pre)))
+    times = []
+    t_start = time.perf_counter()
+    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 5):
+        t0 = time.perf_counter()
+        o.fuse(r, new)
+        res = o.draft(r, anchor)
+        cand, _ = oracle.topk(res["logits"], 1)
+        oracle.accept(cand[:, 0], np.zeros(d.B, np.int64))
+        times.append(time.perf_counter() - t0)
+        o.reset(r, pre)
+    t = float(np.median(times))
+    return {"value": round(d.B / t, 3), "unit": "drafted tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"1 request of the workload (ctx {wl.ctx[r]}, {wl.n_new[r]} new rows), "
+                      f"median of {len(times)} float64 steps, {t:.2f} s/step"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="qwen3_8b_bs32")
+    ap.add_argument("--companion", default="qwen3_8b_bs1", help="second workload reported under 'bs1' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the draft step shards by request across GPUs with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import block_diffusion_drafter_fuse_amd as dfa
+    import synth
+
+    wl = synth.get_config(args.workload)
+    print(f"[bench] generating weights for {wl.dims.name}", file=sys.stderr, flush=True)
+    w_np = synth.make_weights(wl.dims, wl.seed)
+    w_dev = dfa.Drafter.upload_weights(w_np)
+    print(f"[bench] measuring {args.workload}", file=sys.stderr, flush=True)
+    main_res = measure(wl, w_dev, torch, args.steps, args.warmup, args.workload)
+    comp = None
+    if args.companion:
+        wc = synth.get_config(args.companion)
+        assert wc.dims == wl.dims, "companion must share the model shape"
+        print(f"[bench] measuring {args.companion}", file=sys.stderr, flush=True)
+        comp = measure(wc, w_dev, torch, args.steps, args.warmup, args.companion)
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, w_np)
+    d = wl.dims
+    line = {
+        "metric": "drafted tokens/s (blocks/s x B) at Qwen3-8B shape",
+        "value": main_res["drafted_tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": d.dtype,
+        "data": "synthetic (seeded random-init weights and verifier features)",
+        "config": {"workload": args.workload, "model": d.name, "batch": wl.bs, "block": d.B,
+                   "ctx_sum": sum(wl.ctx), "new_rows": sum(wl.n_new), "top_k": 1},
+        "blocks_per_s": main_res["blocks_per_s"],
+        "roofline": main_res["roofline"],
+        "step_hbm_roof_frac": main_res["step_hbm_roof_frac"],
+        "step_mfma_roof_frac": main_res["step_mfma_roof_frac"],
+        "breakdown_ms": main_res["breakdown_ms"],
+        "cpu_baseline": cpu,
+    }
+    if comp:
+        line["bs1"] = {k: comp[k] for k in ("workload", "drafted_tokens_per_s", "blocks_per_s", "ms_per_step",
+                                            "step_hbm_roof_frac", "roofline", "breakdown_ms")}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

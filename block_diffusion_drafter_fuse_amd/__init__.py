@@ -21,7 +21,11 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",
 
 EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fuse_ctx",
             "dflash_draft_block", "dflash_accept", "dflash_slot_reset", "dflash_slot_len",
-            "dflash_read_cache", "dflash_strerror", "dflash_last_error")
+            "dflash_read_cache", "dflash_profile_enable", "dflash_profile_read",
+            "dflash_strerror", "dflash_last_error")
+
+KERNEL_KINDS = ("fuse_gemm", "fuse_norm", "ctx_kv_gemm", "embed", "norm", "qkv_gemm", "attention",
+                "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "accept")
 
 
 class DflashError(RuntimeError):
@@ -74,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.dflash_slot_reset.argtypes = [vp, i32, i32]
     L.dflash_slot_len.argtypes = [vp, i32, P(i32)]
     L.dflash_read_cache.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    L.dflash_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
+    L.dflash_profile_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.dflash_strerror.argtypes = [ctypes.c_int]
     L.dflash_strerror.restype = ctypes.c_char_p
     L.dflash_last_error.argtypes = []
@@ -190,6 +196,19 @@ class Drafter:
         v = ctypes.c_int32()
         _check(lib().dflash_slot_len(self.h, int(slot), ctypes.byref(v)), "dflash_slot_len")
         return v.value
+
+    def profile_enable(self, kinds: Sequence[str], max_launches: int = 4096):
+        mask = 0
+        for k in kinds:
+            mask |= 1 << KERNEL_KINDS.index(k)
+        _check(lib().dflash_profile_enable(self.h, mask, int(max_launches)), "dflash_profile_enable")
+
+    def profile_read(self) -> dict:
+        n = len(KERNEL_KINDS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int32 * n)()
+        _check(lib().dflash_profile_read(self.h, ms, cnt), "dflash_profile_read")
+        return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n) if cnt[i]}
 
     def read_cache(self, slot: int, layer: int, pos0: int, n: int, k_out, v_out, stream=None):
         _check(lib().dflash_read_cache(self.h, _stream(stream), int(slot), int(layer), int(pos0), int(n),

@@ -39,6 +39,8 @@ int fail(int code, const std::string& msg) {
 constexpr size_t kAlign = 256;
 constexpr int kFuseChunk = 1024;      // rows per fusion GEMM launch
 constexpr int kAttnWorkMax = 4096;    // attention split work items per call
+constexpr int kAttnTargetWG = 2048;   // attention work-groups aimed for
+constexpr int kAttnMinChunk = 256;    // minimum context keys per split
 constexpr int kLmTargetWG = 2048;     // LM-head work-groups aimed for
 constexpr int kLmWV = 4;              // waves per LM-head work-group
 
@@ -48,7 +50,7 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 struct Plan {
   // pool
-  size_t kv_off, rope_off, ctr_off, pool_bytes;
+  size_t kv_off, rope_off, pool_bytes;
   size_t head_stride, kv_stride, layer_stride, slot_stride;  // elements
   int ctx_pad;
   // workspace
@@ -110,8 +112,6 @@ void make_plan(const dflash_dims* d, Plan* p) {
   off = align_up(off + p->slot_stride * d->max_slots * e);
   p->rope_off = off;
   off = align_up(off + (size_t)(d->max_ctx + d->B) * (d->hd / 2) * sizeof(float2));
-  p->ctr_off = off;
-  off = align_up(off + (size_t)kMaxReq * d->Hkv * sizeof(int));
   p->pool_bytes = off;
 
   const int M = d->max_batch * d->B;
@@ -154,7 +154,15 @@ bool hip_ok(hipError_t e, const char* what, int* rc) {
 
 }  // namespace
 
+struct ProfRec {
+  int kind;
+  hipEvent_t a, b;
+};
+
 struct dflash_ctx {
+  uint32_t prof_mask = 0;
+  std::vector<hipEvent_t> prof_events;  // pool, 2 per launch
+  std::vector<ProfRec> prof_recs;
   dflash_dims d;
   dflash_weights w;
   std::vector<dflash_layer_weights> layers;
@@ -166,6 +174,26 @@ struct dflash_ctx {
 };
 
 namespace {
+
+// Event pair around one launch when its kind is being profiled.
+struct ProfScope {
+  dflash_ctx* c;
+  int kind;
+  hipStream_t st;
+  bool on;
+  ProfScope(dflash_ctx* c_, int k, hipStream_t s)
+      : c(c_), kind(k), st(s),
+        on(c_ && ((c_->prof_mask >> k) & 1u) && c_->prof_recs.size() * 2 + 2 <= c_->prof_events.size()) {
+    if (on) {
+      ProfRec r{kind, c->prof_events[c->prof_recs.size() * 2], c->prof_events[c->prof_recs.size() * 2 + 1]};
+      (void)hipEventRecord(r.a, st);
+      c->prof_recs.push_back(r);
+    }
+  }
+  ~ProfScope() {
+    if (on) (void)hipEventRecord(c->prof_recs.back().b, st);
+  }
+};
 
 // ------------------------------------------------------------------ launches
 
@@ -247,9 +275,15 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
     a.kseg = d.Dt;
     a.lda = d.Dt;
     a.M = rows;
-    launch_gemm<T>(wc, a, EpiStoreF32{z, d.D}, st);
-    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(rows), dim3(256), 0, st, z,
-                       static_cast<const T*>(c->w.g_c), hc, d.D, d.rms_eps, 0, d.B);
+    {
+      ProfScope ps(c, DFLASH_K_FUSE_GEMM, st);
+      launch_gemm<T>(wc, a, EpiStoreF32{z, d.D}, st);
+    }
+    {
+      ProfScope ps(c, DFLASH_K_FUSE_NORM, st);
+      hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(rows), dim3(256), 0, st, z,
+                         static_cast<const T*>(c->w.g_c), hc, d.D, d.rms_eps, 0, d.B);
+    }
     EpiKVAppend<T> epi{};
     epi.pool = pool;
     epi.slot_stride = p.slot_stride;
@@ -263,13 +297,16 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
     epi.use_rope = d.use_rope;
     epi.row_base = base;
     epi.meta = fm;
+    ProfScope ps(c, DFLASH_K_CTX_KV_GEMM, st);
     launch_gemm<T>(wkv, aop<T>(hc, rows, d.D), epi, st);
   }
 }
 
 template <typename T, int HD, int QF>
 void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<T, HD, QF>), dim3(work), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((attn_kernel<T, HD, QF>), dim3(work), dim3(64 * QF), 0, st, a);
+  const int threads = a.meta.n_req * a.Hkv * a.G * a.B * (HD / 4);
+  hipLaunchKernelGGL((attn_combine_kernel<T, HD, QF * 16>), dim3(ceil_div(threads, 256)), dim3(256), 0, st, a);
 }
 
 template <typename T>
@@ -299,13 +336,16 @@ struct AttnPlan {
 
 int plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPlan* ap) {
   const dflash_dims& d = c->d;
+  // Splits of at least kAttnMinChunk keys (partial results stay small next to
+  // the K/V they summarise), about kAttnTargetWG work-groups per call.
   long long total = 0;
   for (int r = 0; r < n_req; ++r) total += c->len[slot[r]];
-  int chunk = round_up((int)std::max<long long>(1, (total * d.Hkv + 1023) / 1024), 32);
-  chunk = std::max(chunk, 256);
+  int chunk = round_up((int)std::max<long long>(1, (total * d.Hkv + kAttnTargetWG - 1) / kAttnTargetWG), 32);
+  chunk = std::max(chunk, kAttnMinChunk);
   for (;;) {
     long long work = 0;
-    for (int r = 0; r < n_req; ++r) work += (long long)d.Hkv * (ceil_div(c->len[slot[r]], chunk) + 1);
+    for (int r = 0; r < n_req; ++r)
+      work += (long long)d.Hkv * std::max(1, ceil_div(c->len[slot[r]], chunk));
     if (work <= kAttnWorkMax) {
       ap->chunk = chunk;
       ap->work = (int)work;
@@ -320,9 +360,9 @@ int plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPlan
   for (int r = 0; r < n_req; ++r) {
     m.ctx[r] = c->len[slot[r]];
     m.slot[r] = slot[r];
-    m.nsplit[r] = ceil_div(m.ctx[r], ap->chunk);
+    m.nsplit[r] = std::max(1, ceil_div(m.ctx[r], ap->chunk));
     m.work0[r] = w;
-    w += d.Hkv * (m.nsplit[r] + 1);
+    w += d.Hkv * m.nsplit[r];
   }
   m.work0[n_req] = w;
   return DFLASH_OK;
@@ -350,8 +390,11 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   dm.B = d.B;
   for (int r = 0; r < n_req; ++r) dm.ctx[r] = c->len[slot[r]];
 
-  hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(c->w.embed),
-                     static_cast<const T*>(c->w.e_mask), anchor, d.B, d.D, d.V, x);
+  {
+    ProfScope ps(c, DFLASH_K_EMBED, st);
+    hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(c->w.embed),
+                       static_cast<const T*>(c->w.e_mask), anchor, d.B, d.D, d.V, x);
+  }
 
   AttnArgs<T> aa{};
   aa.q = q;
@@ -373,14 +416,16 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d.hd));
   aa.part_o = c->wsp<float>(p.po_off);
   aa.part_ml = c->wsp<float>(p.pml_off);
-  aa.counters = reinterpret_cast<int*>(c->pool + p.ctr_off);
   aa.meta = apl.meta;
 
   const int qd = d.Hq * d.hd, kd = d.Hkv * d.hd;
   for (int l = 0; l < d.N; ++l) {
     const dflash_layer_weights& lw = c->layers[l];
-    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
-                       static_cast<const T*>(lw.g_attn), u, d.D, d.rms_eps, 0, d.B);
+    {
+      ProfScope ps(c, DFLASH_K_NORM, st);
+      hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
+                         static_cast<const T*>(lw.g_attn), u, d.D, d.rms_eps, 0, d.B);
+    }
     EpiQKV<T> eq{};
     eq.q = q;
     eq.kb = kb;
@@ -392,19 +437,40 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     eq.BP = p.BP;
     eq.use_rope = d.use_rope;
     eq.meta = dm;
-    launch_gemm<T>(wop<T>({{lw.w_q, qd}, {lw.w_kb, kd}, {lw.w_vb, kd}}, d.hd / 2), aop<T>(u, M, d.D), eq,
-                   st);
+    {
+      ProfScope ps(c, DFLASH_K_QKV_GEMM, st);
+      launch_gemm<T>(wop<T>({{lw.w_q, qd}, {lw.w_kb, kd}, {lw.w_vb, kd}}, d.hd / 2), aop<T>(u, M, d.D),
+                     eq, st);
+    }
     aa.layer = l;
-    attn_dispatch<T>(aa, apl.work, d.hd, p.qf, st);
-    launch_gemm<T>(wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), EpiResidual{x, d.D}, st);
-    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
-                       static_cast<const T*>(lw.g_ffn), u, d.D, d.rms_eps, 0, d.B);
-    launch_gemm<T>(wop<T>({{lw.w_gate, d.I}, {lw.w_up, d.I}}, d.I), aop<T>(u, M, d.D),
-                   EpiSwiGLU<T>{h, d.I}, st);
-    launch_gemm<T>(wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), EpiResidual{x, d.D}, st);
+    {
+      ProfScope ps(c, DFLASH_K_ATTENTION, st);
+      attn_dispatch<T>(aa, apl.work, d.hd, p.qf, st);
+    }
+    {
+      ProfScope ps(c, DFLASH_K_O_GEMM, st);
+      launch_gemm<T>(wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), EpiResidual{x, d.D}, st);
+    }
+    {
+      ProfScope ps(c, DFLASH_K_NORM, st);
+      hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
+                         static_cast<const T*>(lw.g_ffn), u, d.D, d.rms_eps, 0, d.B);
+    }
+    {
+      ProfScope ps(c, DFLASH_K_GATEUP_GEMM, st);
+      launch_gemm<T>(wop<T>({{lw.w_gate, d.I}, {lw.w_up, d.I}}, d.I), aop<T>(u, M, d.D),
+                     EpiSwiGLU<T>{h, d.I}, st);
+    }
+    {
+      ProfScope ps(c, DFLASH_K_DOWN_GEMM, st);
+      launch_gemm<T>(wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), EpiResidual{x, d.D}, st);
+    }
   }
-  hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(Mlm), dim3(256), 0, st, x,
-                     static_cast<const T*>(c->w.g_final), ufin, d.D, d.rms_eps, 1, d.B);
+  {
+    ProfScope ps(c, DFLASH_K_NORM, st);
+    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(Mlm), dim3(256), 0, st, x,
+                       static_cast<const T*>(c->w.g_final), ufin, d.D, d.rms_eps, 1, d.B);
+  }
 
   int tpw, nchunk, rowblocks;
   lm_shape(Mlm, d.V, &tpw, &nchunk, &rowblocks);
@@ -419,16 +485,24 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   la.part_v = c->wsp<float>(p.lmv_off);
   la.part_i = c->wsp<int>(p.lmi_off);
   const bool small = lm_rows_per_wg(Mlm) == 16;
-  if (top_k == 1) {
-    if (small) launch_lm<T, 1, 1>(la, nchunk, rowblocks, st);
-    else launch_lm<T, 4, 1>(la, nchunk, rowblocks, st);
-    hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i, nchunk,
-                       Mlm, top_k, out_ids, out_vals);
-  } else {
-    if (small) launch_lm<T, 1, 16>(la, nchunk, rowblocks, st);
-    else launch_lm<T, 4, 16>(la, nchunk, rowblocks, st);
-    hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i,
-                       nchunk, Mlm, top_k, out_ids, out_vals);
+  {
+    ProfScope ps(c, DFLASH_K_LM_HEAD, st);
+    if (top_k == 1) {
+      if (small) launch_lm<T, 1, 1>(la, nchunk, rowblocks, st);
+      else launch_lm<T, 4, 1>(la, nchunk, rowblocks, st);
+    } else {
+      if (small) launch_lm<T, 1, 16>(la, nchunk, rowblocks, st);
+      else launch_lm<T, 4, 16>(la, nchunk, rowblocks, st);
+    }
+  }
+  {
+    ProfScope ps(c, DFLASH_K_TOPK_MERGE, st);
+    if (top_k == 1)
+      hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i, nchunk,
+                         Mlm, top_k, out_ids, out_vals);
+    else
+      hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i,
+                         nchunk, Mlm, top_k, out_ids, out_vals);
   }
 }
 
@@ -519,7 +593,48 @@ int dflash_create(const dflash_dims* dims, const dflash_weights* weights, void* 
   return DFLASH_OK;
 }
 
-void dflash_destroy(dflash_ctx* ctx) { delete ctx; }
+void dflash_destroy(dflash_ctx* ctx) {
+  if (!ctx) return;
+  for (hipEvent_t e : ctx->prof_events) (void)hipEventDestroy(e);
+  delete ctx;
+}
+
+int dflash_profile_enable(dflash_ctx* ctx, uint32_t kind_mask, int32_t max_launches) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  if (kind_mask >> DFLASH_K_COUNT) return fail(DFLASH_EINVAL, "unknown kernel kind in mask");
+  if (max_launches < 0 || max_launches > (1 << 20)) return fail(DFLASH_EINVAL, "max_launches out of range");
+  ctx->prof_mask = 0;
+  ctx->prof_recs.clear();
+  const size_t need = kind_mask ? (size_t)max_launches * 2 : 0;
+  int rc = DFLASH_OK;
+  while (ctx->prof_events.size() < need) {
+    hipEvent_t e;
+    if (!hip_ok(hipEventCreate(&e), "hipEventCreate", &rc)) return rc;
+    ctx->prof_events.push_back(e);
+  }
+  ctx->prof_mask = kind_mask;
+  return DFLASH_OK;
+}
+
+int dflash_profile_read(dflash_ctx* ctx, double* total_ms, int32_t* launches) {
+  g_last_error.clear();
+  if (!ctx || !total_ms || !launches) return fail(DFLASH_EINVAL, "NULL argument");
+  for (int k = 0; k < DFLASH_K_COUNT; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  int rc = DFLASH_OK;
+  for (const ProfRec& r : ctx->prof_recs) {
+    if (!hip_ok(hipEventSynchronize(r.b), "hipEventSynchronize", &rc)) return rc;
+    float ms = 0.f;
+    if (!hip_ok(hipEventElapsedTime(&ms, r.a, r.b), "hipEventElapsedTime", &rc)) return rc;
+    total_ms[r.kind] += ms;
+    launches[r.kind] += 1;
+  }
+  ctx->prof_recs.clear();
+  return DFLASH_OK;
+}
 
 int dflash_slot_reset(dflash_ctx* ctx, int32_t slot, int32_t keep_len) {
   g_last_error.clear();

@@ -119,8 +119,7 @@ typedef struct dflash_weights {
 typedef struct dflash_ctx dflash_ctx;
 
 /* Byte sizes of the two caller-allocated device buffers for `dims`: the KV
- * pool (projected context K/V of every slot, the RoPE table and a few
- * counters; persistent) and the workspace (per-call scratch).  Pure host
+ * pool (projected context K/V of every slot and the RoPE table; persistent) and the workspace (per-call scratch).  Pure host
  * computation.  Returns DFLASH_OK or DFLASH_EINVAL / DFLASH_EUNSUPPORTED. */
 int dflash_query_sizes(const dflash_dims* dims, size_t* kv_pool_bytes, size_t* workspace_bytes);
 
@@ -185,6 +184,35 @@ int dflash_slot_len(const dflash_ctx* ctx, int32_t slot, int32_t* len);
  * their absolute positions.  For inspection and tests. */
 int dflash_read_cache(dflash_ctx* ctx, void* stream, int32_t slot, int32_t layer, int32_t pos0,
                       int32_t n, float* k_out, float* v_out);
+
+/* Kernel kinds, for per-kernel timing. */
+enum dflash_kernel_kind {
+  DFLASH_K_FUSE_GEMM = 0,   /* context fusion GEMM W_c [H^(l1);...] */
+  DFLASH_K_FUSE_NORM,       /* RMSNorm of the fused context */
+  DFLASH_K_CTX_KV_GEMM,     /* per-layer context K/V projection + RoPE + cache append */
+  DFLASH_K_EMBED,           /* block assembly */
+  DFLASH_K_NORM,            /* pre-attention / pre-FFN / final RMSNorm */
+  DFLASH_K_QKV_GEMM,        /* block Q/K_b/V_b projection + RoPE */
+  DFLASH_K_ATTENTION,       /* KV-injected block attention (split + combine) */
+  DFLASH_K_O_GEMM,          /* output projection + residual */
+  DFLASH_K_GATEUP_GEMM,     /* gate/up projection + SwiGLU */
+  DFLASH_K_DOWN_GEMM,       /* down projection + residual */
+  DFLASH_K_LM_HEAD,         /* LM head with fused top-k */
+  DFLASH_K_TOPK_MERGE,      /* top-k merge */
+  DFLASH_K_ACCEPT,          /* acceptance scan (stateless call: never timed) */
+  DFLASH_K_COUNT
+};
+
+/* Diagnostics: time every launch of the kernel kinds in `kind_mask` (bit k =
+ * kind k) with a HIP event pair recorded on the launch stream, up to
+ * `max_launches` launches in total (events are created here, on the host).
+ * Disable with kind_mask = 0.  Not for use under graph capture. */
+int dflash_profile_enable(dflash_ctx* ctx, uint32_t kind_mask, int32_t max_launches);
+
+/* Wait for the recorded events and return, per kind, the summed milliseconds
+ * and the launch count (arrays of DFLASH_K_COUNT entries, [host]); then
+ * clears the records. */
+int dflash_profile_read(dflash_ctx* ctx, double* total_ms, int32_t* launches);
 
 /* Static text for a status code. */
 const char* dflash_strerror(int status);

@@ -2,11 +2,17 @@
 // carving, launch planning and the C ABI declared in include/dflash_fuse.h.
 //
 // One launch sequence per call, all on the caller's stream:
-//   fuse_ctx:   [fusion GEMM -> RMSNorm -> context K/V GEMM with RoPE + cache append] per row chunk
-//   draft:      embed, then per layer {RMSNorm, QKV GEMM (+RoPE), attention,
-//               O GEMM (+residual), RMSNorm, gate/up GEMM (+SwiGLU), down GEMM
-//               (+residual)}, final RMSNorm, LM head with top-k, top-k merge
-//   accept:     one scan kernel
+//   fuse_ctx:  per row chunk, fusion GEMM (writes T(z*g_c) and row sums of
+//              squares) -> context K/V GEMM (RMSNorm scale, RoPE, cache append)
+//   draft:     embed (x, T(x*g_attn0), sums of squares), then per layer
+//              {QKV GEMM (+norm scale, RoPE), attention + combine,
+//               O GEMM (+residual, next norm input), gate/up GEMM (+norm scale,
+//               SwiGLU), down GEMM (+residual, next norm input)},
+//              LM head with fused top-k (+final norm scale), top-k merge
+//   accept:    one scan kernel
+// RMSNorm never runs as a separate pass: the producer of a normed operand
+// writes x*g and per-64-feature sums of squares, the consumer GEMM scales its
+// rows by rsqrt(mean + eps) in the epilogue.
 // Per-call request metadata travels in kernel arguments (no host-to-device
 // copies), so a call sequence can be captured in a HIP graph.
 #include <hip/hip_runtime.h>
@@ -22,6 +28,7 @@
 #include "attention.h"
 #include "common.h"
 #include "gemm.h"
+#include "gemm_tiled.h"
 #include "lmhead.h"
 #include "misc.h"
 
@@ -37,16 +44,26 @@ int fail(int code, const std::string& msg) {
 }
 
 constexpr size_t kAlign = 256;
-constexpr int kFuseChunk = 1024;      // rows per fusion GEMM launch
-constexpr int kAttnWorkMax = 4096;    // attention split work items per call
-constexpr int kAttnTargetWG = 2048;   // attention work-groups aimed for
-constexpr int kAttnMinChunk = 256;    // minimum context keys per split
-constexpr int kLmTargetWG = 2048;     // LM-head work-groups aimed for
-constexpr int kLmWV = 4;              // waves per LM-head work-group
+constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
+constexpr int kAttnWorkMax = 4096;     // attention split work items per call
+constexpr int kAttnTargetWG = 2048;    // attention work-groups aimed for
+constexpr int kAttnMinChunk = 256;     // minimum context keys per split
+constexpr int kLmTargetWG = 2048;      // few-token LM-head work-groups aimed for
+constexpr int kLmWV = 4;               // waves per few-token LM-head work-group
+constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
+constexpr int kGemvBytes = 8;          // KB of weights in flight per wave (U * FN)
+constexpr int kGemvFNUnpaired = 1, kGemvFNPaired = 2;  // skinny GEMM fragments per wave
+constexpr int kGemvTargetWaves = 4096;
+constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, unroll
+constexpr int kTBM = 128, kTBN = 256;  // tiled GEMM work-group tile
+constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
+constexpr size_t kPartFloats = size_t(16) << 20;  // split-K partials (64 MB)
+constexpr int kCounters = 1 << 16;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+int ceil_div_l(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 struct Plan {
   // pool
@@ -54,8 +71,8 @@ struct Plan {
   size_t head_stride, kv_stride, layer_stride, slot_stride;  // elements
   int ctx_pad;
   // workspace
-  size_t x_off, u_off, q_off, kb_off, vbt_off, o_off, h_off, ufin_off;
-  size_t po_off, pml_off, lmv_off, lmi_off, z_off, hc_off, ws_bytes;
+  size_t x_off, u_off, ssq_off, q_off, kb_off, vbt_off, o_off, h_off;
+  size_t po_off, pml_off, lmv_off, lmi_off, hc_off, hclo_off, fssq_off, part_off, ctr_off, ws_bytes;
   int BP;
   size_t lm_entries;
   int qf;
@@ -63,15 +80,20 @@ struct Plan {
 
 int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
 
-int lm_rows_per_wg(int M) { return M <= 16 ? 16 : 64; }
-
-void lm_shape(int M, int V, int* tpw, int* nchunk, int* rowblocks) {
-  const int rpw = lm_rows_per_wg(M);
-  *rowblocks = ceil_div(M, rpw);
-  const int ntiles = V / 16;
+void lm_shape_small(int M, int V, int* tpw, int* nchunk, int* rowblocks) {
+  *rowblocks = ceil_div(M, 16);
+  const int ngroups = V / (16 * kLmFN);
   const int chunks_target = std::max(1, kLmTargetWG / *rowblocks);
-  *tpw = std::max(1, ceil_div(ntiles, kLmWV * chunks_target));
-  *nchunk = ceil_div(ntiles, kLmWV * *tpw);
+  *tpw = std::max(1, ceil_div(ngroups, kLmWV * chunks_target));
+  *nchunk = ceil_div(ngroups, kLmWV * *tpw);
+}
+
+// LM-head partial-list entries a call needs (KTOP = 16 for top_k > 1).
+size_t lm_entries_for(int Mlm, int V, int top_k) {
+  if (top_k == 1 && Mlm > kSkinnyMaxM) return (size_t)ceil_div(V, kTBN / 2) * Mlm;
+  int tpw, nchunk, rb;
+  lm_shape_small(Mlm, V, &tpw, &nchunk, &rb);
+  return (size_t)nchunk * Mlm * (top_k == 1 ? 1 : 16);
 }
 
 int validate_dims(const dflash_dims* d) {
@@ -90,9 +112,9 @@ int validate_dims(const dflash_dims* d) {
   if (d->Hq % d->Hkv) return fail(DFLASH_EINVAL, "Hq must be a multiple of Hkv");
   if ((d->Hq / d->Hkv) * d->B > 64)
     return fail(DFLASH_EUNSUPPORTED, "(Hq/Hkv)*B must be <= 64 (query rows per KV head)");
-  if (d->D % 32 || d->Dt % 32 || d->I % 32)
-    return fail(DFLASH_EUNSUPPORTED, "D, Dt and I must be multiples of 32");
-  if (d->V % 16) return fail(DFLASH_EUNSUPPORTED, "V must be a multiple of 16");
+  if (d->D % 64 || d->Dt % 64 || d->I % 64)
+    return fail(DFLASH_EUNSUPPORTED, "D, Dt and I must be multiples of 64");
+  if (d->V % 64) return fail(DFLASH_EUNSUPPORTED, "V must be a multiple of 64");
   if (!(d->rms_eps >= 0.f) || !(d->rope_base > 0.f))
     return fail(DFLASH_EINVAL, "rms_eps must be >= 0 and rope_base > 0");
   if ((long long)d->max_ctx > (1 << 24)) return fail(DFLASH_EUNSUPPORTED, "max_ctx too large");
@@ -116,32 +138,33 @@ void make_plan(const dflash_dims* d, Plan* p) {
 
   const int M = d->max_batch * d->B;
   const int Mlm = d->max_batch * (d->B - 1);
+  const int nslot = d->D / 16;
   p->BP = round_up(d->B, KS);
   p->qf = ceil_div((d->Hq / d->Hkv) * d->B, 16);
   if (p->qf == 3) p->qf = 4;
   off = 0;
   p->x_off = off;    off = align_up(off + (size_t)M * d->D * 4);
   p->u_off = off;    off = align_up(off + (size_t)M * d->D * e);
+  p->ssq_off = off;  off = align_up(off + (size_t)M * nslot * 4);
   p->q_off = off;    off = align_up(off + (size_t)M * d->Hq * d->hd * e);
   p->kb_off = off;   off = align_up(off + (size_t)M * d->Hkv * d->hd * e);
   p->vbt_off = off;  off = align_up(off + (size_t)d->max_batch * d->Hkv * d->hd * p->BP * e);
   p->o_off = off;    off = align_up(off + (size_t)M * d->Hq * d->hd * e);
   p->h_off = off;    off = align_up(off + (size_t)M * d->I * e);
-  p->ufin_off = off; off = align_up(off + (size_t)Mlm * d->D * e);
   const int qr = p->qf * 16;
   p->po_off = off;   off = align_up(off + (size_t)kAttnWorkMax * qr * d->hd * 4);
   p->pml_off = off;  off = align_up(off + (size_t)kAttnWorkMax * qr * 2 * 4);
   size_t lm = 0;
-  for (int m = 1; m <= Mlm; ++m) {
-    int tpw, nchunk, rb;
-    lm_shape(m, d->V, &tpw, &nchunk, &rb);
-    lm = std::max(lm, (size_t)nchunk * m * 16);
-  }
+  for (int m = 1; m <= Mlm; ++m)
+    lm = std::max(lm, std::max(lm_entries_for(m, d->V, 1), lm_entries_for(m, d->V, 16)));
   p->lm_entries = lm;
   p->lmv_off = off;  off = align_up(off + lm * 4);
   p->lmi_off = off;  off = align_up(off + lm * 4);
-  p->z_off = off;    off = align_up(off + (size_t)kFuseChunk * d->D * 4);
   p->hc_off = off;   off = align_up(off + (size_t)kFuseChunk * d->D * e);
+  p->hclo_off = off; off = align_up(off + (size_t)kFuseChunk * d->D * e);
+  p->fssq_off = off; off = align_up(off + (size_t)kFuseChunk * nslot * 4);
+  p->part_off = off; off = align_up(off + kPartFloats * 4);
+  p->ctr_off = off;  off = align_up(off + (size_t)kCounters * 4);
   p->ws_bytes = off;
 }
 
@@ -195,23 +218,64 @@ struct ProfScope {
   }
 };
 
-// ------------------------------------------------------------------ launches
+// ------------------------------------------------------------------ GEMM dispatch
 
-template <typename T, class Epi>
-void launch_gemm(const WOperand<T>& w, const AOperand<T>& a, const Epi& epi, hipStream_t st) {
+template <typename T, bool ALO = false, class Epi>
+void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
+                 hipStream_t st) {
   if (a.M <= 0 || w.ngroups <= 0) return;
-  if (a.M <= 32) {
-    constexpr int FM = 1, FN = Epi::kPaired ? 2 : 1, WM = 1, WN = 1, WK = 4, U = 8;
-    const int tiles_n = ceil_div(w.ngroups, FN * WN);
-    const int tiles_m = ceil_div(a.M, 16 * FM * WM);
-    hipLaunchKernelGGL((gemm_kernel<T, FM, FN, WM, WN, WK, U, Epi>), dim3(tiles_n * tiles_m),
-                       dim3(64 * WM * WN * WK), 0, st, w, a, epi);
+  float* part = c->wsp<float>(c->p.part_off);
+  int* ctr = c->wsp<int>(c->p.ctr_off);
+  const int K = a.nk * a.kseg;
+  if (a.M <= kSkinnyMaxM) {
+    // K is split only across the waves of a work-group (LDS reduction): a
+    // cross-work-group split needs device-scope fences, which write back and
+    // invalidate the XCD's L2 and cost more than they save here.
+    constexpr int FN = Epi::kPaired ? kGemvFNPaired : kGemvFNUnpaired;
+    constexpr int U = kGemvBytes / FN;
+    const int nks = K / Mma<T>::KSTEP;
+    const int tiles = ceil_div(w.ngroups, FN) * ceil_div(a.M, 16);
+    const int want = ceil_div(kGemvTargetWaves, tiles);
+    const int kmax = std::max(1, nks / U);  // waves that still get a full run of U k-steps
+    const int wk = std::min(want, kmax);
+    const SplitK sk{1, nks, part, ctr};
+    if (wk >= 12)
+      hipLaunchKernelGGL((gemv_kernel<T, FN, 16, U, ALO, Epi>), dim3(tiles), dim3(64 * 16), 0, st, w, a, nrm, sk, epi);
+    else if (wk >= 6)
+      hipLaunchKernelGGL((gemv_kernel<T, FN, 8, U, ALO, Epi>), dim3(tiles), dim3(64 * 8), 0, st, w, a, nrm, sk, epi);
+    else
+      hipLaunchKernelGGL((gemv_kernel<T, FN, 4, U, ALO, Epi>), dim3(tiles), dim3(64 * 4), 0, st, w, a, nrm, sk, epi);
   } else {
-    constexpr int FM = 4, FN = 4, WM = 2, WN = 2, WK = 1, U = 2;
-    const int tiles_n = ceil_div(w.ngroups, FN * WN);
-    const int tiles_m = ceil_div(a.M, 16 * FM * WM);
-    hipLaunchKernelGGL((gemm_kernel<T, FM, FN, WM, WN, WK, U, Epi>), dim3(tiles_n * tiles_m),
-                       dim3(64 * WM * WN * WK), 0, st, w, a, epi);
+    constexpr int BKE = 128 / sizeof(T);
+    const int nst = K / BKE;
+    const int MT = ceil_div(a.M, kTBM), NT = ceil_div(w.ngroups, kTBN / 16);
+    const int tiles = MT * NT;
+    // Split K to fill the machine: minimise (rounds of kTiledSlots) x (stages per split).
+    int best = 1;
+    long long best_cost = -1;
+    for (int sk_try = 1; sk_try <= std::max(1, nst / 8); ++sk_try) {
+      const int kps = ceil_div(nst, sk_try);
+      const int skr = ceil_div(nst, kps);
+      if (skr > 1 && ((size_t)tiles * skr * kTBM * kTBN > kPartFloats || tiles > kCounters)) break;
+      const long long cost = (long long)ceil_div(tiles * skr, kTiledSlots) * kps;
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best = skr;
+      }
+    }
+    const int kps = ceil_div(nst, best);
+    const int SK = ceil_div(nst, kps);
+    const SplitK sk{SK, kps, part, ctr};
+    const int nblocks = tiles * SK;
+    const int lds = 2 * ((ALO ? 2 : 1) * kTBM + kTBN) * (128 + 16);
+    auto kern = gemm_tiled_kernel<T, kTBM, kTBN, 2, 2, ALO, Epi>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds);
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(round_up(nblocks, 8)), dim3(256), lds, st, w, a, nrm, sk, epi, nblocks);
   }
 }
 
@@ -232,22 +296,30 @@ WOperand<T> wop(std::initializer_list<std::pair<const void*, int>> segs, int pai
 }
 
 template <typename T>
-AOperand<T> aop(const void* p, int M, int K) {
+AOperand<T> aop(const void* p, int M, int K, int rowmap_b = 0) {
   AOperand<T> a{};
   a.ptr[0] = static_cast<const T*>(p);
   a.nk = 1;
   a.kseg = K;
   a.lda = K;
   a.M = M;
+  a.rowmap_b = rowmap_b;
   return a;
 }
+
+NormIn norm_in(const float* ssq, int D, float eps) { return NormIn{ssq, D / 16, 1.0f / (float)D, eps}; }
+
+// ------------------------------------------------------------------ fuse
 
 template <typename T>
 void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, const void* const* hid) {
   const dflash_dims& d = c->d;
   const Plan& p = c->p;
-  float* z = c->wsp<float>(p.z_off);
   T* hc = c->wsp<T>(p.hc_off);
+  // bf16: H_c is kept as hi + lo bf16 planes so the context K/V projection
+  // sees it at near-fp32 precision (that GEMM is small next to the fusion).
+  T* hclo = sizeof(T) == 2 ? c->wsp<T>(p.hclo_off) : nullptr;
+  float* fssq = c->wsp<float>(p.fssq_off);
   T* pool = reinterpret_cast<T*>(c->pool + p.kv_off);
   const float2* rope = reinterpret_cast<const float2*>(c->pool + p.rope_off);
 
@@ -267,6 +339,7 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
     wkv.pair = d.hd / 2;
     wkv.ngroups = end / 16;
   }
+  const NormIn none{nullptr, 0, 0.f, 0.f};
   for (int base = 0; base < total; base += kFuseChunk) {
     const int rows = std::min(kFuseChunk, total - base);
     AOperand<T> a{};
@@ -277,12 +350,8 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
     a.M = rows;
     {
       ProfScope ps(c, DFLASH_K_FUSE_GEMM, st);
-      launch_gemm<T>(wc, a, EpiStoreF32{z, d.D}, st);
-    }
-    {
-      ProfScope ps(c, DFLASH_K_FUSE_NORM, st);
-      hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(rows), dim3(256), 0, st, z,
-                         static_cast<const T*>(c->w.g_c), hc, d.D, d.rms_eps, 0, d.B);
+      launch_gemm<T>(c, wc, a, none, EpiNormOut<T>{hc, hclo, static_cast<const T*>(c->w.g_c), fssq, d.D, d.D / 16},
+                     st);
     }
     EpiKVAppend<T> epi{};
     epi.pool = pool;
@@ -298,9 +367,17 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
     epi.row_base = base;
     epi.meta = fm;
     ProfScope ps(c, DFLASH_K_CTX_KV_GEMM, st);
-    launch_gemm<T>(wkv, aop<T>(hc, rows, d.D), epi, st);
+    AOperand<T> ah = aop<T>(hc, rows, d.D);
+    if (hclo) {
+      ah.lo_off = (long)(hclo - hc);
+      launch_gemm<T, true>(c, wkv, ah, norm_in(fssq, d.D, d.rms_eps), epi, st);
+    } else {
+      launch_gemm<T>(c, wkv, ah, norm_in(fssq, d.D, d.rms_eps), epi, st);
+    }
   }
 }
+
+// ------------------------------------------------------------------ attention
 
 template <typename T, int HD, int QF>
 void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
@@ -322,30 +399,22 @@ void attn_dispatch(const AttnArgs<T>& a, int work, int hd, int qf, hipStream_t s
   }
 }
 
-template <typename T, int FM, int KTOP>
-void launch_lm(const LmArgs<T>& a, int nchunk, int rowblocks, hipStream_t st) {
-  constexpr int U = FM == 1 ? 8 : 4;
-  hipLaunchKernelGGL((lmhead_kernel<T, FM, KTOP, kLmWV, U>), dim3(nchunk, rowblocks), dim3(64 * kLmWV),
-                     0, st, a);
-}
-
 struct AttnPlan {
   int chunk, work;
   AttnMeta meta;
 };
 
-int plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPlan* ap) {
+void plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPlan* ap) {
   const dflash_dims& d = c->d;
   // Splits of at least kAttnMinChunk keys (partial results stay small next to
   // the K/V they summarise), about kAttnTargetWG work-groups per call.
   long long total = 0;
   for (int r = 0; r < n_req; ++r) total += c->len[slot[r]];
-  int chunk = round_up((int)std::max<long long>(1, (total * d.Hkv + kAttnTargetWG - 1) / kAttnTargetWG), 32);
+  int chunk = round_up(std::max(1, ceil_div_l(total * d.Hkv, kAttnTargetWG)), 32);
   chunk = std::max(chunk, kAttnMinChunk);
   for (;;) {
     long long work = 0;
-    for (int r = 0; r < n_req; ++r)
-      work += (long long)d.Hkv * std::max(1, ceil_div(c->len[slot[r]], chunk));
+    for (int r = 0; r < n_req; ++r) work += (long long)d.Hkv * std::max(1, ceil_div(c->len[slot[r]], chunk));
     if (work <= kAttnWorkMax) {
       ap->chunk = chunk;
       ap->work = (int)work;
@@ -365,8 +434,51 @@ int plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPlan
     w += d.Hkv * m.nsplit[r];
   }
   m.work0[n_req] = w;
-  return DFLASH_OK;
 }
+
+// ------------------------------------------------------------------ LM head
+
+template <typename T, int KTOP>
+void launch_lm_small(const LmArgs<T>& la, int nchunk, int rowblocks, hipStream_t st) {
+  hipLaunchKernelGGL((lmhead_kernel<T, KTOP, kLmWV, kLmFN, kLmU>), dim3(nchunk, rowblocks), dim3(64 * kLmWV), 0,
+                     st, la);
+}
+
+template <typename T>
+void run_lmhead(dflash_ctx* c, hipStream_t st, int n_req, int top_k, int32_t* out_ids, float* out_vals,
+                float* out_logits) {
+  const dflash_dims& d = c->d;
+  const Plan& p = c->p;
+  const int Mlm = n_req * (d.B - 1);
+  float* pv = c->wsp<float>(p.lmv_off);
+  int* pi = c->wsp<int>(p.lmi_off);
+  const AOperand<T> a = aop<T>(c->wsp<T>(p.u_off), Mlm, d.D, d.B);
+  const NormIn nrm = norm_in(c->wsp<float>(p.ssq_off), d.D, d.rms_eps);
+  int nchunk;
+  {
+    ProfScope ps(c, DFLASH_K_LM_HEAD, st);
+    if (top_k == 1 && Mlm > kSkinnyMaxM) {
+      nchunk = ceil_div(d.V, kTBN / 2);
+      EpiTop1 epi{pv, pi, out_logits, Mlm, d.V};
+      launch_gemm<T>(c, wop<T>({{c->w.w_lm, d.V}}, 0), a, nrm, epi, st);
+    } else {
+      int tpw, rowblocks;
+      lm_shape_small(Mlm, d.V, &tpw, &nchunk, &rowblocks);
+      LmArgs<T> la{a, nrm, static_cast<const T*>(c->w.w_lm), d.V, tpw, out_logits, pv, pi};
+      if (top_k == 1) launch_lm_small<T, 1>(la, nchunk, rowblocks, st);
+      else launch_lm_small<T, 16>(la, nchunk, rowblocks, st);
+    }
+  }
+  ProfScope ps(c, DFLASH_K_TOPK_MERGE, st);
+  if (top_k == 1)
+    hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, Mlm, top_k, out_ids,
+                       out_vals);
+  else
+    hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, Mlm, top_k,
+                       out_ids, out_vals);
+}
+
+// ------------------------------------------------------------------ draft
 
 template <typename T>
 void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, const int32_t* anchor,
@@ -374,16 +486,18 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   const dflash_dims& d = c->d;
   const Plan& p = c->p;
   const int M = n_req * d.B;
-  const int Mlm = n_req * (d.B - 1);
   float* x = c->wsp<float>(p.x_off);
   T* u = c->wsp<T>(p.u_off);
+  float* ssq = c->wsp<float>(p.ssq_off);
   T* q = c->wsp<T>(p.q_off);
   T* kb = c->wsp<T>(p.kb_off);
   T* vbT = c->wsp<T>(p.vbt_off);
   T* o = c->wsp<T>(p.o_off);
   T* h = c->wsp<T>(p.h_off);
-  T* ufin = c->wsp<T>(p.ufin_off);
   const float2* rope = reinterpret_cast<const float2*>(c->pool + p.rope_off);
+  const NormIn nrm = norm_in(ssq, d.D, d.rms_eps);
+  const NormIn none{nullptr, 0, 0.f, 0.f};
+  const int nslot = d.D / 16;
 
   DraftMeta dm{};
   dm.n_req = n_req;
@@ -393,7 +507,8 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   {
     ProfScope ps(c, DFLASH_K_EMBED, st);
     hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(c->w.embed),
-                       static_cast<const T*>(c->w.e_mask), anchor, d.B, d.D, d.V, x);
+                       static_cast<const T*>(c->w.e_mask), anchor, static_cast<const T*>(c->layers[0].g_attn), d.B,
+                       d.D, d.V, x, u, ssq);
   }
 
   AttnArgs<T> aa{};
@@ -421,11 +536,7 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   const int qd = d.Hq * d.hd, kd = d.Hkv * d.hd;
   for (int l = 0; l < d.N; ++l) {
     const dflash_layer_weights& lw = c->layers[l];
-    {
-      ProfScope ps(c, DFLASH_K_NORM, st);
-      hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
-                         static_cast<const T*>(lw.g_attn), u, d.D, d.rms_eps, 0, d.B);
-    }
+    const T* g_next = static_cast<const T*>(l + 1 < d.N ? c->layers[l + 1].g_attn : c->w.g_final);
     EpiQKV<T> eq{};
     eq.q = q;
     eq.kb = kb;
@@ -439,7 +550,7 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     eq.meta = dm;
     {
       ProfScope ps(c, DFLASH_K_QKV_GEMM, st);
-      launch_gemm<T>(wop<T>({{lw.w_q, qd}, {lw.w_kb, kd}, {lw.w_vb, kd}}, d.hd / 2), aop<T>(u, M, d.D),
+      launch_gemm<T>(c, wop<T>({{lw.w_q, qd}, {lw.w_kb, kd}, {lw.w_vb, kd}}, d.hd / 2), aop<T>(u, M, d.D), nrm,
                      eq, st);
     }
     aa.layer = l;
@@ -449,61 +560,21 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     }
     {
       ProfScope ps(c, DFLASH_K_O_GEMM, st);
-      launch_gemm<T>(wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), EpiResidual{x, d.D}, st);
-    }
-    {
-      ProfScope ps(c, DFLASH_K_NORM, st);
-      hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(M), dim3(256), 0, st, x,
-                         static_cast<const T*>(lw.g_ffn), u, d.D, d.rms_eps, 0, d.B);
+      launch_gemm<T>(c, wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), none,
+                     EpiResidualNorm<T>{x, u, static_cast<const T*>(lw.g_ffn), ssq, d.D, nslot}, st);
     }
     {
       ProfScope ps(c, DFLASH_K_GATEUP_GEMM, st);
-      launch_gemm<T>(wop<T>({{lw.w_gate, d.I}, {lw.w_up, d.I}}, d.I), aop<T>(u, M, d.D),
+      launch_gemm<T>(c, wop<T>({{lw.w_gate, d.I}, {lw.w_up, d.I}}, d.I), aop<T>(u, M, d.D), nrm,
                      EpiSwiGLU<T>{h, d.I}, st);
     }
     {
       ProfScope ps(c, DFLASH_K_DOWN_GEMM, st);
-      launch_gemm<T>(wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), EpiResidual{x, d.D}, st);
+      launch_gemm<T>(c, wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), none,
+                     EpiResidualNorm<T>{x, u, g_next, ssq, d.D, nslot}, st);
     }
   }
-  {
-    ProfScope ps(c, DFLASH_K_NORM, st);
-    hipLaunchKernelGGL((rmsnorm_kernel<T, float>), dim3(Mlm), dim3(256), 0, st, x,
-                       static_cast<const T*>(c->w.g_final), ufin, d.D, d.rms_eps, 1, d.B);
-  }
-
-  int tpw, nchunk, rowblocks;
-  lm_shape(Mlm, d.V, &tpw, &nchunk, &rowblocks);
-  LmArgs<T> la{};
-  la.u = ufin;
-  la.w = static_cast<const T*>(c->w.w_lm);
-  la.M = Mlm;
-  la.V = d.V;
-  la.D = d.D;
-  la.tpw = tpw;
-  la.logits = out_logits;
-  la.part_v = c->wsp<float>(p.lmv_off);
-  la.part_i = c->wsp<int>(p.lmi_off);
-  const bool small = lm_rows_per_wg(Mlm) == 16;
-  {
-    ProfScope ps(c, DFLASH_K_LM_HEAD, st);
-    if (top_k == 1) {
-      if (small) launch_lm<T, 1, 1>(la, nchunk, rowblocks, st);
-      else launch_lm<T, 4, 1>(la, nchunk, rowblocks, st);
-    } else {
-      if (small) launch_lm<T, 1, 16>(la, nchunk, rowblocks, st);
-      else launch_lm<T, 4, 16>(la, nchunk, rowblocks, st);
-    }
-  }
-  {
-    ProfScope ps(c, DFLASH_K_TOPK_MERGE, st);
-    if (top_k == 1)
-      hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i, nchunk,
-                         Mlm, top_k, out_ids, out_vals);
-    else
-      hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, la.part_v, la.part_i,
-                         nchunk, Mlm, top_k, out_ids, out_vals);
-  }
+  run_lmhead<T>(c, st, n_req, top_k, out_ids, out_vals, out_logits);
 }
 
 }  // namespace
@@ -717,9 +788,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32
   AttnPlan apl;
   plan_attention(ctx, n_req, slot, &apl);
   const int Mlm = n_req * (ctx->d.B - 1);
-  int tpw, nchunk, rb;
-  lm_shape(Mlm, ctx->d.V, &tpw, &nchunk, &rb);
-  if ((size_t)nchunk * Mlm * 16 > ctx->p.lm_entries)
+  if (lm_entries_for(Mlm, ctx->d.V, top_k) > ctx->p.lm_entries)
     return fail(DFLASH_ECAPACITY, "LM-head partial buffer too small");
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (ctx->d.dtype == DFLASH_BF16)

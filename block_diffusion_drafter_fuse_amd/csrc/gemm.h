@@ -1,20 +1,22 @@
-// MFMA GEMM  C[m, f] = sum_k A[m, k] * W[f, k]  with fused epilogues.
+// Operands, fused epilogues and the skinny (few-token) MFMA GEMM.
+//
+//   C[m, f] = s_m * sum_k A[m, k] * W[f, k]
 //
 // W is a "virtual" weight: the concatenation of up to kMaxSeg [rows, K]
 // matrices (e.g. [W_q; W_kb; W_vb]).  A is [M, K] with K optionally split into
 // segments at separate addresses (the L tapped target layers of the fusion
-// step, concatenated along features without a copy).
+// step are read in place).  s_m is an optional per-row RMSNorm scale
+// rsqrt(mean(x_m^2) + eps): the producer of A already multiplied x by the
+// norm gain and left per-16-feature sums of squares, so the norm costs the
+// consumer one short reduction in its epilogue and no extra pass.
 //
-// Each wave owns FM x FN MFMA tiles (16 tokens x 16 features each): W rows are
-// the 16-row MFMA A operand, activation rows the 16-column B operand, so a lane
-// ends up holding 4 consecutive features of one token.  Operands are loaded
-// straight from global memory with 16-byte loads (W is streamed once, A is
-// small and cache-resident).  A work-group holds WM x WN x WK waves; the WK
-// waves split K and are reduced through LDS in a fixed order (deterministic).
+// MFMA orientation: W rows are the 16-row A operand and activation rows the
+// 16-column B operand, so a lane ends up holding 4 consecutive features of one
+// token (C[4*(l>>4) + i][l & 15]).
 //
-// Paired epilogues (RoPE, SwiGLU) need feature f and its partner f + P in the
-// same lane: with a pair distance P, 16-feature groups 2i and 2i+1 map to
-// features (first half) and (first half + P).
+// Paired epilogues (RoPE, SwiGLU) need feature f and its partner f + P in one
+// lane: with a pair distance P, 16-feature groups 2i and 2i+1 map to features
+// (first half) and (first half + P).
 #pragma once
 #include "common.h"
 
@@ -45,137 +47,55 @@ struct WOperand {
 template <typename T>
 struct AOperand {
   const T* ptr[kMaxKSeg];
-  int nk;    // K segments
-  int kseg;  // columns per segment (multiple of the MFMA k-step)
-  int lda;   // row stride (elements)
-  int M;     // rows
+  int nk;        // K segments
+  int kseg;      // columns per segment (multiple of the MFMA k-step)
+  int lda;       // row stride (elements)
+  int M;         // logical rows
+  int rowmap_b;  // 0: identity; B > 1: logical row i reads row (i/(B-1))*B + 1 + i%(B-1)
+  long lo_off;   // element offset of the low-half plane (split activations), 0 if none
+  __device__ __forceinline__ int row(int i) const {
+    if (!rowmap_b) return i;
+    const int r = i / (rowmap_b - 1);
+    return r * rowmap_b + 1 + (i - r * (rowmap_b - 1));
+  }
 };
 
-template <typename T, int FM, int FN, int WM, int WN, int WK, int U, class Epi>
-__global__ __launch_bounds__(64 * WM * WN * WK) void gemm_kernel(const WOperand<T> w,
-                                                                  const AOperand<T> a,
-                                                                  const Epi epi) {
-  using MM = Mma<T>;
-  constexpr int KS = MM::KSTEP;
-  constexpr int EPL = MM::EPL;
-  static_assert(!Epi::kPaired || (FN % 2 == 0), "paired epilogue needs even FN");
+// RMSNorm folded into a consumer: sums of squares per (row, 16-feature slot).
+struct NormIn {
+  const float* ssq;  // nullable: no row scale
+  int nslot;         // D / 16
+  float inv_d, eps;
+};
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wk = wave % WK;
-  const int wn = (wave / WK) % WN;
-  const int wm = wave / (WK * WN);
-  const int r16 = lane & 15, kg = lane >> 4;
-
-  const int gpb = FN * WN;
-  const int tiles_n = (w.ngroups + gpb - 1) / gpb;
-  const int bn = blockIdx.x % tiles_n;
-  const int bm = blockIdx.x / tiles_n;
-  const int m0 = (bm * WM + wm) * 16 * FM;
-  const int g0 = (bn * WN + wn) * FN;
-  const int K = a.nk * a.kseg;
-
-  const T* wp[FN];
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const int gi = g0 + fn;
-    const int f = gi < w.ngroups ? w.feature_of_group(gi) + r16 : r16;
-    wp[fn] = w.row(f, K) + kg * EPL;
+// Row scale for this lane's token row `arow` (physical row); all 64 lanes of
+// the wave must call it.  The 4 lanes of a token (same l & 15) each sum a
+// contiguous quarter of the slots and combine with two butterflies.
+__device__ __forceinline__ float norm_scale(const NormIn& n, int arow, int kg) {
+  if (!n.ssq) return 1.0f;
+  const int q = n.nslot >> 2;  // slots per lane (nslot is a multiple of 4)
+  const float* p = n.ssq + (size_t)arow * n.nslot + kg * q;
+  float s = 0.f;
+  int j = 0;
+  for (; j + 4 <= q; j += 4) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + j);
+    s += (v[0] + v[1]) + (v[2] + v[3]);
   }
-  int arow[FM];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + fm * 16 + r16;
-    arow[fm] = m < a.M ? m : a.M - 1;
-  }
-
-  f32x4_t acc[FM][FN];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int nks = a.kseg / KS;
-  const int nfull = (nks / U) * U;
-  for (int s = 0; s < a.nk; ++s) {
-    const T* ap[FM];
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) ap[fm] = a.ptr[s] + (size_t)arow[fm] * a.lda + kg * EPL;
-    const T* wps[FN];
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) wps[fn] = wp[fn] + (size_t)s * a.kseg;
-
-    for (int ks = wk * U; ks + U <= nfull; ks += WK * U) {
-      uint4 wf[U][FN], af[U][FM];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) wf[u][fn] = ld16_stream(wps[fn] + (ks + u) * KS);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) af[u][fm] = ld16(ap[fm] + (ks + u) * KS);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::step(wf[u][fn], af[u][fm], acc[fm][fn]);
-    }
-    for (int ks = nfull + wk; ks < nks; ks += WK) {
-      uint4 wf[FN], af[FM];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) wf[fn] = ld16_stream(wps[fn] + ks * KS);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm) af[fm] = ld16(ap[fm] + ks * KS);
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = MM::step(wf[fn], af[fm], acc[fm][fn]);
-    }
-  }
-
-  if constexpr (WK > 1) {
-    __shared__ f32x4_t red[WM * WN][WK - 1][FM * FN][64];
-    const int wmn = wm * WN + wn;
-    if (wk > 0) {
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) red[wmn][wk - 1][fm * FN + fn][lane] = acc[fm][fn];
-    }
-    __syncthreads();
-    if (wk != 0) return;
-    for (int j = 0; j < WK - 1; ++j)
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] += red[wmn][j][fm * FN + fn][lane];
-  }
-
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + fm * 16 + r16;
-    if (m >= a.M) continue;
-    if constexpr (Epi::kPaired) {
-#pragma unroll
-      for (int fn = 0; fn < FN; fn += 2) {
-        const int gi = g0 + fn;
-        if (gi >= w.ngroups) continue;
-        epi.pair(m, w.feature_of_group(gi) + 4 * kg, acc[fm][fn], acc[fm][fn + 1]);
-      }
-    } else {
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        const int gi = g0 + fn;
-        if (gi >= w.ngroups) continue;
-        epi.single(m, w.feature_of_group(gi) + 4 * kg, acc[fm][fn]);
-      }
-    }
-  }
+  for (; j < q; ++j) s += p[j];
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  return 1.0f / sqrtf(s * n.inv_d + n.eps);
 }
 
-// ---------------------------------------------------------------- epilogues
+// Split-K across work-groups: the last work-group of a tile to finish sums
+// the partials in split order and runs the epilogue.
+struct SplitK {
+  int SK;       // splits
+  int kps;      // k-steps per split
+  float* part;  // [tiles][SK][FN * 256]
+  int* ctr;     // [tiles], zero between launches (reset by the last arriver)
+};
+
+// ---------------------------------------------------------------- helpers
 
 template <typename T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
@@ -191,40 +111,99 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* p, float a, float b, floa
   *reinterpret_cast<uint2*>(p) = v;
 }
 
-// out[m, f..f+3] = acc (fp32)
-struct EpiStoreF32 {
+template <typename T>
+__device__ __forceinline__ f32x4_t load4(const T* p);
+template <>
+__device__ __forceinline__ f32x4_t load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4_t*>(p);
+}
+template <>
+__device__ __forceinline__ f32x4_t load4<bf16_t>(const bf16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return f32x4_t{bf2f((bf16_t)(v.x & 0xffff)), bf2f((bf16_t)(v.x >> 16)), bf2f((bf16_t)(v.y & 0xffff)),
+                 bf2f((bf16_t)(v.y >> 16))};
+}
+
+// x rounded to the storage type, back in float.
+template <typename T>
+__device__ __forceinline__ float round_to(float x) {
+  return to_f<T>(from_f<T>(x));
+}
+
+// Sum over the 4 lanes holding one token (fixed butterfly order).
+__device__ __forceinline__ float token_sum(float s) {
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  return s;
+}
+
+// ---------------------------------------------------------------- epilogues
+// Unpaired: apply1(m, valid, f, v) - v holds features f..f+3 of row m (this
+// lane's part of one 16-feature fragment).  Paired: apply2(m, valid, f, a, b)
+// - a holds features f..f+3, b the partners f+P..f+P+3.  Every lane calls
+// the epilogue (shuffles inside); stores are guarded by `valid`.
+
+// Fusion output: u = T(z * g) (plus the low half z*g - u when lo != 0), and
+// per-16-feature sums of squares of z.
+template <typename T>
+struct EpiNormOut {
   static constexpr bool kPaired = false;
-  float* out;
-  int ldo;
-  __device__ __forceinline__ void single(int m, int f, f32x4_t v) const {
-    *reinterpret_cast<f32x4_t*>(out + (size_t)m * ldo + f) = v;
+  static constexpr bool kRow = false;
+  T* u;
+  T* lo;  // nullable low-half plane
+  const T* g;
+  float* ssq;
+  int ld, nslot;
+  __device__ __forceinline__ void apply1(int m, bool valid, int f, f32x4_t v) const {
+    const float ss = token_sum(v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3]);
+    if (!valid) return;
+    const f32x4_t gg = load4<T>(g + f);
+    const f32x4_t y = v * gg;
+    store4<T>(u + (size_t)m * ld + f, y[0], y[1], y[2], y[3]);
+    if (lo)
+      store4<T>(lo + (size_t)m * ld + f, y[0] - round_to<T>(y[0]), y[1] - round_to<T>(y[1]),
+                y[2] - round_to<T>(y[2]), y[3] - round_to<T>(y[3]));
+    if ((threadIdx.x & 63) < 16) ssq[(size_t)m * nslot + (f >> 4)] = ss;
   }
 };
 
-// x[m, f..f+3] += acc (fp32 residual stream)
-struct EpiResidual {
+// Residual: x += v; u = T(x * g_next); per-16-feature sums of squares of x.
+template <typename T>
+struct EpiResidualNorm {
   static constexpr bool kPaired = false;
+  static constexpr bool kRow = false;
   float* x;
-  int ldx;
-  __device__ __forceinline__ void single(int m, int f, f32x4_t v) const {
-    f32x4_t* p = reinterpret_cast<f32x4_t*>(x + (size_t)m * ldx + f);
-    *p = *p + v;
+  T* u;
+  const T* g;
+  float* ssq;
+  int ld, nslot;
+  __device__ __forceinline__ void apply1(int m, bool valid, int f, f32x4_t v) const {
+    f32x4_t* xp = reinterpret_cast<f32x4_t*>(x + (size_t)m * ld + f);
+    const f32x4_t xn = valid ? *xp + v : v;
+    const float ss = token_sum(xn[0] * xn[0] + xn[1] * xn[1] + xn[2] * xn[2] + xn[3] * xn[3]);
+    if (!valid) return;
+    *xp = xn;
+    const f32x4_t gg = load4<T>(g + f);
+    store4<T>(u + (size_t)m * ld + f, xn[0] * gg[0], xn[1] * gg[1], xn[2] * gg[2], xn[3] * gg[3]);
+    if ((threadIdx.x & 63) < 16) ssq[(size_t)m * nslot + (f >> 4)] = ss;
   }
 };
 
-// h[m, f] = SiLU(gate) * up, gate rows first, up rows at +I
+// h[m, f] = SiLU(gate) * up; the pair is (gate, up).
 template <typename T>
 struct EpiSwiGLU {
   static constexpr bool kPaired = true;
+  static constexpr bool kRow = false;
   T* h;
   int ldh;
-  __device__ __forceinline__ void pair(int m, int f, f32x4_t g, f32x4_t u) const {
+  __device__ __forceinline__ void apply2(int m, bool valid, int f, f32x4_t g, f32x4_t u) const {
+    if (!valid) return;
     store4<T>(h + (size_t)m * ldh + f, silu(g[0]) * u[0], silu(g[1]) * u[1], silu(g[2]) * u[2],
               silu(g[3]) * u[3]);
   }
 };
 
-// Rotate-half RoPE of a channel pair (c, c + hd/2) at table row `pos`.
+// Rotate-half RoPE of channel pairs (c, c + hd/2) at table row `pos`.
 __device__ __forceinline__ void rope4(const float2* tab, int half, int pos, int c, int use, f32x4_t& a,
                                       f32x4_t& b) {
   if (!use) return;
@@ -244,13 +223,14 @@ __device__ __forceinline__ void rope4(const float2* tab, int half, int pos, int 
 template <typename T>
 struct EpiQKV {
   static constexpr bool kPaired = true;
+  static constexpr bool kRow = false;
   T* q;
   T* kb;
   T* vbT;
   const float2* rope;
   int Hq, Hkv, hd, BP, use_rope;
   DraftMeta meta;
-  __device__ __forceinline__ void pair(int m, int f, f32x4_t a, f32x4_t b) const {
+  __device__ __forceinline__ void one(int m, int f, f32x4_t a, f32x4_t b) const {
     const int B = meta.B;
     const int r = m / B, j = m - r * B;
     const int qd = Hq * hd, kd = Hkv * hd, half = hd >> 1;
@@ -271,21 +251,25 @@ struct EpiQKV {
       }
     }
   }
+  __device__ __forceinline__ void apply2(int m, bool valid, int f, f32x4_t a, f32x4_t b) const {
+    if (valid) one(m, f, a, b);
+  }
 };
 
 // Context projections of the fusion step: virtual weight
 // [W_kc^0; W_vc^0; W_kc^1; W_vc^1; ...], pair distance hd/2.  Keys are rotated
 // at their absolute positions and written row-major into the slot's cache;
-// values are written transposed (cache layout [Hkv][hd][max_ctx_pad]).
+// values are written transposed (cache layout [Hkv][hd][ctx_pad]).
 template <typename T>
 struct EpiKVAppend {
   static constexpr bool kPaired = true;
+  static constexpr bool kRow = false;
   T* pool;
   size_t slot_stride, layer_stride, kv_stride, head_stride;
   const float2* rope;
   int Hkv, hd, ctx_pad, use_rope, row_base;
   FuseMeta meta;
-  __device__ __forceinline__ void pair(int m, int f, f32x4_t a, f32x4_t b) const {
+  __device__ __forceinline__ void one(int m, int f, f32x4_t a, f32x4_t b) const {
     const int per_layer = 2 * Hkv * hd;
     const int layer = f / per_layer;
     int rem = f - layer * per_layer;
@@ -310,6 +294,154 @@ struct EpiKVAppend {
       }
     }
   }
+  __device__ __forceinline__ void apply2(int m, bool valid, int f, f32x4_t a, f32x4_t b) const {
+    if (valid) one(m, f, a, b);
+  }
 };
+
+// ---------------------------------------------------------------- skinny GEMM
+//
+// One 16-token tile per work-group row; each wave owns FN 16-feature
+// fragments that share one activation fragment per k-step.  The WK waves of
+// a work-group split the k-steps of the group's K range in interleaved runs
+// of U and are reduced through LDS; SK work-groups split K further and meet
+// in the SplitK fixup.  Weights are streamed with non-temporal loads.  With
+// ALO the activations come as bf16 hi + lo planes and every weight fragment
+// feeds two MFMAs (near-fp32 activations for memory-bound GEMMs).
+
+template <typename T>
+__device__ __forceinline__ const T* a_ptr(const AOperand<T>& a, int arow, int kg, int ks) {
+  constexpr int KS = Mma<T>::KSTEP, EPL = Mma<T>::EPL;
+  if (a.nk == 1) return a.ptr[0] + (size_t)arow * a.lda + kg * EPL + (size_t)ks * KS;
+  const int nks_seg = a.kseg / KS;
+  const int seg = ks / nks_seg;
+  return a.ptr[seg] + (size_t)arow * a.lda + kg * EPL + (size_t)(ks - seg * nks_seg) * KS;
+}
+
+// Epilogue dispatch over a wave's FN fragments of one token row: pairs,
+// single fragments, or (kRow) all FN fragments at once.  Fragments j >=
+// nvalid lie past the last weight row and are not stored.
+template <int FN, class Epi>
+__device__ __forceinline__ void run_epilogue(const Epi& epi, int m, bool mvalid, int nvalid, const int (&fb)[FN],
+                                             const f32x4_t (&acc)[FN], float sc, int kg) {
+  if constexpr (Epi::kRow) {
+    epi.template apply_row<FN>(m, mvalid, nvalid, fb, acc, sc, kg);
+  } else if constexpr (Epi::kPaired) {
+#pragma unroll
+    for (int j = 0; j < FN; j += 2)
+      epi.apply2(m, mvalid && j + 1 < nvalid, fb[j] + 4 * kg, acc[j] * sc, acc[j + 1] * sc);
+  } else {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) epi.apply1(m, mvalid && j < nvalid, fb[j] + 4 * kg, acc[j] * sc);
+  }
+}
+
+template <typename T, int FN, int WK, int U, bool ALO, class Epi>
+__global__ __launch_bounds__(64 * WK) void gemv_kernel(const WOperand<T> w, const AOperand<T> a,
+                                                        const NormIn nrm, const SplitK sk, const Epi epi) {
+  using MM = Mma<T>;
+  constexpr int KS = MM::KSTEP;
+  constexpr int EPL = MM::EPL;
+  static_assert(!Epi::kPaired || FN % 2 == 0, "paired epilogue needs even FN");
+  const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
+  const int r16 = lane & 15, kg = lane >> 4;
+  const int ngt = (w.ngroups + FN - 1) / FN;
+  int b = blockIdx.x;
+  const int s = b % sk.SK;
+  b /= sk.SK;
+  const int tg = b % ngt, mt = b / ngt;
+  const int m0 = mt * 16, g0 = tg * FN;
+  const int K = a.nk * a.kseg;
+  const int nks = K / KS;
+  const int k0 = s * sk.kps, k1 = min(nks, k0 + sk.kps);
+
+  const T* wp[FN];
+  int fbase[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int gi = g0 + fn;
+    fbase[fn] = gi < w.ngroups ? w.feature_of_group(gi) : 0;
+    wp[fn] = w.row(fbase[fn] + r16, K) + kg * EPL;
+  }
+  const int m = m0 + r16;
+  const int arow = a.row(m < a.M ? m : a.M - 1);
+
+  f32x4_t acc[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = k0 + wk * U; kb < k1; kb += WK * U) {
+    if (kb + U <= k1) {
+      uint4 wf[U][FN], af[U], al[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) wf[u][fn] = ld16_stream(wp[fn] + (size_t)(kb + u) * KS);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const T* ap = a_ptr(a, arow, kg, kb + u);
+        af[u] = ld16(ap);
+        if constexpr (ALO) al[u] = ld16(ap + a.lo_off);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          acc[fn] = MM::step(wf[u][fn], af[u], acc[fn]);
+          if constexpr (ALO) acc[fn] = MM::step(wf[u][fn], al[u], acc[fn]);
+        }
+    } else {
+      for (int ks = kb; ks < k1; ++ks) {
+        const T* ap = a_ptr(a, arow, kg, ks);
+        const uint4 af = ld16(ap);
+        uint4 al;
+        if constexpr (ALO) al = ld16(ap + a.lo_off);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+          const uint4 wf = ld16_stream(wp[fn] + (size_t)ks * KS);
+          acc[fn] = MM::step(wf, af, acc[fn]);
+          if constexpr (ALO) acc[fn] = MM::step(wf, al, acc[fn]);
+        }
+      }
+    }
+  }
+
+  if constexpr (WK > 1) {
+    __shared__ f32x4_t red[WK - 1][FN][64];
+    if (wk > 0) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) red[wk - 1][fn][lane] = acc[fn];
+    }
+    __syncthreads();
+    if (wk != 0) return;
+    for (int j = 0; j < WK - 1; ++j)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fn] += red[j][fn][lane];
+  }
+
+  if (sk.SK > 1) {
+    const int tile = mt * ngt + tg;
+    float* pbase = sk.part + (size_t)tile * sk.SK * (FN * 256);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      *reinterpret_cast<f32x4_t*>(pbase + (size_t)s * (FN * 256) + fn * 256 + lane * 4) = acc[fn];
+    __threadfence();
+    int prev = 0;
+    if (lane == 0) prev = atomicAdd(sk.ctr + tile, 1);
+    prev = __shfl(prev, 0);
+    if (prev != sk.SK - 1) return;
+    __threadfence();
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < sk.SK; ++j)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        acc[fn] += *reinterpret_cast<const f32x4_t*>(pbase + (size_t)j * (FN * 256) + fn * 256 + lane * 4);
+    if (lane == 0) sk.ctr[tile] = 0;
+  }
+
+  const float sc = norm_scale(nrm, arow, kg);
+  run_epilogue<FN>(epi, m, m < a.M, w.ngroups - g0, fbase, acc, sc, kg);
+}
 
 }  // namespace dfl

@@ -7,7 +7,7 @@
 // lists are merged across lanes and waves in LDS and written per work-group
 // as partial lists, which a second kernel merges per row.
 #pragma once
-#include "common.h"
+#include "gemm.h"
 
 namespace dfl {
 
@@ -35,127 +35,166 @@ __device__ __forceinline__ void tk_insert(float (&lv)[K], int (&li)[K], float v,
 
 template <typename T>
 struct LmArgs {
-  const T* u;       // [M, D] normed final states of offsets 1..B-1
+  AOperand<T> a;    // normed final states; rowmap skips the anchor rows
+  NormIn nrm;       // final RMSNorm scale
   const T* w;       // [V, D]
-  int M, V, D;
-  int tpw;          // 16-row vocab tiles per wave
+  int V;
+  int tpw;          // 64-row vocab groups per wave
   float* logits;    // nullable [M, V]
   float* part_v;    // [nchunk][M][KTOP]
   int* part_i;
 };
 
-// Work-group: WV waves along the vocabulary, all on the same 16*FM rows.
-template <typename T, int FM, int KTOP, int WV, int U>
-__global__ __launch_bounds__(64 * WV) void lmhead_kernel(const LmArgs<T> a) {
+// Few-token LM head: WV waves per work-group, each wave owns tpw groups of
+// 16*FN vocabulary rows (FN MFMA fragments sharing one activation fragment)
+// over the full K for one 16-token fragment.
+template <typename T, int KTOP, int WV, int FN, int U>
+__global__ __launch_bounds__(64 * WV) void lmhead_kernel(const LmArgs<T> p) {
   using MM = Mma<T>;
   constexpr int KS = MM::KSTEP;
   constexpr int EPL = MM::EPL;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
   const int chunk = blockIdx.x;
-  const int m0 = blockIdx.y * 16 * FM;
-  const int ntiles = a.V >> 4;
-  const int t0 = (chunk * WV + wv) * a.tpw;
-  const int t1 = min(ntiles, t0 + a.tpw);
+  const int m0 = blockIdx.y * 16;
+  const int D = p.a.kseg;
+  const int ngroups = p.V / (16 * FN);
+  const int t0 = (chunk * WV + wv) * p.tpw;
+  const int t1 = min(ngroups, t0 + p.tpw);
+  const int m = m0 + r16;
+  const int arow = p.a.row(m < p.a.M ? m : p.a.M - 1);
+  const T* ap = p.a.ptr[0] + (size_t)arow * p.a.lda + kg * EPL;
+  const float sc = norm_scale(p.nrm, arow, kg);
 
-  const T* ap[FM];
+  float lv[KTOP];
+  int li[KTOP];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int m = m0 + fm * 16 + r16;
-    ap[fm] = a.u + (size_t)(m < a.M ? m : a.M - 1) * a.D + kg * EPL;
+  for (int k = 0; k < KTOP; ++k) {
+    lv[k] = -INFINITY;
+    li[k] = 0x7fffffff;
   }
-  float lv[FM][KTOP];
-  int li[FM][KTOP];
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-    for (int k = 0; k < KTOP; ++k) {
-      lv[fm][k] = -INFINITY;
-      li[fm][k] = 0x7fffffff;
-    }
 
-  const int nks = a.D / KS;
+  const int nks = D / KS;
   const int nfull = (nks / U) * U;
   for (int t = t0; t < t1; ++t) {
-    const T* wp = a.w + (size_t)(t * 16 + r16) * a.D + kg * EPL;
-    f32x4_t acc[FM];
+    const T* wp[FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) acc[fm] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int fn = 0; fn < FN; ++fn) wp[fn] = p.w + (size_t)(t * 16 * FN + fn * 16 + r16) * D + kg * EPL;
+    f32x4_t acc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int ks = 0; ks < nfull; ks += U) {
-      uint4 wf[U], af[U][FM];
-#pragma unroll
-      for (int u = 0; u < U; ++u) wf[u] = ld16_stream(wp + (ks + u) * KS);
+      uint4 wf[U][FN], af[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) af[u][fm] = ld16(ap[fm] + (ks + u) * KS);
+        for (int fn = 0; fn < FN; ++fn) wf[u][fn] = ld16_stream(wp[fn] + (ks + u) * KS);
+#pragma unroll
+      for (int u = 0; u < U; ++u) af[u] = ld16(ap + (ks + u) * KS);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) acc[fm] = MM::step(wf[u], af[u][fm], acc[fm]);
+        for (int fn = 0; fn < FN; ++fn) acc[fn] = MM::step(wf[u][fn], af[u], acc[fn]);
     }
     for (int ks = nfull; ks < nks; ++ks) {
-      const uint4 wf = ld16_stream(wp + ks * KS);
+      const uint4 af = ld16(ap + ks * KS);
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm) acc[fm] = MM::step(wf, ld16(ap[fm] + ks * KS), acc[fm]);
+      for (int fn = 0; fn < FN; ++fn) acc[fn] = MM::step(ld16_stream(wp[fn] + ks * KS), af, acc[fn]);
     }
-    const int id0 = t * 16 + 4 * kg;
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
+    for (int fn = 0; fn < FN; ++fn) {
+      const int id0 = t * 16 * FN + fn * 16 + 4 * kg;
+      const f32x4_t v = acc[fn] * sc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tk_insert<KTOP>(lv[fm], li[fm], acc[fm][i], id0 + i);
-      if (a.logits) {
-        const int m = m0 + fm * 16 + r16;
-        if (m < a.M) *reinterpret_cast<f32x4_t*>(a.logits + (size_t)m * a.V + id0) = acc[fm];
-      }
+      for (int i = 0; i < 4; ++i) tk_insert<KTOP>(lv, li, v[i], id0 + i);
+      if (p.logits && m < p.a.M) *reinterpret_cast<f32x4_t*>(p.logits + (size_t)m * p.V + id0) = v;
     }
   }
 
-  // Merge: per row, WV*4 sorted lists -> one; one 16-row group at a time.
+  // Merge: per row, WV*4 sorted lists -> one.
   constexpr int NL = WV * 4;
   __shared__ float sv[16][NL][KTOP];
   __shared__ int si[16][NL][KTOP];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
+  for (int k = 0; k < KTOP; ++k) {
+    sv[r16][wv * 4 + kg][k] = lv[k];
+    si[r16][wv * 4 + kg][k] = li[k];
+  }
+  __syncthreads();
+  const int row = threadIdx.x;
+  const int mr = m0 + row;
+  if (row < 16 && mr < p.a.M) {
+    int head[NL];
 #pragma unroll
+    for (int l = 0; l < NL; ++l) head[l] = 0;
+    float* ov = p.part_v + ((size_t)chunk * p.a.M + mr) * KTOP;
+    int* oi = p.part_i + ((size_t)chunk * p.a.M + mr) * KTOP;
     for (int k = 0; k < KTOP; ++k) {
-      sv[r16][wv * 4 + kg][k] = lv[fm][k];
-      si[r16][wv * 4 + kg][k] = li[fm][k];
-    }
-    __syncthreads();
-    const int row = threadIdx.x;
-    const int m = m0 + fm * 16 + row;
-    if (row < 16 && m < a.M) {
-      int head[NL];
+      int best = -1;
+      float bv = -INFINITY;
+      int bi = 0x7fffffff;
 #pragma unroll
-      for (int l = 0; l < NL; ++l) head[l] = 0;
-      float* ov = a.part_v + ((size_t)chunk * a.M + m) * KTOP;
-      int* oi = a.part_i + ((size_t)chunk * a.M + m) * KTOP;
-      for (int k = 0; k < KTOP; ++k) {
-        int best = -1;
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int l = 0; l < NL; ++l) {
-          if (head[l] >= KTOP) continue;
-          const float v = sv[row][l][head[l]];
-          const int id = si[row][l][head[l]];
-          if (best < 0 || tk_better(v, id, bv, bi)) {
-            bv = v;
-            bi = id;
-            best = l;
-          }
+      for (int l = 0; l < NL; ++l) {
+        if (head[l] >= KTOP) continue;
+        const float v = sv[row][l][head[l]];
+        const int id = si[row][l][head[l]];
+        if (best < 0 || tk_better(v, id, bv, bi)) {
+          bv = v;
+          bi = id;
+          best = l;
         }
-        ov[k] = bv;
-        oi[k] = bi;
-#pragma unroll
-        for (int l = 0; l < NL; ++l)
-          if (l == best) ++head[l];
       }
+      ov[k] = bv;
+      oi[k] = bi;
+#pragma unroll
+      for (int l = 0; l < NL; ++l)
+        if (l == best) ++head[l];
     }
-    __syncthreads();
   }
 }
+
+// Top-1 epilogue for the tiled GEMM: the best (logit, id) of each token over
+// the 16*FN vocabulary rows a wave holds, written as that chunk's partial list.
+struct EpiTop1 {
+  static constexpr bool kPaired = false;
+  static constexpr bool kRow = true;
+  float* part_v;   // [ceil(V / (16*FN))][M]
+  int* part_i;
+  float* logits;   // nullable [M, V]
+  int M, V;
+  template <int FN>
+  __device__ __forceinline__ void apply_row(int m, bool mvalid, int nvalid, const int (&fb)[FN],
+                                            const f32x4_t (&acc)[FN], float sc, int kg) const {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      if (j >= nvalid) continue;
+      const f32x4_t v = acc[j] * sc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (tk_better(v[i], fb[j] + 4 * kg + i, bv, bi)) {
+          bv = v[i];
+          bi = fb[j] + 4 * kg + i;
+        }
+      if (logits && mvalid) *reinterpret_cast<f32x4_t*>(logits + (size_t)m * V + fb[j] + 4 * kg) = v;
+    }
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float v2 = __shfl_xor(bv, o);
+      const int i2 = __shfl_xor(bi, o);
+      if (tk_better(v2, i2, bv, bi)) {
+        bv = v2;
+        bi = i2;
+      }
+    }
+    if (mvalid && nvalid > 0 && (threadIdx.x & 63) < 16) {
+      const size_t idx = (size_t)(fb[0] / (16 * FN)) * M + m;
+      part_v[idx] = bv;
+      part_i[idx] = bi;
+    }
+  }
+};
 
 // Second stage: merge nchunk partial lists of one row; 256 threads per row.
 // Each thread keeps a top-KTOP list of its share of the candidates; then

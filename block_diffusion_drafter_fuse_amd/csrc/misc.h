@@ -6,12 +6,16 @@
 namespace dfl {
 
 // Block assembly: row r*B + j of the fp32 residual stream is the anchor's
-// token embedding (j == 0) or the shared mask embedding (j > 0).
+// token embedding (j == 0) or the shared mask embedding (j > 0).  Also writes
+// the first layer's normed-input operand u = T(x * g) and per-16-feature sums
+// of squares (the RMSNorm is completed by the consuming GEMM).
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const T* e_mask, const int* anchor,
-                                                    int B, int D, int V, float* x) {
+                                                    const T* g, int B, int D, int V, float* x, T* u,
+                                                    float* ssq) {
   const int m = blockIdx.x;
   const int r = m / B, j = m - r * B;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const T* src;
   if (j == 0) {
     int a = anchor[r];
@@ -20,34 +24,16 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const T* e_m
   } else {
     src = e_mask;
   }
-  for (int d = threadIdx.x; d < D; d += 256) x[(size_t)m * D + d] = to_f<T>(src[d]);
-}
-
-// y[mo] = x[mi] * rsqrt(mean(x[mi]^2) + eps) * g, output in the storage type.
-// skip_anchor: output row mo = r*(B-1) + (j-1) reads input row r*B + j.
-template <typename T, typename TI>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const TI* x, const T* g, T* y, int D, float eps,
-                                                      int skip_anchor, int B) {
-  const int mo = blockIdx.x;
-  int mi = mo;
-  if (skip_anchor) {
-    const int r = mo / (B - 1);
-    mi = r * B + (mo - r * (B - 1)) + 1;
+  const int nslot = D >> 4;
+  for (int c = wave; c < (D >> 6); c += 4) {
+    const int d = c * 64 + lane;
+    const float v = to_f<T>(src[d]);
+    x[(size_t)m * D + d] = v;
+    u[(size_t)m * D + d] = from_f<T>(v * to_f<T>(g[d]));
+    float ss = v * v;
+    for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
+    if ((lane & 15) == 0) ssq[(size_t)m * nslot + (d >> 4)] = ss;
   }
-  const TI* xr = x + (size_t)mi * D;
-  float ss = 0.f;
-  for (int d = threadIdx.x; d < D; d += 256) {
-    const float v = to_f<TI>(xr[d]);
-    ss += v * v;
-  }
-  ss = wave_sum(ss);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = 1.0f / sqrtf(tot / (float)D + eps);
-  for (int d = threadIdx.x; d < D; d += 256)
-    y[(size_t)mo * D + d] = from_f<T>(to_f<TI>(xr[d]) * inv * to_f<T>(g[d]));
 }
 
 // RoPE table: tab[pos][i] = (cos, sin)(pos * base^(-2i/hd)), computed in

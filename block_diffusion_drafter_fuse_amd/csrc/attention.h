@@ -4,22 +4,28 @@
 // Per (request r, KV head g) the queries are the G*B rows (head-in-group,
 // block offset) of the block; the keys/values are the cached context entries
 // of the slot followed by the block's own K_b/V_b.  There is no mask.  The
-// context is cut into splits of `chunk` keys; the last split also takes the
-// B block keys.  One work-group per split holds QF waves, one per 16 query
-// rows; all waves walk the same keys (shared through L1).  Each wave computes
-// S^T = K Q^T and O^T += V^T P^T with MFMA and keeps an online softmax per
-// query column, then stores its partial (max, sum, O).  The combine kernel
-// merges the splits of every (r, g) in split order, so results are
-// deterministic.
+// context is cut into splits of `chunk` keys (a multiple of 64); the last
+// split also takes the block keys.  One work-group per split holds QF waves,
+// one per 16 query rows.  Keys are consumed in stages of 64: the work-group
+// copies the stage's K rows and V^T rows into LDS (double buffered, the next
+// stage's global loads in flight while the current one is consumed), so every
+// K/V byte crosses the vector-memory path once per work-group.  Each wave
+// computes S^T = K Q^T and O^T += V^T P^T with MFMA and keeps an online
+// softmax per query column, then stores its partial (max, sum, O).  The
+// combine kernel merges the splits of every (r, g) in split order, so results
+// are deterministic.
 //
-// Layouts: Q, K_b rows [M, heads*hd]; V_b transposed vbT[(r*Hkv+g)*hd + d][BP];
-// cache keys [pos][hd] and values transposed [hd][ctx_pad] per (slot, layer,
-// head).  A lane holds 4*NT consecutive keys of one query column, which is
-// exactly the key run it needs as the P^T operand of the next MFMA.
+// Layouts: Q, K_b rows [M, heads*hd]; V_b transposed vbT[(r*Hkv+g)*hd + d][BP]
+// with BP = 64 (zero padded); cache keys [pos][hd] and values transposed
+// [hd][ctx_pad] per (slot, layer, head).  Within a 16*NT-key MFMA step a lane
+// holds 4*NT consecutive keys of one query column, which is exactly the key
+// run it needs as the P^T operand of the next MFMA.
 #pragma once
 #include "common.h"
 
 namespace dfl {
+
+constexpr int kAttnStage = 64;  // keys per LDS stage
 
 struct AttnMeta {
   int n_req;
@@ -45,112 +51,35 @@ struct AttnArgs {
   AttnMeta meta;
 };
 
-template <typename T, int HD>
-struct KeySource {
-  const T* kbase;  // key row 0
-  int kstride;     // elements between key rows
-  const T* vtbase; // V^T row 0 (d = 0)
-  int ldvt;        // elements between V^T rows
-  int kbeg, kend;  // key range [kbeg, kend), kend > kbeg
+template <typename T, int HD, int QF>
+struct AttnStage {
+  static constexpr int KROWB = HD * (int)sizeof(T) + 16;          // padded K row bytes
+  static constexpr int VROWB = kAttnStage * (int)sizeof(T) + 16;  // padded V^T row bytes
+  static constexpr int KBYTES = kAttnStage * KROWB;
+  static constexpr int VBYTES = HD * VROWB;
+  static constexpr int BUF = KBYTES + VBYTES;
+  static constexpr int KCH = HD * (int)sizeof(T) / 16;           // 16-byte chunks per K row
+  static constexpr int VCH = kAttnStage * (int)sizeof(T) / 16;   // 16-byte chunks per V^T row
+  static constexpr int NCH = kAttnStage * KCH + HD * VCH;        // chunks per stage
+  static constexpr int NTH = 64 * QF;
+  static constexpr int CPT = (NCH + NTH - 1) / NTH;              // chunks per thread
 };
-
-// Online-softmax attention of one wave's 16 query rows over one key source.
-template <typename T, int HD>
-__device__ __forceinline__ void attn_source(const KeySource<T, HD>& src, const uint4 (&qf)[HD / Mma<T>::KSTEP],
-                                            float scale_log2, int r16, int kg, f32x4_t (&o)[HD / 16],
-                                            float& mrow, float& lrow) {
-  using MM = Mma<T>;
-  constexpr int KS = MM::KSTEP;
-  constexpr int EPL = MM::EPL;
-  constexpr int NT = KS / 16;
-  constexpr int HS = HD / KS;
-  constexpr int DF = HD / 16;
-  const int kend = src.kend;
-
-  auto load = [&](int k0, uint4 (&kf)[NT][HS], uint4 (&vf)[DF]) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const int key = k0 + (r16 >> 2) * (4 * NT) + 4 * t + (r16 & 3);
-      const int keyc = key < kend ? key : kend - 1;
-      const T* kp = src.kbase + (size_t)keyc * src.kstride + kg * EPL;
-#pragma unroll
-      for (int h = 0; h < HS; ++h) kf[t][h] = ld16(kp + h * KS);
-    }
-#pragma unroll
-    for (int d = 0; d < DF; ++d)
-      vf[d] = ld16(src.vtbase + (size_t)(d * 16 + r16) * src.ldvt + k0 + kg * (4 * NT));
-  };
-
-  uint4 kf[NT][HS], vf[DF];
-  load(src.kbeg, kf, vf);
-  for (int k0 = src.kbeg; k0 < kend; k0 += KS) {
-    uint4 nkf[NT][HS], nvf[DF];
-    const int kn = k0 + KS < kend ? k0 + KS : k0;
-    load(kn, nkf, nvf);
-
-    float sv[NT][4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int h = 0; h < HS; ++h) c = MM::step(kf[t][h], qf[h], c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = k0 + kg * (4 * NT) + 4 * t + i;
-        const float x = key < kend ? c[i] * scale_log2 : -INFINITY;
-        sv[t][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(mrow, mx);
-    const float alpha = exp2f(mrow - mnew);
-    float ps = 0.f;
-    float p[NT][4];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        p[t][i] = exp2f(sv[t][i] - mnew);
-        ps += p[t][i];
-      }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    lrow = lrow * alpha + ps;
-    mrow = mnew;
-    uint4 pp;
-    if constexpr (NT == 1) {
-      pp = make_uint4(__float_as_uint(p[0][0]), __float_as_uint(p[0][1]), __float_as_uint(p[0][2]),
-                      __float_as_uint(p[0][3]));
-    } else {
-      pp.x = (uint32_t)f2bf(p[0][0]) | ((uint32_t)f2bf(p[0][1]) << 16);
-      pp.y = (uint32_t)f2bf(p[0][2]) | ((uint32_t)f2bf(p[0][3]) << 16);
-      pp.z = (uint32_t)f2bf(p[1][0]) | ((uint32_t)f2bf(p[1][1]) << 16);
-      pp.w = (uint32_t)f2bf(p[1][2]) | ((uint32_t)f2bf(p[1][3]) << 16);
-    }
-#pragma unroll
-    for (int d = 0; d < DF; ++d) o[d] = MM::step(vf[d], pp, o[d] * alpha);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int h = 0; h < HS; ++h) kf[t][h] = nkf[t][h];
-#pragma unroll
-    for (int d = 0; d < DF; ++d) vf[d] = nvf[d];
-  }
-}
 
 template <typename T, int HD, int QF>
 __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
   using MM = Mma<T>;
-  constexpr int KS = MM::KSTEP;
+  using SG = AttnStage<T, HD, QF>;
+  constexpr int KS = MM::KSTEP;  // keys per P.V step
   constexpr int EPL = MM::EPL;
-  constexpr int HS = HD / KS;
-  constexpr int DF = HD / 16;
+  constexpr int NT = KS / 16;    // S^T tiles per P.V step
+  constexpr int HS = HD / KS;    // k-steps over the head dim
+  constexpr int DF = HD / 16;    // output d fragments
   constexpr int QR = QF * 16;
+  constexpr int PVS = kAttnStage / KS;  // P.V steps per stage
 
-  const int lane = threadIdx.x & 63, f = threadIdx.x >> 6;
+  extern __shared__ __align__(16) char lds[];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, f = tid >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
   const int w = blockIdx.x;
   int r = 0;
@@ -173,23 +102,127 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
     for (int h = 0; h < HS; ++h) qf[h] = valid ? ld16(qp + h * KS) : make_uint4(0, 0, 0, 0);
   }
 
+  // Stages: context keys [kbeg, kend) of this split, then (last split) the block.
+  const int kbeg = s * a.chunk;
+  const int kend = min(ctx, kbeg + a.chunk);
+  const int nctx = kend > kbeg ? (kend - kbeg + kAttnStage - 1) / kAttnStage : 0;
+  const int nst = nctx + (s == S - 1 ? 1 : 0);
+  const T* hb = a.pool + (size_t)a.meta.slot[r] * a.slot_stride + (size_t)a.layer * a.layer_stride +
+                (size_t)g * a.head_stride;
+  const T* bkb = a.kb + (size_t)(r * a.B) * kd + (size_t)g * HD;
+  const T* bvt = a.vbT + (size_t)(r * a.Hkv + g) * HD * a.BP;
+
+  uint4 stg[SG::CPT];
+  // global -> registers for stage i
+  auto gload = [&](int i) {
+    const bool blk = i >= nctx;
+    const int k0 = blk ? 0 : kbeg + i * kAttnStage;
+    const int ke = blk ? a.B : kend;
+#pragma unroll
+    for (int c = 0; c < SG::CPT; ++c) {
+      const int ch = tid + c * SG::NTH;
+      if (ch < kAttnStage * SG::KCH) {
+        const int row = ch / SG::KCH, col = ch - row * SG::KCH;
+        int key = k0 + row;
+        key = key < ke ? key : ke - 1;
+        const T* src = blk ? bkb + (size_t)key * kd : hb + (size_t)key * HD;
+        stg[c] = ld16(reinterpret_cast<const char*>(src) + col * 16);
+      } else if (ch < SG::NCH) {
+        const int vch = ch - kAttnStage * SG::KCH;
+        const int d = vch / SG::VCH, col = vch - d * SG::VCH;
+        const T* src = blk ? bvt + (size_t)d * a.BP : hb + a.kv_stride + (size_t)d * a.ctx_pad + k0;
+        stg[c] = ld16(reinterpret_cast<const char*>(src) + col * 16);
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+    char* base = lds + buf * SG::BUF;
+#pragma unroll
+    for (int c = 0; c < SG::CPT; ++c) {
+      const int ch = tid + c * SG::NTH;
+      if (ch < kAttnStage * SG::KCH) {
+        const int row = ch / SG::KCH, col = ch - row * SG::KCH;
+        *reinterpret_cast<uint4*>(base + row * SG::KROWB + col * 16) = stg[c];
+      } else if (ch < SG::NCH) {
+        const int vch = ch - kAttnStage * SG::KCH;
+        const int d = vch / SG::VCH, col = vch - d * SG::VCH;
+        *reinterpret_cast<uint4*>(base + SG::KBYTES + d * SG::VROWB + col * 16) = stg[c];
+      }
+    }
+  };
+
   f32x4_t o[DF];
 #pragma unroll
   for (int d = 0; d < DF; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrow = -INFINITY, lrow = 0.f;
 
-  const int kbeg = s * a.chunk;
-  const int kend = min(ctx, kbeg + a.chunk);
-  if (kend > kbeg) {
-    const T* hb = a.pool + (size_t)a.meta.slot[r] * a.slot_stride + (size_t)a.layer * a.layer_stride +
-                  (size_t)g * a.head_stride;
-    KeySource<T, HD> src{hb, HD, hb + a.kv_stride, a.ctx_pad, kbeg, kend};
-    attn_source<T, HD>(src, qf, a.scale_log2, r16, kg, o, mrow, lrow);
-  }
-  if (s == S - 1) {
-    KeySource<T, HD> src{a.kb + (size_t)(r * a.B) * kd + (size_t)g * HD, kd,
-                         a.vbT + (size_t)(r * a.Hkv + g) * HD * a.BP, a.BP, 0, a.B};
-    attn_source<T, HD>(src, qf, a.scale_log2, r16, kg, o, mrow, lrow);
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int i = 0; i < nst; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < nst) gload(i + 1);
+    const bool blk = i >= nctx;
+    const int klim = blk ? a.B : kend - (kbeg + i * kAttnStage);  // valid keys in this stage
+    const char* kl = lds + buf * SG::BUF;
+    const char* vl = kl + SG::KBYTES;
+#pragma unroll
+    for (int p = 0; p < PVS; ++p) {
+      const int kb0 = p * KS;  // stage-local first key of this P.V step
+      if (kb0 >= klim) break;
+      float sv[NT][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int krow = kb0 + (r16 >> 2) * (4 * NT) + 4 * t + (r16 & 3);
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < HS; ++h)
+          c = MM::step(*reinterpret_cast<const uint4*>(kl + krow * SG::KROWB + h * 64 + kg * 16), qf[h], c);
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int key = kb0 + kg * (4 * NT) + 4 * t + ii;
+          const float x = key < klim ? c[ii] * a.scale_log2 : -INFINITY;
+          sv[t][ii] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow, mx);
+      const float alpha = exp2f(mrow - mnew);
+      float ps = 0.f;
+      float pr[NT][4];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          pr[t][ii] = exp2f(sv[t][ii] - mnew);
+          ps += pr[t][ii];
+        }
+      ps += __shfl_xor(ps, 16);
+      ps += __shfl_xor(ps, 32);
+      lrow = lrow * alpha + ps;
+      mrow = mnew;
+      uint4 pp;
+      if constexpr (NT == 1) {
+        pp = make_uint4(__float_as_uint(pr[0][0]), __float_as_uint(pr[0][1]), __float_as_uint(pr[0][2]),
+                        __float_as_uint(pr[0][3]));
+      } else {
+        pp.x = (uint32_t)f2bf(pr[0][0]) | ((uint32_t)f2bf(pr[0][1]) << 16);
+        pp.y = (uint32_t)f2bf(pr[0][2]) | ((uint32_t)f2bf(pr[0][3]) << 16);
+        pp.z = (uint32_t)f2bf(pr[1][0]) | ((uint32_t)f2bf(pr[1][1]) << 16);
+        pp.w = (uint32_t)f2bf(pr[1][2]) | ((uint32_t)f2bf(pr[1][3]) << 16);
+      }
+#pragma unroll
+      for (int d = 0; d < DF; ++d) {
+        const uint4 vf = *reinterpret_cast<const uint4*>(vl + (d * 16 + r16) * SG::VROWB +
+                                                          (kb0 + kg * 4 * NT) * (int)sizeof(T));
+        o[d] = MM::step(vf, pp, o[d] * alpha);
+      }
+    }
+    if (i + 1 < nst) lstore(buf ^ 1);
+    __syncthreads();
   }
 
   float* po = a.part_o + (size_t)w * QR * HD;

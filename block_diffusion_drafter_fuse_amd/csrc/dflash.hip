@@ -47,13 +47,12 @@ constexpr size_t kAlign = 256;
 constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
 constexpr int kAttnWorkMax = 4096;     // attention split work items per call
 constexpr int kAttnTargetWG = 2048;    // attention work-groups aimed for
-constexpr int kAttnMinChunk = 256;     // minimum context keys per split
-constexpr int kLmTargetWG = 2048;      // few-token LM-head work-groups aimed for
-constexpr int kLmWV = 4;               // waves per few-token LM-head work-group
+constexpr int kAttnMinChunk = 128;     // minimum context keys per split
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
-constexpr int kGemvBytes = 8;          // KB of weights in flight per wave (U * FN)
-constexpr int kGemvFNUnpaired = 1, kGemvFNPaired = 2;  // skinny GEMM fragments per wave
-constexpr int kGemvTargetWaves = 4096;
+constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
+constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (LDS: TB x waves x 1 KB)
+constexpr bool kGemvPF = false;        // prefetch the next tile's weights before the current MFMAs
+constexpr int kGemvWGs = 256;          // skinny GEMM work-groups per 16-token block
 constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, unroll
 constexpr int kTBM = 128, kTBN = 256;  // tiled GEMM work-group tile
 constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
@@ -80,20 +79,13 @@ struct Plan {
 
 int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
 
-void lm_shape_small(int M, int V, int* tpw, int* nchunk, int* rowblocks) {
-  *rowblocks = ceil_div(M, 16);
-  const int ngroups = V / (16 * kLmFN);
-  const int chunks_target = std::max(1, kLmTargetWG / *rowblocks);
-  *tpw = std::max(1, ceil_div(ngroups, kLmWV * chunks_target));
-  *nchunk = ceil_div(ngroups, kLmWV * *tpw);
-}
+// Few-token LM head: one 16-wave work-group per CU and 16-row block.
+int lm_chunks_small(int rowblocks) { return std::max(1, 256 / rowblocks); }
 
 // LM-head partial-list entries a call needs (KTOP = 16 for top_k > 1).
 size_t lm_entries_for(int Mlm, int V, int top_k) {
   if (top_k == 1 && Mlm > kSkinnyMaxM) return (size_t)ceil_div(V, kTBN / 2) * Mlm;
-  int tpw, nchunk, rb;
-  lm_shape_small(Mlm, V, &tpw, &nchunk, &rb);
-  return (size_t)nchunk * Mlm * (top_k == 1 ? 1 : 16);
+  return (size_t)lm_chunks_small(ceil_div(Mlm, 16)) * Mlm * (top_k == 1 ? 1 : 16);
 }
 
 int validate_dims(const dflash_dims* d) {
@@ -123,7 +115,6 @@ int validate_dims(const dflash_dims* d) {
 
 void make_plan(const dflash_dims* d, Plan* p) {
   const size_t e = elt_size(d->dtype);
-  const int KS = d->dtype == DFLASH_BF16 ? 32 : 16;
   p->ctx_pad = round_up(d->max_ctx, 64);
   p->head_stride = (size_t)p->ctx_pad * d->hd;
   p->kv_stride = p->head_stride * d->Hkv;
@@ -139,7 +130,7 @@ void make_plan(const dflash_dims* d, Plan* p) {
   const int M = d->max_batch * d->B;
   const int Mlm = d->max_batch * (d->B - 1);
   const int nslot = d->D / 16;
-  p->BP = round_up(d->B, KS);
+  p->BP = kAttnStage;  // block V^T padded to one attention stage
   p->qf = ceil_div((d->Hq / d->Hkv) * d->B, 16);
   if (p->qf == 3) p->qf = 4;
   off = 0;
@@ -227,25 +218,32 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
   float* part = c->wsp<float>(c->p.part_off);
   int* ctr = c->wsp<int>(c->p.ctr_off);
   const int K = a.nk * a.kseg;
-  if (a.M <= kSkinnyMaxM) {
-    // K is split only across the waves of a work-group (LDS reduction): a
-    // cross-work-group split needs device-scope fences, which write back and
-    // invalidate the XCD's L2 and cost more than they save here.
-    constexpr int FN = Epi::kPaired ? kGemvFNPaired : kGemvFNUnpaired;
-    constexpr int U = kGemvBytes / FN;
-    const int nks = K / Mma<T>::KSTEP;
-    const int tiles = ceil_div(w.ngroups, FN) * ceil_div(a.M, 16);
-    const int want = ceil_div(kGemvTargetWaves, tiles);
-    const int kmax = std::max(1, nks / U);  // waves that still get a full run of U k-steps
-    const int wk = std::min(want, kmax);
-    const SplitK sk{1, nks, part, ctr};
-    if (wk >= 12)
-      hipLaunchKernelGGL((gemv_kernel<T, FN, 16, U, ALO, Epi>), dim3(tiles), dim3(64 * 16), 0, st, w, a, nrm, sk, epi);
-    else if (wk >= 6)
-      hipLaunchKernelGGL((gemv_kernel<T, FN, 8, U, ALO, Epi>), dim3(tiles), dim3(64 * 8), 0, st, w, a, nrm, sk, epi);
-    else
-      hipLaunchKernelGGL((gemv_kernel<T, FN, 4, U, ALO, Epi>), dim3(tiles), dim3(64 * 4), 0, st, w, a, nrm, sk, epi);
-  } else {
+  if constexpr (!Epi::kRow) {
+      if (a.M <= kSkinnyMaxM) {
+      // Activation-stationary GEMV: 16-row tiles, K split across the waves of
+      // a work-group (LDS reduction; a cross-work-group split would need
+      // device-scope fences, which write back and invalidate the XCD's L2).
+      constexpr int KSW = kGemvKSW;
+      const int nks = K / Mma<T>::KSTEP;
+      const int nw = std::max(1, std::min(16, ceil_div(nks, KSW)));
+      const int mt = ceil_div(a.M, 16);
+      // tiles per work-group: fill every CU once per 16-token block (even for paired epilogues)
+      int tpw = std::max(1, ceil_div(w.ngroups, std::max(1, kGemvWGs / mt)));
+      if (Epi::kPaired) tpw += tpw & 1;
+      const int nwg = ceil_div(w.ngroups, tpw);
+      const int lds = kGemvTB * nw * 64 * 16;
+      auto kern = gemv_as_kernel<T, KSW, ALO, kGemvTB, kGemvPF, Epi>;
+      static bool attr_set = false;
+      if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kGemvTB * 16 * 64 * 16);
+        attr_set = true;
+      }
+      hipLaunchKernelGGL(kern, dim3(nwg, mt), dim3(64 * nw), lds, st, w, a, nrm, epi, tpw);
+      return;
+    }
+  }
+  {
     constexpr int BKE = 128 / sizeof(T);
     const int nst = K / BKE;
     const int MT = ceil_div(a.M, kTBM), NT = ceil_div(w.ngroups, kTBN / 16);
@@ -381,7 +379,14 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
 
 template <typename T, int HD, int QF>
 void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
-  hipLaunchKernelGGL((attn_kernel<T, HD, QF>), dim3(work), dim3(64 * QF), 0, st, a);
+  const int lds = 2 * AttnStage<T, HD, QF>::BUF;
+  auto kern = attn_kernel<T, HD, QF>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(work), dim3(64 * QF), lds, st, a);
   const int threads = a.meta.n_req * a.Hkv * a.G * a.B * (HD / 4);
   hipLaunchKernelGGL((attn_combine_kernel<T, HD, QF * 16>), dim3(ceil_div(threads, 256)), dim3(256), 0, st, a);
 }
@@ -410,7 +415,7 @@ void plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPla
   // the K/V they summarise), about kAttnTargetWG work-groups per call.
   long long total = 0;
   for (int r = 0; r < n_req; ++r) total += c->len[slot[r]];
-  int chunk = round_up(std::max(1, ceil_div_l(total * d.Hkv, kAttnTargetWG)), 32);
+  int chunk = round_up(std::max(1, ceil_div_l(total * d.Hkv, kAttnTargetWG)), kAttnStage);
   chunk = std::max(chunk, kAttnMinChunk);
   for (;;) {
     long long work = 0;
@@ -439,9 +444,17 @@ void plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPla
 // ------------------------------------------------------------------ LM head
 
 template <typename T, int KTOP>
-void launch_lm_small(const LmArgs<T>& la, int nchunk, int rowblocks, hipStream_t st) {
-  hipLaunchKernelGGL((lmhead_kernel<T, KTOP, kLmWV, kLmFN, kLmU>), dim3(nchunk, rowblocks), dim3(64 * kLmWV), 0,
-                     st, la);
+void launch_lm_small(const LmArgs<T>& la, int nchunk, int rowblocks, int* tile_ctr, hipStream_t st) {
+  // staged rows, reused afterwards for the 16 x 64 x KTOP list merge
+  const int lds = std::max(16 * (la.a.kseg * (int)sizeof(T) + 16), 16 * 64 * KTOP * 8);
+  auto kern = lmhead_lds_kernel<T, KTOP, kLmFN, kLmU>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              160 * 1024);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(nchunk, rowblocks), dim3(1024), lds, st, la, tile_ctr);
 }
 
 template <typename T>
@@ -452,6 +465,7 @@ void run_lmhead(dflash_ctx* c, hipStream_t st, int n_req, int top_k, int32_t* ou
   const int Mlm = n_req * (d.B - 1);
   float* pv = c->wsp<float>(p.lmv_off);
   int* pi = c->wsp<int>(p.lmi_off);
+  int* tile_ctr = c->wsp<int>(p.ctr_off) + (kCounters - 64);
   const AOperand<T> a = aop<T>(c->wsp<T>(p.u_off), Mlm, d.D, d.B);
   const NormIn nrm = norm_in(c->wsp<float>(p.ssq_off), d.D, d.rms_eps);
   int nchunk;
@@ -462,20 +476,20 @@ void run_lmhead(dflash_ctx* c, hipStream_t st, int n_req, int top_k, int32_t* ou
       EpiTop1 epi{pv, pi, out_logits, Mlm, d.V};
       launch_gemm<T>(c, wop<T>({{c->w.w_lm, d.V}}, 0), a, nrm, epi, st);
     } else {
-      int tpw, rowblocks;
-      lm_shape_small(Mlm, d.V, &tpw, &nchunk, &rowblocks);
-      LmArgs<T> la{a, nrm, static_cast<const T*>(c->w.w_lm), d.V, tpw, out_logits, pv, pi};
-      if (top_k == 1) launch_lm_small<T, 1>(la, nchunk, rowblocks, st);
-      else launch_lm_small<T, 16>(la, nchunk, rowblocks, st);
+      const int rowblocks = ceil_div(Mlm, 16);
+      nchunk = lm_chunks_small(rowblocks);
+      LmArgs<T> la{a, nrm, static_cast<const T*>(c->w.w_lm), d.V, out_logits, pv, pi};
+      if (top_k == 1) launch_lm_small<T, 1>(la, nchunk, rowblocks, tile_ctr, st);
+      else launch_lm_small<T, 16>(la, nchunk, rowblocks, tile_ctr, st);
     }
   }
   ProfScope ps(c, DFLASH_K_TOPK_MERGE, st);
   if (top_k == 1)
     hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, Mlm, top_k, out_ids,
-                       out_vals);
+                       out_vals, tile_ctr, 64);
   else
     hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, Mlm, top_k,
-                       out_ids, out_vals);
+                       out_ids, out_vals, tile_ctr, 64);
 }
 
 // ------------------------------------------------------------------ draft

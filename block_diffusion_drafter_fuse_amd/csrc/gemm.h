@@ -299,15 +299,7 @@ struct EpiKVAppend {
   }
 };
 
-// ---------------------------------------------------------------- skinny GEMM
-//
-// One 16-token tile per work-group row; each wave owns FN 16-feature
-// fragments that share one activation fragment per k-step.  The WK waves of
-// a work-group split the k-steps of the group's K range in interleaved runs
-// of U and are reduced through LDS; SK work-groups split K further and meet
-// in the SplitK fixup.  Weights are streamed with non-temporal loads.  With
-// ALO the activations come as bf16 hi + lo planes and every weight fragment
-// feeds two MFMAs (near-fp32 activations for memory-bound GEMMs).
+// ---------------------------------------------------------------- helpers for the GEMM kernels
 
 template <typename T>
 __device__ __forceinline__ const T* a_ptr(const AOperand<T>& a, int arow, int kg, int ks) {
@@ -336,112 +328,129 @@ __device__ __forceinline__ void run_epilogue(const Epi& epi, int m, bool mvalid,
   }
 }
 
-template <typename T, int FN, int WK, int U, bool ALO, class Epi>
-__global__ __launch_bounds__(64 * WK) void gemv_kernel(const WOperand<T> w, const AOperand<T> a,
-                                                        const NormIn nrm, const SplitK sk, const Epi epi) {
+// ---------------------------------------------------------------- activation-stationary GEMV
+//
+// Few-token GEMM for the memory-bound case.  A work-group of NW waves (NW =
+// blockDim/64 <= 16) walks a range of 16-row weight tiles; wave w owns the
+// k-steps [c*NW*KSW + w*KSW, +KSW) of every K chunk c and keeps the matching
+// activation fragments in registers, so the vector-memory path carries only
+// the weight stream (re-reading activations from L2 costs a third of the
+// bandwidth).  Tiles are processed in batches of up to TB: inside a batch the
+// waves never synchronise (each writes its partial tile to LDS and the next
+// tile's weight loads are issued before the current MFMAs); one barrier per
+// batch, then the partial tiles are summed in wave order and the epilogues
+// run spread over the waves (a paired epilogue takes two consecutive tiles).
+// When K spans several chunks the activations are reloaded per chunk (such
+// GEMMs have one or two tiles per work-group).
+
+template <typename T, int KSW, bool ALO, int TB, bool PF, class Epi>
+__global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, const AOperand<T> a,
+                                                        const NormIn nrm, const Epi epi, int tiles_per_wg) {
   using MM = Mma<T>;
   constexpr int KS = MM::KSTEP;
   constexpr int EPL = MM::EPL;
-  static_assert(!Epi::kPaired || FN % 2 == 0, "paired epilogue needs even FN");
-  const int lane = threadIdx.x & 63, wk = threadIdx.x >> 6;
+  extern __shared__ __align__(16) char lds_raw[];
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds_raw);  // [TB][NW][64]
+  const int NW = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int ngt = (w.ngroups + FN - 1) / FN;
-  int b = blockIdx.x;
-  const int s = b % sk.SK;
-  b /= sk.SK;
-  const int tg = b % ngt, mt = b / ngt;
-  const int m0 = mt * 16, g0 = tg * FN;
+  const int t_begin = blockIdx.x * tiles_per_wg;
+  const int t_end = min(w.ngroups, t_begin + tiles_per_wg);
+  if (t_begin >= t_end) return;
+  const int m0 = blockIdx.y * 16;
   const int K = a.nk * a.kseg;
   const int nks = K / KS;
-  const int k0 = s * sk.kps, k1 = min(nks, k0 + sk.kps);
-
-  const T* wp[FN];
-  int fbase[FN];
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const int gi = g0 + fn;
-    fbase[fn] = gi < w.ngroups ? w.feature_of_group(gi) : 0;
-    wp[fn] = w.row(fbase[fn] + r16, K) + kg * EPL;
-  }
+  const int span = NW * KSW;
+  const int nchunks = (nks + span - 1) / span;
   const int m = m0 + r16;
   const int arow = a.row(m < a.M ? m : a.M - 1);
 
-  f32x4_t acc[FN];
+  uint4 areg[KSW], alo[KSW];
+  auto load_a = [&](int c) {
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = k0 + wk * U; kb < k1; kb += WK * U) {
-    if (kb + U <= k1) {
-      uint4 wf[U][FN], af[U], al[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) wf[u][fn] = ld16_stream(wp[fn] + (size_t)(kb + u) * KS);
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const T* ap = a_ptr(a, arow, kg, kb + u);
-        af[u] = ld16(ap);
-        if constexpr (ALO) al[u] = ld16(ap + a.lo_off);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          acc[fn] = MM::step(wf[u][fn], af[u], acc[fn]);
-          if constexpr (ALO) acc[fn] = MM::step(wf[u][fn], al[u], acc[fn]);
-        }
-    } else {
-      for (int ks = kb; ks < k1; ++ks) {
+    for (int j = 0; j < KSW; ++j) {
+      const int ks = c * span + wave * KSW + j;
+      if (ks < nks) {
         const T* ap = a_ptr(a, arow, kg, ks);
-        const uint4 af = ld16(ap);
-        uint4 al;
-        if constexpr (ALO) al = ld16(ap + a.lo_off);
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-          const uint4 wf = ld16_stream(wp[fn] + (size_t)ks * KS);
-          acc[fn] = MM::step(wf, af, acc[fn]);
-          if constexpr (ALO) acc[fn] = MM::step(wf, al, acc[fn]);
-        }
+        areg[j] = ld16(ap);
+        if constexpr (ALO) alo[j] = ld16(ap + a.lo_off);
+      } else {
+        areg[j] = make_uint4(0, 0, 0, 0);
+        if constexpr (ALO) alo[j] = make_uint4(0, 0, 0, 0);
       }
     }
-  }
-
-  if constexpr (WK > 1) {
-    __shared__ f32x4_t red[WK - 1][FN][64];
-    if (wk > 0) {
+  };
+  auto wrow = [&](int t) { return w.row(w.feature_of_group(t) + r16, K) + kg * EPL; };
+  auto load_w = [&](const T* wp, int c, uint4 (&wf)[KSW]) {
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) red[wk - 1][fn][lane] = acc[fn];
+    for (int j = 0; j < KSW; ++j) {
+      const int ks = c * span + wave * KSW + j;
+      wf[j] = ks < nks ? ld16_stream(wp + (size_t)ks * KS) : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  if (nchunks == 1) load_a(0);
+  const float sc = norm_scale(nrm, arow, kg);
+  for (int b0 = t_begin; b0 < t_end; b0 += TB) {
+    const int bt = min(TB, t_end - b0);
+    const int items = bt * nchunks;  // (tile, chunk) in order
+    const T* wp = wrow(b0);
+    uint4 wcur[KSW];
+    if constexpr (PF) load_w(wp, 0, wcur);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < items; ++it) {
+      const int tl = it / nchunks, c = it - tl * nchunks;
+      if (nchunks > 1) load_a(c);
+      if constexpr (!PF) {
+        if (c == 0) wp = wrow(b0 + tl);
+        load_w(wp, c, wcur);
+      }
+      uint4 wnext[PF ? KSW : 1];
+      const bool more = it + 1 < items;
+      const T* wpn = wp;
+      if constexpr (PF) {
+        if (more) {
+          const int tn = (it + 1) / nchunks, cn = (it + 1) - tn * nchunks;
+          if (tn != tl) wpn = wrow(b0 + tn);
+          load_w(wpn, cn, wnext);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KSW; ++j) {
+        acc = MM::step(wcur[j], areg[j], acc);
+        if constexpr (ALO) acc = MM::step(wcur[j], alo[j], acc);
+      }
+      if (c == nchunks - 1) {
+        red[(tl * NW + wave) * 64 + lane] = acc;
+        acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      if constexpr (PF) {
+        if (more) {
+          wp = wpn;
+#pragma unroll
+          for (int j = 0; j < KSW; ++j) wcur[j] = wnext[j];
+        }
+      }
     }
     __syncthreads();
-    if (wk != 0) return;
-    for (int j = 0; j < WK - 1; ++j)
+    // reduce + epilogue: unit j (a tile, or a pair of tiles) handled by wave j % NW
+    constexpr int PT = Epi::kPaired ? 2 : 1;
+    for (int j = wave; j * PT < bt; j += NW) {
+      f32x4_t sum[PT];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) acc[fn] += red[j][fn][lane];
+      for (int p = 0; p < PT; ++p) {
+        const int tl = j * PT + p;
+        sum[p] = red[(tl * NW) * 64 + lane];
+        for (int w2 = 1; w2 < NW; ++w2) sum[p] += red[(tl * NW + w2) * 64 + lane];
+      }
+      const int t = b0 + j * PT;
+      if constexpr (Epi::kPaired)
+        epi.apply2(m, m < a.M, w.feature_of_group(t) + 4 * kg, sum[0] * sc, sum[1] * sc);
+      else
+        epi.apply1(m, m < a.M, w.feature_of_group(t) + 4 * kg, sum[0] * sc);
+    }
+    __syncthreads();
   }
-
-  if (sk.SK > 1) {
-    const int tile = mt * ngt + tg;
-    float* pbase = sk.part + (size_t)tile * sk.SK * (FN * 256);
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-      *reinterpret_cast<f32x4_t*>(pbase + (size_t)s * (FN * 256) + fn * 256 + lane * 4) = acc[fn];
-    __threadfence();
-    int prev = 0;
-    if (lane == 0) prev = atomicAdd(sk.ctr + tile, 1);
-    prev = __shfl(prev, 0);
-    if (prev != sk.SK - 1) return;
-    __threadfence();
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < sk.SK; ++j)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-        acc[fn] += *reinterpret_cast<const f32x4_t*>(pbase + (size_t)j * (FN * 256) + fn * 256 + lane * 4);
-    if (lane == 0) sk.ctr[tile] = 0;
-  }
-
-  const float sc = norm_scale(nrm, arow, kg);
-  run_epilogue<FN>(epi, m, m < a.M, w.ngroups - g0, fbase, acc, sc, kg);
 }
 
 }  // namespace dfl

@@ -39,32 +39,41 @@ struct LmArgs {
   NormIn nrm;       // final RMSNorm scale
   const T* w;       // [V, D]
   int V;
-  int tpw;          // 64-row vocab groups per wave
   float* logits;    // nullable [M, V]
   float* part_v;    // [nchunk][M][KTOP]
   int* part_i;
 };
 
-// Few-token LM head: WV waves per work-group, each wave owns tpw groups of
-// 16*FN vocabulary rows (FN MFMA fragments sharing one activation fragment)
-// over the full K for one 16-token fragment.
-template <typename T, int KTOP, int WV, int FN, int U>
-__global__ __launch_bounds__(64 * WV) void lmhead_kernel(const LmArgs<T> p) {
+// Few-token LM head with the activations staged in LDS: one work-group of
+// 16 waves per CU holds the 16 normed rows [16][D] (rows padded by 16 bytes),
+// so the vector-memory path carries only the weight stream.  Waves take
+// 16*FN-row vocabulary tiles from a per-launch atomic counter (reset by the
+// merge kernel) and keep a running top-KTOP per lane; the lists are merged
+// per work-group in LDS.  The partial lists depend on which wave took which
+// tile, the merged result does not.
+template <typename T, int KTOP, int FN, int U>
+__global__ __launch_bounds__(1024) void lmhead_lds_kernel(const LmArgs<T> p, int* tile_ctr) {
   using MM = Mma<T>;
   constexpr int KS = MM::KSTEP;
   constexpr int EPL = MM::EPL;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  extern __shared__ __align__(16) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int chunk = blockIdx.x;
   const int m0 = blockIdx.y * 16;
   const int D = p.a.kseg;
-  const int ngroups = p.V / (16 * FN);
-  const int t0 = (chunk * WV + wv) * p.tpw;
-  const int t1 = min(ngroups, t0 + p.tpw);
+  const int rowb = D * (int)sizeof(T) + 16;
+  // stage the 16 activation rows
+  const int cpr = D * (int)sizeof(T) / 16;  // 16-byte chunks per row
+  for (int i = tid; i < 16 * cpr; i += 1024) {
+    const int row = i / cpr, c = i - row * cpr;
+    const int m = m0 + row < p.a.M ? m0 + row : p.a.M - 1;
+    *reinterpret_cast<uint4*>(lds + row * rowb + c * 16) =
+        ld16(reinterpret_cast<const char*>(p.a.ptr[0] + (size_t)p.a.row(m) * p.a.lda) + c * 16);
+  }
   const int m = m0 + r16;
   const int arow = p.a.row(m < p.a.M ? m : p.a.M - 1);
-  const T* ap = p.a.ptr[0] + (size_t)arow * p.a.lda + kg * EPL;
   const float sc = norm_scale(p.nrm, arow, kg);
+  __syncthreads();
 
   float lv[KTOP];
   int li[KTOP];
@@ -73,33 +82,32 @@ __global__ __launch_bounds__(64 * WV) void lmhead_kernel(const LmArgs<T> p) {
     lv[k] = -INFINITY;
     li[k] = 0x7fffffff;
   }
-
+  const int ntiles = p.V / (16 * FN);
   const int nks = D / KS;
-  const int nfull = (nks / U) * U;
-  for (int t = t0; t < t1; ++t) {
+  const char* abase = lds + r16 * rowb + kg * 16;
+  for (;;) {
+    int t = 0;
+    if (lane == 0) t = atomicAdd(tile_ctr + blockIdx.y, 1);
+    t = __shfl(t, 0);
+    if (t >= ntiles) break;
     const T* wp[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) wp[fn] = p.w + (size_t)(t * 16 * FN + fn * 16 + r16) * D + kg * EPL;
     f32x4_t acc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < nfull; ks += U) {
+    for (int ks = 0; ks < nks; ks += U) {
       uint4 wf[U][FN], af[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) wf[u][fn] = ld16_stream(wp[fn] + (ks + u) * KS);
 #pragma unroll
-      for (int u = 0; u < U; ++u) af[u] = ld16(ap + (ks + u) * KS);
+      for (int u = 0; u < U; ++u) af[u] = *reinterpret_cast<const uint4*>(abase + (ks + u) * 64);
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fn] = MM::step(wf[u][fn], af[u], acc[fn]);
-    }
-    for (int ks = nfull; ks < nks; ++ks) {
-      const uint4 af = ld16(ap + ks * KS);
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) acc[fn] = MM::step(ld16_stream(wp[fn] + ks * KS), af, acc[fn]);
     }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {
@@ -111,33 +119,32 @@ __global__ __launch_bounds__(64 * WV) void lmhead_kernel(const LmArgs<T> p) {
     }
   }
 
-  // Merge: per row, WV*4 sorted lists -> one.
-  constexpr int NL = WV * 4;
-  __shared__ float sv[16][NL][KTOP];
-  __shared__ int si[16][NL][KTOP];
+  // Merge the 64 lists per row (16 waves x 4 lanes) in LDS, one row per thread.
+  __syncthreads();
+  constexpr int NL = 64;
+  float* sv = reinterpret_cast<float*>(lds);
+  int* si = reinterpret_cast<int*>(lds + 16 * NL * KTOP * sizeof(float));
 #pragma unroll
   for (int k = 0; k < KTOP; ++k) {
-    sv[r16][wv * 4 + kg][k] = lv[k];
-    si[r16][wv * 4 + kg][k] = li[k];
+    sv[(r16 * NL + wv * 4 + kg) * KTOP + k] = lv[k];
+    si[(r16 * NL + wv * 4 + kg) * KTOP + k] = li[k];
   }
   __syncthreads();
-  const int row = threadIdx.x;
-  const int mr = m0 + row;
-  if (row < 16 && mr < p.a.M) {
+  const int mr = m0 + tid;
+  if (tid < 16 && mr < p.a.M) {
     int head[NL];
 #pragma unroll
     for (int l = 0; l < NL; ++l) head[l] = 0;
-    float* ov = p.part_v + ((size_t)chunk * p.a.M + mr) * KTOP;
-    int* oi = p.part_i + ((size_t)chunk * p.a.M + mr) * KTOP;
+    float* ov = p.part_v + ((size_t)blockIdx.x * p.a.M + mr) * KTOP;
+    int* oi = p.part_i + ((size_t)blockIdx.x * p.a.M + mr) * KTOP;
     for (int k = 0; k < KTOP; ++k) {
       int best = -1;
       float bv = -INFINITY;
       int bi = 0x7fffffff;
-#pragma unroll
       for (int l = 0; l < NL; ++l) {
         if (head[l] >= KTOP) continue;
-        const float v = sv[row][l][head[l]];
-        const int id = si[row][l][head[l]];
+        const float v = sv[(tid * NL + l) * KTOP + head[l]];
+        const int id = si[(tid * NL + l) * KTOP + head[l]];
         if (best < 0 || tk_better(v, id, bv, bi)) {
           bv = v;
           bi = id;
@@ -146,9 +153,7 @@ __global__ __launch_bounds__(64 * WV) void lmhead_kernel(const LmArgs<T> p) {
       }
       ov[k] = bv;
       oi[k] = bi;
-#pragma unroll
-      for (int l = 0; l < NL; ++l)
-        if (l == best) ++head[l];
+      head[best]++;
     }
   }
 }
@@ -202,8 +207,9 @@ struct EpiTop1 {
 template <int KTOP>
 __global__ __launch_bounds__(256) void topk_merge_kernel(const float* part_v, const int* part_i,
                                                          int nchunk, int M, int top_k, int* out_ids,
-                                                         float* out_vals) {
+                                                         float* out_vals, int* tile_ctr, int nctr) {
   const int m = blockIdx.x;
+  if (m == 0 && threadIdx.x < nctr) tile_ctr[threadIdx.x] = 0;  // LM-head tile counters for the next call
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float lv[KTOP];
   int li[KTOP];

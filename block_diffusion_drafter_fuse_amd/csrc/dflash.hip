@@ -54,7 +54,6 @@ constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (L
 constexpr bool kGemvPF = false;        // prefetch the next tile's weights before the current MFMAs
 constexpr int kGemvWGs = 256;          // skinny GEMM work-groups per 16-token block
 constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, unroll
-constexpr int kTBM = 128, kTBN = 256;  // tiled GEMM work-group tile
 constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
 constexpr size_t kPartFloats = size_t(16) << 20;  // split-K partials (64 MB)
 constexpr int kCounters = 1 << 16;
@@ -77,6 +76,17 @@ struct Plan {
   int qf;
 };
 
+// Tiled GEMM work-group shapes: BM tokens x BN features, WM x WN waves, ring depth.
+template <int BM_, int BN_, int WM_, int WN_, int NBUF_>
+struct TileCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NBUF = NBUF_;
+  static constexpr int kFeatPerWave = BN / WN;  // features of one wave's fragment row
+};
+using TileStd = TileCfg<128, 128, 2, 4, 3>;   // general
+using TileWide = TileCfg<256, 256, 2, 4, 2>;  // many tokens against a wide weight (and the LM head)
+using TileLo = TileCfg<64, 128, 2, 4, 3>;     // activations as hi + lo planes
+constexpr int kWideMinFeatures = 16384;
+
 int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
 
 // Few-token LM head: one 16-wave work-group per CU and 16-row block.
@@ -84,7 +94,7 @@ int lm_chunks_small(int rowblocks) { return std::max(1, 256 / rowblocks); }
 
 // LM-head partial-list entries a call needs (KTOP = 16 for top_k > 1).
 size_t lm_entries_for(int Mlm, int V, int top_k) {
-  if (top_k == 1 && Mlm > kSkinnyMaxM) return (size_t)ceil_div(V, kTBN / 2) * Mlm;
+  if (top_k == 1 && Mlm > kSkinnyMaxM) return (size_t)ceil_div(V, TileWide::kFeatPerWave) * Mlm;
   return (size_t)lm_chunks_small(ceil_div(Mlm, 16)) * Mlm * (top_k == 1 ? 1 : 16);
 }
 
@@ -211,15 +221,39 @@ struct ProfScope {
 
 // ------------------------------------------------------------------ GEMM dispatch
 
+template <class C, typename T, bool ALO, class Epi>
+void launch_tiled(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
+                  hipStream_t st) {
+  constexpr int BKE = 128 / sizeof(T);
+  const int nst = a.nk * a.kseg / BKE;
+  const int MT = ceil_div(a.M, C::BM), NT = ceil_div(w.ngroups, C::BN / 16);
+  const int tiles = MT * NT;
+  // Split K only when the tiles alone leave CUs idle: at least 8 stages per
+  // split, partials and tickets within the workspace.
+  int SK = std::max(1, std::min(kTiledSlots / tiles, nst / 8));
+  while (SK > 1 && ((size_t)tiles * SK * C::BM * C::BN > kPartFloats || tiles > kCounters - 64)) --SK;
+  const int kps = ceil_div(nst, SK);
+  SK = ceil_div(nst, kps);
+  const SplitK sk{SK, kps, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off)};
+  const int nblocks = tiles * SK;
+  const int lds = C::NBUF * ((ALO ? 2 : 1) * C::BM + C::BN) * 128;
+  auto kern = gemm_tiled_kernel<T, C::BM, C::BN, C::WM, C::WN, C::NBUF, ALO, Epi>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(kern, dim3(round_up(nblocks, 8)), dim3(64 * C::WM * C::WN), lds, st, w, a, nrm, sk, epi,
+                     nblocks);
+}
+
 template <typename T, bool ALO = false, class Epi>
 void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
                  hipStream_t st) {
   if (a.M <= 0 || w.ngroups <= 0) return;
-  float* part = c->wsp<float>(c->p.part_off);
-  int* ctr = c->wsp<int>(c->p.ctr_off);
   const int K = a.nk * a.kseg;
   if constexpr (!Epi::kRow) {
-      if (a.M <= kSkinnyMaxM) {
+    if (a.M <= kSkinnyMaxM) {
       // Activation-stationary GEMV: 16-row tiles, K split across the waves of
       // a work-group (LDS reduction; a cross-work-group split would need
       // device-scope fences, which write back and invalidate the XCD's L2).
@@ -243,38 +277,12 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
       return;
     }
   }
-  {
-    constexpr int BKE = 128 / sizeof(T);
-    const int nst = K / BKE;
-    const int MT = ceil_div(a.M, kTBM), NT = ceil_div(w.ngroups, kTBN / 16);
-    const int tiles = MT * NT;
-    // Split K to fill the machine: minimise (rounds of kTiledSlots) x (stages per split).
-    int best = 1;
-    long long best_cost = -1;
-    for (int sk_try = 1; sk_try <= std::max(1, nst / 8); ++sk_try) {
-      const int kps = ceil_div(nst, sk_try);
-      const int skr = ceil_div(nst, kps);
-      if (skr > 1 && ((size_t)tiles * skr * kTBM * kTBN > kPartFloats || tiles > kCounters)) break;
-      const long long cost = (long long)ceil_div(tiles * skr, kTiledSlots) * kps;
-      if (best_cost < 0 || cost < best_cost) {
-        best_cost = cost;
-        best = skr;
-      }
-    }
-    const int kps = ceil_div(nst, best);
-    const int SK = ceil_div(nst, kps);
-    const SplitK sk{SK, kps, part, ctr};
-    const int nblocks = tiles * SK;
-    const int lds = 2 * ((ALO ? 2 : 1) * kTBM + kTBN) * (128 + 16);
-    auto kern = gemm_tiled_kernel<T, kTBM, kTBN, 2, 2, ALO, Epi>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds);
-      attr_set = true;
-    }
-    hipLaunchKernelGGL(kern, dim3(round_up(nblocks, 8)), dim3(256), lds, st, w, a, nrm, sk, epi, nblocks);
-  }
+  if constexpr (ALO)
+    launch_tiled<TileLo, T, true>(c, w, a, nrm, epi, st);
+  else if (Epi::kRow || (a.M >= 256 && w.ngroups * 16 >= kWideMinFeatures))
+    launch_tiled<TileWide, T, false>(c, w, a, nrm, epi, st);
+  else
+    launch_tiled<TileStd, T, false>(c, w, a, nrm, epi, st);
 }
 
 template <typename T>
@@ -472,7 +480,7 @@ void run_lmhead(dflash_ctx* c, hipStream_t st, int n_req, int top_k, int32_t* ou
   {
     ProfScope ps(c, DFLASH_K_LM_HEAD, st);
     if (top_k == 1 && Mlm > kSkinnyMaxM) {
-      nchunk = ceil_div(d.V, kTBN / 2);
+      nchunk = ceil_div(d.V, TileWide::kFeatPerWave);
       EpiTop1 epi{pv, pi, out_logits, Mlm, d.V};
       launch_gemm<T>(c, wop<T>({{c->w.w_lm, d.V}}, 0), a, nrm, epi, st);
     } else {

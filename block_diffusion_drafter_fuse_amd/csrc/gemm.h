@@ -90,9 +90,9 @@ __device__ __forceinline__ float norm_scale(const NormIn& n, int arow, int kg) {
 // the partials in split order and runs the epilogue.
 struct SplitK {
   int SK;       // splits
-  int kps;      // k-steps per split
-  float* part;  // [tiles][SK][FN * 256]
-  int* ctr;     // [tiles], zero between launches (reset by the last arriver)
+  int kps;      // K stages per split
+  float* part;  // [tiles][SK][waves][FM * FN * 256]
+  int* ctr;     // [tiles] tickets, zero between launches (reset by the last arriver)
 };
 
 // ---------------------------------------------------------------- helpers

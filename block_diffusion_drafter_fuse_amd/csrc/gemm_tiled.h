@@ -1,42 +1,78 @@
 // LDS-staged MFMA GEMM for many tokens (batched drafting, context prefill).
 //
-// Work-group tile BM tokens x BN features, 4 waves in WM x WN, each wave
-// FM x FN fragments of 16 x 16.  Each K stage covers 128 bytes of every row
-// (64 bf16 or 32 fp32 = two MFMA k-steps); stages are double-buffered in LDS
-// (rows padded by 16 bytes against bank conflicts) with the next stage's
-// global loads in flight while the current one is consumed.  With ALO the
-// activations come as bf16 hi + lo planes (both staged) and every weight
-// fragment feeds two MFMAs.  Blocks are
-// ordered so that the work-groups of one XCD walk the M tiles of a weight tile
-// back to back, which keeps that weight tile in the XCD's L2.
+// Work-group tile BM tokens x BN features, WM x WN waves, each wave FM x FN
+// fragments of 16 x 16.  Each K stage covers 128 bytes of every row
+// (64 bf16 or 32 fp32 = two MFMA k-steps).  Stages are copied global -> LDS
+// asynchronously (global_load_lds, 16 bytes per lane, no register round
+// trip) into a ring of NBUF buffers, so NBUF-1 stages are in flight while one
+// is consumed; one work-group barrier per stage.  A stage holds AR activation
+// rows then BN weight rows, 128 bytes each, with the 16-byte chunks of row r
+// stored at slot (chunk ^ (r & 7)): the copy of one wave instruction stays
+// contiguous (8 whole rows) and the fragment reads of 8 lanes (8 rows, one
+// chunk) fall on 8 distinct 16-byte bank groups.  K may be split over several
+// work-groups: each split publishes its partial tile with device-coherent
+// stores and the last one to arrive (atomic ticket) sums them and runs the
+// epilogue, with no cache write-back or invalidate.  With ALO the activations
+// come as bf16 hi + lo planes (both staged) and every weight fragment feeds
+// two MFMAs.  Blocks are ordered so that the work-groups of one XCD walk the
+// K splits and M tiles of one weight tile back to back, which keeps that
+// weight tile in the XCD's L2.
 #pragma once
 #include "gemm.h"
 
 namespace dfl {
 
-template <typename T, int BM, int BN, int WM, int WN, bool ALO, class Epi>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(const WOperand<T> w, const AOperand<T> a,
+typedef __attribute__((address_space(3))) void* lds_dst_t;
+
+// Asynchronous copy of 16 bytes per lane from `g` into LDS: lane i's bytes land
+// at wave_base + 16 * i (wave_base is wave-uniform).  Counted by vmcnt and
+// waited for explicitly (wait_vmcnt): the instruction is issued from inline
+// assembly so that the compiler does not put a full vmcnt(0) in front of every
+// LDS read that might alias a copy still in flight, which would serialise the
+// stage ring.  Nothing else in the kernels that use it keeps a value in m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, char* wave_base) {
+  const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_dst_t)wave_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// Work-group barrier for the stage ring: the wave's LDS reads are complete
+// (so a buffer may be refilled after it) and no memory access is moved across.
+// Outstanding asynchronous copies are not waited for here.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <typename T, int BM, int BN, int WM, int WN, int NBUF, bool ALO, class Epi>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand<T> w, const AOperand<T> a,
                                                          const NormIn nrm, const SplitK sk, const Epi epi,
                                                          int nblocks) {
   using MM = Mma<T>;
   constexpr int KS = MM::KSTEP;
-  constexpr int EPL = MM::EPL;
   constexpr int BKE = 128 / sizeof(T);  // elements per row per stage
   constexpr int KPS = BKE / KS;         // k-steps per stage (2)
-  constexpr int ROWB = 128 + 16;        // padded LDS row bytes
   constexpr int FM = BM / WM / 16;
   constexpr int FN = BN / WN / 16;
-  constexpr int CPR = 8;                // 16-byte chunks per row per stage
-  constexpr int AR = ALO ? 2 * BM : BM; // staged activation rows (hi, then lo)
-  constexpr int ACH = AR * CPR / 256;   // A chunks per thread
-  constexpr int WCH = BN * CPR / 256;   // W chunks per thread
+  constexpr int AR = ALO ? 2 * BM : BM;  // staged activation rows (hi, then lo)
+  constexpr int ROWS = AR + BN;
+  constexpr int SBYTES = ROWS * 128;
+  constexpr int NWV = WM * WN;
+  constexpr int NI = ROWS / (8 * NWV);  // copy instructions per wave per stage (8 rows each)
+  constexpr int NIA = AR / (8 * NWV);   // of which activation rows
   static_assert(FN % 2 == 0, "paired epilogues take fragment pairs");
-  static_assert(WM * WN == 4, "4 waves");
+  static_assert(AR % (8 * NWV) == 0 && BN % (8 * NWV) == 0, "stage rows in whole copy blocks");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  static_assert(NI * (NBUF - 2) < 64, "vmcnt range");
 
   extern __shared__ __align__(16) char lds[];
-  // stage buffer b: AR activation rows at lds + b*(AR+BN)*ROWB, W rows after them
-  auto lA = [&](int b) { return lds + b * (AR + BN) * ROWB; };
-  auto lW = [&](int b) { return lds + b * (AR + BN) * ROWB + AR * ROWB; };
 
   // XCD-grouped block order (grid padded to a multiple of 8).
   const int per_xcd = gridDim.x >> 3;
@@ -54,30 +90,27 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const WOperand<T> w, co
   const int K = a.nk * a.kseg;
   const int nst_total = K / BKE;
   const int st0 = s * sk.kps, st1 = min(nst_total, st0 + sk.kps);
+  const int nst = st1 - st0;
   const int ngroups_tile0 = bn * (BN / 16);
 
-  // Global chunk pointers for this thread (row and 16-byte column fixed per chunk).
-  const char* gA[ACH];
-  const char* gW[WCH];
-  int oA[ACH], oW[WCH];
+  // Copy assignment: instruction i of wave v fills stage rows 8*(NWV*i+v) .. +7;
+  // lane l covers row +(l>>3), slot l&7, i.e. chunk (l&7) ^ (l>>3).
+  const int crow = lane >> 3, cchunk = (lane & 7) ^ crow;
+  const char* src[NI];
 #pragma unroll
-  for (int i = 0; i < ACH; ++i) {
-    const int c = tid + i * 256;
-    const int row = c / CPR, col = c % CPR;
-    const int plane = row / BM;  // 0: hi, 1: lo
-    int m = bm * BM + (row - plane * BM);
-    m = m < a.M ? m : a.M - 1;
-    gA[i] = reinterpret_cast<const char*>(a.ptr[0] + (size_t)a.row(m) * a.lda + plane * a.lo_off) + col * 16;
-    oA[i] = row * ROWB + col * 16;
-  }
-#pragma unroll
-  for (int i = 0; i < WCH; ++i) {
-    const int c = tid + i * 256;
-    const int row = c / CPR, col = c % CPR;
-    const int gi = ngroups_tile0 + row / 16;
-    const int f = gi < w.ngroups ? w.feature_of_group(gi) + (row & 15) : (row & 15);
-    gW[i] = reinterpret_cast<const char*>(w.row(f, K)) + col * 16;
-    oW[i] = row * ROWB + col * 16;
+  for (int i = 0; i < NI; ++i) {
+    const int row = 8 * (NWV * i + wave) + crow;
+    if (i < NIA) {
+      const int plane = row / BM;  // 0: hi, 1: lo
+      int m = bm * BM + (row - plane * BM);
+      m = m < a.M ? m : a.M - 1;
+      src[i] = reinterpret_cast<const char*>(a.ptr[0] + (size_t)a.row(m) * a.lda + plane * a.lo_off) + cchunk * 16;
+    } else {
+      const int wr = row - AR;
+      const int gi = ngroups_tile0 + wr / 16;
+      const int f = gi < w.ngroups ? w.feature_of_group(gi) + (wr & 15) : (wr & 15);
+      src[i] = reinterpret_cast<const char*>(w.row(f, K)) + cchunk * 16;
+    }
   }
   // Activation segment base offset for stage st (segments are stage-aligned).
   const int st_per_seg = a.kseg / BKE;
@@ -87,21 +120,18 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const WOperand<T> w, co
     return (long)(reinterpret_cast<const char*>(a.ptr[seg]) - reinterpret_cast<const char*>(a.ptr[0])) +
            (long)(st - seg * st_per_seg) * 128;
   };
-
-  uint4 rA[ACH], rW[WCH];
-  auto gload = [&](int st) {
+  auto issue = [&](int st, int buf) {
+    char* base = lds + buf * SBYTES + wave * 1024;
     const long ao = a_off(st);
+    const long wo = (long)st * 128;
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) rA[i] = ld16(gA[i] + ao);
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) rW[i] = ld16_stream(gW[i] + (long)st * 128);
+    for (int i = 0; i < NI; ++i) dma16(src[i] + (i < NIA ? ao : wo), base + i * NWV * 1024);
   };
-  auto lstore = [&](int buf) {
+
+  // Fragment read offsets within a stage: row r16 of a 16-row block, chunk kk*4+kg.
+  int offk[KPS];
 #pragma unroll
-    for (int i = 0; i < ACH; ++i) *reinterpret_cast<uint4*>(lA(buf) + oA[i]) = rA[i];
-#pragma unroll
-    for (int i = 0; i < WCH; ++i) *reinterpret_cast<uint4*>(lW(buf) + oW[i]) = rW[i];
-  };
+  for (int kk = 0; kk < KPS; ++kk) offk[kk] = r16 * 128 + (((kk * 4 + kg) ^ (r16 & 7)) << 4);
 
   f32x4_t acc[FM][FN];
 #pragma unroll
@@ -109,27 +139,44 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const WOperand<T> w, co
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  if (st0 < st1) {
-    gload(st0);
-    lstore(0);
-    __syncthreads();
-  }
-  for (int st = st0; st < st1; ++st) {
-    const int buf = (st - st0) & 1;
-    const bool more = st + 1 < st1;
-    if (more) gload(st + 1);
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nst) issue(st0 + p, p);
+
+  int buf = 0;
+  for (int k = 0; k < nst; ++k) {
+    // Own copies of stage k done (younger stages may stay in flight), then
+    // everyone's, and everyone is past stage k-1, whose buffer is refilled next.
+    const int younger = min(NBUF - 2, nst - 1 - k);
+    if constexpr (NBUF >= 4) {
+      if (younger >= 2) wait_vmcnt<2 * NI>();
+      else if (younger == 1) wait_vmcnt<NI>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NBUF == 3) {
+      if (younger >= 1) wait_vmcnt<NI>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    ring_barrier();
+    if (k + NBUF - 1 < nst) {
+      int nb = buf + NBUF - 1;
+      nb = nb >= NBUF ? nb - NBUF : nb;
+      issue(st0 + k + NBUF - 1, nb);
+    }
+    const char* b = lds + buf * SBYTES;
 #pragma unroll
     for (int kk = 0; kk < KPS; ++kk) {
       uint4 af[FM], al[FM], wf[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const int row = wm * FM * 16 + i * 16 + r16;
-        af[i] = *reinterpret_cast<const uint4*>(lA(buf) + row * ROWB + kk * 64 + kg * 16);
-        if constexpr (ALO) al[i] = *reinterpret_cast<const uint4*>(lA(buf) + (BM + row) * ROWB + kk * 64 + kg * 16);
+        const int row = wm * FM * 16 + i * 16;
+        af[i] = *reinterpret_cast<const uint4*>(b + row * 128 + offk[kk]);
+        if constexpr (ALO) al[i] = *reinterpret_cast<const uint4*>(b + (BM + row) * 128 + offk[kk]);
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        wf[j] = *reinterpret_cast<const uint4*>(lW(buf) + (wn * FN * 16 + j * 16 + r16) * ROWB + kk * 64 + kg * 16);
+        wf[j] = *reinterpret_cast<const uint4*>(b + (AR + wn * FN * 16 + j * 16) * 128 + offk[kk]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -138,38 +185,46 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const WOperand<T> w, co
           if constexpr (ALO) acc[i][j] = MM::step(wf[j], al[i], acc[i][j]);
         }
     }
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
+    buf = buf + 1 == NBUF ? 0 : buf + 1;
   }
 
   if (sk.SK > 1) {
+    // Partials are written with agent-scope relaxed stores (coherent across
+    // XCDs, no dirty L2 lines), completed (vmcnt) before the ticket is taken;
+    // the last arriver reads the other splits with agent-scope loads.
     const int tile = bn * MT + bm;
     constexpr int WTILE = FM * FN * 256;  // floats per wave
-    float* pbase = sk.part + ((size_t)tile * sk.SK) * (4 * WTILE) + wave * WTILE;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        *reinterpret_cast<f32x4_t*>(pbase + (size_t)s * (4 * WTILE) + (i * FN + j) * 256 + lane * 4) = acc[i][j];
-    __threadfence();
-    __syncthreads();
-    __shared__ int prev_s;
-    if (tid == 0) prev_s = atomicAdd(sk.ctr + tile, 1);
-    __syncthreads();
-    if (prev_s != sk.SK - 1) return;
-    __threadfence();
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int x = 0; x < sk.SK; ++x)
+    float* pt = sk.part + (size_t)tile * sk.SK * (NWV * WTILE) + wave * WTILE;
+    {
+      float* ps = pt + (size_t)s * (NWV * WTILE);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] += *reinterpret_cast<const f32x4_t*>(pbase + (size_t)x * (4 * WTILE) + (i * FN + j) * 256 +
-                                                         lane * 4);
-    if (tid == 0) sk.ctr[tile] = 0;
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            __hip_atomic_store(ps + (i * FN + j) * 256 + c * 64 + lane, acc[i][j][c], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    int* ticket = reinterpret_cast<int*>(lds);
+    if (tid == 0) *ticket = __hip_atomic_fetch_add(sk.ctr + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*ticket != sk.SK - 1) return;
+    for (int x = 0; x < sk.SK; ++x) {
+      if (x == s) continue;
+      const float* px = pt + (size_t)x * (NWV * WTILE);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[i][j][c] += __hip_atomic_load(px + (i * FN + j) * 256 + c * 64 + lane, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(sk.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   const int g0 = ngroups_tile0 + wn * FN;

@@ -6,26 +6,29 @@
 // of the slot followed by the block's own K_b/V_b.  There is no mask.  The
 // context is cut into splits of `chunk` keys (a multiple of 64); the last
 // split also takes the block keys.  One work-group per split holds QF waves,
-// one per 16 query rows.  Keys are consumed in stages of 64: the work-group
-// copies the stage's K rows and V^T rows into LDS (double buffered, the next
-// stage's global loads in flight while the current one is consumed), so every
-// K/V byte crosses the vector-memory path once per work-group.  Each wave
-// computes S^T = K Q^T and O^T += V^T P^T with MFMA and keeps an online
+// one per 16 query rows.  Keys are consumed in stages of 64: a stage's K rows
+// and V^T tile are copied global -> LDS asynchronously (16 bytes per lane, no
+// register round trip) into a ring of NBUF buffers, one barrier per stage, so
+// every K/V byte crosses the vector-memory path once per work-group.  Each
+// wave computes S^T = K Q^T and O^T += V^T P^T with MFMA and keeps an online
 // softmax per query column, then stores its partial (max, sum, O).  The
 // combine kernel merges the splits of every (r, g) in split order, so results
 // are deterministic.
 //
-// Layouts: Q, K_b rows [M, heads*hd]; V_b transposed vbT[(r*Hkv+g)*hd + d][BP]
-// with BP = 64 (zero padded); cache keys [pos][hd] and values transposed
-// [hd][ctx_pad] per (slot, layer, head).  Within a 16*NT-key MFMA step a lane
-// holds 4*NT consecutive keys of one query column, which is exactly the key
-// run it needs as the P^T operand of the next MFMA.
+// Layouts: Q, K_b rows [M, heads*hd]; V_b transposed vbT[(r*Hkv+g)*hd + d][64]
+// (zero padded past B); cache keys [pos][hd] and values in 64-key tiles
+// [pos/64][hd][64] per (slot, layer, head), so a stage's V^T is one contiguous
+// block.  Within a 16*NT-key MFMA step a lane holds 4*NT consecutive keys of
+// one query column, which is exactly the key run it needs as the P^T operand
+// of the next MFMA.  LDS rows are unpadded; 16-byte chunk c of row r sits at
+// slot c ^ f(r), with f chosen so that the 8 rows one fragment read touches
+// per bank cycle land on distinct bank groups.
 #pragma once
-#include "common.h"
+#include "gemm_tiled.h"
 
 namespace dfl {
 
-constexpr int kAttnStage = 64;  // keys per LDS stage
+constexpr int kAttnStage = 64;  // keys per LDS stage (and per V^T cache tile)
 
 struct AttnMeta {
   int n_req;
@@ -43,7 +46,7 @@ struct AttnArgs {
   T* o;
   const T* pool;
   size_t slot_stride, layer_stride, kv_stride, head_stride;
-  int ctx_pad, layer;
+  int layer;
   int Hq, Hkv, G, B, BP, chunk;
   float scale_log2;  // log2(e) / sqrt(hd)
   float* part_o;     // [work][QR][hd]
@@ -51,24 +54,31 @@ struct AttnArgs {
   AttnMeta meta;
 };
 
-template <typename T, int HD, int QF>
+template <typename T, int HD, int QF, int NBUF>
 struct AttnStage {
-  static constexpr int KROWB = HD * (int)sizeof(T) + 16;          // padded K row bytes
-  static constexpr int VROWB = kAttnStage * (int)sizeof(T) + 16;  // padded V^T row bytes
-  static constexpr int KBYTES = kAttnStage * KROWB;
-  static constexpr int VBYTES = HD * VROWB;
+  static constexpr int KRB = HD * (int)sizeof(T);          // K row bytes
+  static constexpr int VRB = kAttnStage * (int)sizeof(T);  // V^T row bytes
+  static constexpr int KBYTES = kAttnStage * KRB;
+  static constexpr int VBYTES = HD * VRB;
   static constexpr int BUF = KBYTES + VBYTES;
-  static constexpr int KCH = HD * (int)sizeof(T) / 16;           // 16-byte chunks per K row
-  static constexpr int VCH = kAttnStage * (int)sizeof(T) / 16;   // 16-byte chunks per V^T row
-  static constexpr int NCH = kAttnStage * KCH + HD * VCH;        // chunks per stage
-  static constexpr int NTH = 64 * QF;
-  static constexpr int CPT = (NCH + NTH - 1) / NTH;              // chunks per thread
+  static constexpr int KI = KBYTES / 1024;  // copy instructions (1 KB each) per stage
+  static constexpr int VI = VBYTES / 1024;
+  static constexpr int NIW = (KI + VI) / QF;  // per wave
+  static constexpr int LDS = NBUF * BUF;
+  static_assert((KI + VI) % QF == 0 && KI % QF == 0, "copy blocks split evenly over the waves");
 };
 
-template <typename T, int HD, int QF>
+// Swizzle of K rows: the rows of one bank cycle are {4*NT*j + 4t + (0..3)}
+// for j = 0, 1 (NT = 2) or four consecutive pairs (NT = 1).
+template <int NT>
+__device__ __forceinline__ int attn_kswz(int row) {
+  return (row & 3) | (((row >> (NT == 2 ? 3 : 2)) & 1) << 2);
+}
+
+template <typename T, int HD, int QF, int NBUF>
 __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
   using MM = Mma<T>;
-  using SG = AttnStage<T, HD, QF>;
+  using SG = AttnStage<T, HD, QF, NBUF>;
   constexpr int KS = MM::KSTEP;  // keys per P.V step
   constexpr int EPL = MM::EPL;
   constexpr int NT = KS / 16;    // S^T tiles per P.V step
@@ -76,6 +86,8 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
   constexpr int DF = HD / 16;    // output d fragments
   constexpr int QR = QF * 16;
   constexpr int PVS = kAttnStage / KS;  // P.V steps per stage
+  constexpr int KCH = SG::KRB / 16, VCH = SG::VRB / 16;  // 16-byte chunks per row
+  static_assert(KCH >= 8 && VCH >= 8, "swizzle needs 8 chunks per row");
 
   extern __shared__ __align__(16) char lds[];
   const int tid = threadIdx.x;
@@ -112,41 +124,28 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
   const T* bkb = a.kb + (size_t)(r * a.B) * kd + (size_t)g * HD;
   const T* bvt = a.vbT + (size_t)(r * a.Hkv + g) * HD * a.BP;
 
-  uint4 stg[SG::CPT];
-  // global -> registers for stage i
-  auto gload = [&](int i) {
+  // Copy of stage i into buffer b: instruction j = f + QF*ii covers K rows
+  // (j < KI) or V^T rows; each lane one 16-byte chunk of one row.
+  auto issue = [&](int i, int b) {
     const bool blk = i >= nctx;
-    const int k0 = blk ? 0 : kbeg + i * kAttnStage;
-    const int ke = blk ? a.B : kend;
+    const int k0 = blk ? 0 : kbeg + i * kAttnStage;  // multiple of 64
+    char* base = lds + b * SG::BUF;
 #pragma unroll
-    for (int c = 0; c < SG::CPT; ++c) {
-      const int ch = tid + c * SG::NTH;
-      if (ch < kAttnStage * SG::KCH) {
-        const int row = ch / SG::KCH, col = ch - row * SG::KCH;
-        int key = k0 + row;
-        key = key < ke ? key : ke - 1;
-        const T* src = blk ? bkb + (size_t)key * kd : hb + (size_t)key * HD;
-        stg[c] = ld16(reinterpret_cast<const char*>(src) + col * 16);
-      } else if (ch < SG::NCH) {
-        const int vch = ch - kAttnStage * SG::KCH;
-        const int d = vch / SG::VCH, col = vch - d * SG::VCH;
-        const T* src = blk ? bvt + (size_t)d * a.BP : hb + a.kv_stride + (size_t)d * a.ctx_pad + k0;
-        stg[c] = ld16(reinterpret_cast<const char*>(src) + col * 16);
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-    char* base = lds + buf * SG::BUF;
-#pragma unroll
-    for (int c = 0; c < SG::CPT; ++c) {
-      const int ch = tid + c * SG::NTH;
-      if (ch < kAttnStage * SG::KCH) {
-        const int row = ch / SG::KCH, col = ch - row * SG::KCH;
-        *reinterpret_cast<uint4*>(base + row * SG::KROWB + col * 16) = stg[c];
-      } else if (ch < SG::NCH) {
-        const int vch = ch - kAttnStage * SG::KCH;
-        const int d = vch / SG::VCH, col = vch - d * SG::VCH;
-        *reinterpret_cast<uint4*>(base + SG::KBYTES + d * SG::VROWB + col * 16) = stg[c];
+    for (int ii = 0; ii < SG::NIW; ++ii) {
+      const int j = f + QF * ii;
+      if (j < SG::KI) {
+        constexpr int RPI = 1024 / SG::KRB;
+        const int row = j * RPI + lane / KCH;
+        const int chunk = (lane % KCH) ^ attn_kswz<NT>(row);
+        const T* src = blk ? bkb + (size_t)min(row, a.B - 1) * kd : hb + (size_t)(k0 + row) * HD;
+        dma16(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
+      } else {
+        constexpr int RPI = 1024 / SG::VRB;
+        const int row = (j - SG::KI) * RPI + lane / VCH;  // head-dim index d
+        const int chunk = (lane % VCH) ^ (row & 7);
+        const T* src = blk ? bvt + (size_t)row * a.BP
+                           : hb + a.kv_stride + ((size_t)(k0 / kAttnStage) * HD + row) * kAttnStage;
+        dma16(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
       }
     }
   };
@@ -156,12 +155,30 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
   for (int d = 0; d < DF; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrow = -INFINITY, lrow = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nst) issue(p, p);
+
+  int buf = 0;
   for (int i = 0; i < nst; ++i) {
-    const int buf = i & 1;
-    if (i + 1 < nst) gload(i + 1);
+    const int younger = min(NBUF - 2, nst - 1 - i);
+    static_assert(NBUF >= 2 && NBUF <= 4 && SG::NIW * (NBUF - 2) < 64, "ring depth");
+    if constexpr (NBUF == 4) {
+      if (younger >= 2) wait_vmcnt<2 * SG::NIW>();
+      else if (younger == 1) wait_vmcnt<SG::NIW>();
+      else wait_vmcnt<0>();
+    } else if constexpr (NBUF == 3) {
+      if (younger >= 1) wait_vmcnt<SG::NIW>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    ring_barrier();
+    if (i + NBUF - 1 < nst) {
+      int nb = buf + NBUF - 1;
+      nb = nb >= NBUF ? nb - NBUF : nb;
+      issue(i + NBUF - 1, nb);
+    }
     const bool blk = i >= nctx;
     const int klim = blk ? a.B : kend - (kbeg + i * kAttnStage);  // valid keys in this stage
     const char* kl = lds + buf * SG::BUF;
@@ -175,10 +192,12 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int krow = kb0 + (r16 >> 2) * (4 * NT) + 4 * t + (r16 & 3);
+        const char* kr = kl + krow * SG::KRB;
+        const int ksw = attn_kswz<NT>(krow);
         f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int h = 0; h < HS; ++h)
-          c = MM::step(*reinterpret_cast<const uint4*>(kl + krow * SG::KROWB + h * 64 + kg * 16), qf[h], c);
+          c = MM::step(*reinterpret_cast<const uint4*>(kr + (((h * 4 + kg) ^ ksw) << 4)), qf[h], c);
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
           const int key = kb0 + kg * (4 * NT) + 4 * t + ii;
@@ -214,15 +233,15 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
         pp.z = (uint32_t)f2bf(pr[1][0]) | ((uint32_t)f2bf(pr[1][1]) << 16);
         pp.w = (uint32_t)f2bf(pr[1][2]) | ((uint32_t)f2bf(pr[1][3]) << 16);
       }
+      const int vchunk = (kb0 + kg * 4 * NT) * (int)sizeof(T) / 16;
 #pragma unroll
       for (int d = 0; d < DF; ++d) {
-        const uint4 vf = *reinterpret_cast<const uint4*>(vl + (d * 16 + r16) * SG::VROWB +
-                                                          (kb0 + kg * 4 * NT) * (int)sizeof(T));
+        const int vrow = d * 16 + r16;
+        const uint4 vf = *reinterpret_cast<const uint4*>(vl + vrow * SG::VRB + ((vchunk ^ (vrow & 7)) << 4));
         o[d] = MM::step(vf, pp, o[d] * alpha);
       }
     }
-    if (i + 1 < nst) lstore(buf ^ 1);
-    __syncthreads();
+    buf = buf + 1 == NBUF ? 0 : buf + 1;
   }
 
   float* po = a.part_o + (size_t)w * QR * HD;
@@ -239,10 +258,10 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
 
 // Merge the splits of every (r, g): one thread per (query row, 4 channels).
 template <typename T, int HD, int QR>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs<T> a) {
+__global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs<T> a) {
   const int GB = a.G * a.B;
   const int per_rg = GB * (HD / 4);
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  const int t = blockIdx.x * 64 + threadIdx.x;
   const int rg = t / per_rg;
   if (rg >= a.meta.n_req * a.Hkv) return;
   const int rem = t - rg * per_rg;
@@ -251,9 +270,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs<T> a) 
   const int S = a.meta.nsplit[r];
   const int w0 = a.meta.work0[r] + g * S;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[((size_t)(w0 + s) * QR + qi) * 2]);
   float den = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int s = 0; s < S; ++s) {
     const float* ml = a.part_ml + ((size_t)(w0 + s) * QR + qi) * 2;
     const float e = exp2f(ml[0] - M);

@@ -48,6 +48,7 @@ constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
 constexpr int kAttnWorkMax = 4096;     // attention split work items per call
 constexpr int kAttnTargetWG = 2048;    // attention work-groups aimed for
 constexpr int kAttnMinChunk = 128;     // minimum context keys per split
+constexpr int kAttnRing = 2;           // attention stage ring depth
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
 constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (LDS: TB x waves x 1 KB)
@@ -368,7 +369,6 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
     epi.rope = rope;
     epi.Hkv = d.Hkv;
     epi.hd = d.hd;
-    epi.ctx_pad = p.ctx_pad;
     epi.use_rope = d.use_rope;
     epi.row_base = base;
     epi.meta = fm;
@@ -387,8 +387,10 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
 
 template <typename T, int HD, int QF>
 void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
-  const int lds = 2 * AttnStage<T, HD, QF>::BUF;
-  auto kern = attn_kernel<T, HD, QF>;
+  // deeper ring where the copy count per wave allows it (vmcnt range)
+  constexpr int NBUF = AttnStage<T, HD, QF, 2>::NIW * (kAttnRing - 2) < 64 ? kAttnRing : 2;
+  const int lds = AttnStage<T, HD, QF, NBUF>::LDS;
+  auto kern = attn_kernel<T, HD, QF, NBUF>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -396,7 +398,7 @@ void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
   }
   hipLaunchKernelGGL(kern, dim3(work), dim3(64 * QF), lds, st, a);
   const int threads = a.meta.n_req * a.Hkv * a.G * a.B * (HD / 4);
-  hipLaunchKernelGGL((attn_combine_kernel<T, HD, QF * 16>), dim3(ceil_div(threads, 256)), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((attn_combine_kernel<T, HD, QF * 16>), dim3(ceil_div(threads, 64)), dim3(64), 0, st, a);
 }
 
 template <typename T>
@@ -543,7 +545,6 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   aa.layer_stride = p.layer_stride;
   aa.kv_stride = p.kv_stride;
   aa.head_stride = p.head_stride;
-  aa.ctx_pad = p.ctx_pad;
   aa.Hq = d.Hq;
   aa.Hkv = d.Hkv;
   aa.G = d.Hq / d.Hkv;
@@ -853,12 +854,12 @@ int dflash_read_cache(dflash_ctx* ctx, void* stream, int32_t slot, int32_t layer
   if (ctx->d.dtype == DFLASH_BF16)
     hipLaunchKernelGGL(read_cache_kernel<bf16_t>, dim3(ceil_div(total, 256)), dim3(256), 0, st,
                        reinterpret_cast<const bf16_t*>(base),
-                       reinterpret_cast<const bf16_t*>(base + p.kv_stride * e), p.head_stride, p.ctx_pad,
+                       reinterpret_cast<const bf16_t*>(base + p.kv_stride * e), p.head_stride,
                        ctx->d.hd, ctx->d.Hkv, pos0, n, k_out, v_out);
   else
     hipLaunchKernelGGL(read_cache_kernel<float>, dim3(ceil_div(total, 256)), dim3(256), 0, st,
                        reinterpret_cast<const float*>(base),
-                       reinterpret_cast<const float*>(base + p.kv_stride * e), p.head_stride, p.ctx_pad,
+                       reinterpret_cast<const float*>(base + p.kv_stride * e), p.head_stride,
                        ctx->d.hd, ctx->d.Hkv, pos0, n, k_out, v_out);
   int rc = DFLASH_OK;
   if (!hip_ok(hipGetLastError(), "read_cache launch", &rc)) return rc;

@@ -259,7 +259,8 @@ struct EpiQKV {
 // Context projections of the fusion step: virtual weight
 // [W_kc^0; W_vc^0; W_kc^1; W_vc^1; ...], pair distance hd/2.  Keys are rotated
 // at their absolute positions and written row-major into the slot's cache;
-// values are written transposed (cache layout [Hkv][hd][ctx_pad]).
+// values are written transposed in 64-key tiles (cache layout
+// [Hkv][ctx_pad/64][hd][64]).
 template <typename T>
 struct EpiKVAppend {
   static constexpr bool kPaired = true;
@@ -267,7 +268,7 @@ struct EpiKVAppend {
   T* pool;
   size_t slot_stride, layer_stride, kv_stride, head_stride;
   const float2* rope;
-  int Hkv, hd, ctx_pad, use_rope, row_base;
+  int Hkv, hd, use_rope, row_base;
   FuseMeta meta;
   __device__ __forceinline__ void one(int m, int f, f32x4_t a, f32x4_t b) const {
     const int per_layer = 2 * Hkv * hd;
@@ -287,10 +288,11 @@ struct EpiKVAppend {
       store4<T>(dst, a[0], a[1], a[2], a[3]);
       store4<T>(dst + half, b[0], b[1], b[2], b[3]);
     } else {
+      T* tile = base + (size_t)(pos >> 6) * hd * 64 + (pos & 63);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        base[(size_t)(c + i) * ctx_pad + pos] = from_f<T>(a[i]);
-        base[(size_t)(c + half + i) * ctx_pad + pos] = from_f<T>(b[i]);
+        tile[(size_t)(c + i) * 64] = from_f<T>(a[i]);
+        tile[(size_t)(c + half + i) * 64] = from_f<T>(b[i]);
       }
     }
   }

@@ -60,10 +60,11 @@ __global__ void accept_kernel(int n_req, int B, const int* cand, int cand_stride
   bonus[r] = t[n];
 }
 
-// Read back cached K/V of one (slot, layer) into fp32 [Hkv][n][hd].
+// Read back cached K/V of one (slot, layer) into fp32 [Hkv][n][hd]; values
+// are stored in 64-key tiles [pos/64][hd][64] per head.
 template <typename T>
-__global__ void read_cache_kernel(const T* kbase, const T* vtbase, size_t head_stride, int ctx_pad,
-                                  int hd, int Hkv, int pos0, int n, float* kout, float* vout) {
+__global__ void read_cache_kernel(const T* kbase, const T* vtbase, size_t head_stride, int hd, int Hkv,
+                                  int pos0, int n, float* kout, float* vout) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   const int total = Hkv * n * hd;
   if (idx >= total) return;
@@ -71,7 +72,8 @@ __global__ void read_cache_kernel(const T* kbase, const T* vtbase, size_t head_s
   const int rem = idx - g * n * hd;
   const int p = rem / hd, d = rem - p * hd;
   kout[idx] = to_f<T>(kbase[(size_t)g * head_stride + (size_t)(pos0 + p) * hd + d]);
-  vout[idx] = to_f<T>(vtbase[(size_t)g * head_stride + (size_t)d * ctx_pad + pos0 + p]);
+  const int pos = pos0 + p;
+  vout[idx] = to_f<T>(vtbase[(size_t)g * head_stride + ((size_t)(pos >> 6) * hd + d) * 64 + (pos & 63)]);
 }
 
 }  // namespace dfl

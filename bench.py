@@ -23,6 +23,7 @@ workload.
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
@@ -63,8 +64,10 @@ def kernel_work(d, wl):
     w["embed"] = (M * d.D * (4 + e), 0.0, 1)
     w["norm"] = (M * d.D * (4 + e), 0.0, 2 * d.N + 1)
     w["qkv_gemm"] = (qkv * d.D * e + M * d.D * e + M * qkv * e, 2.0 * M * qkv * d.D, d.N)
-    w["attention"] = (sctx * 2 * d.Hkv * d.hd * e + M * (2 * d.Hq + 2 * d.Hkv) * d.hd * e,
+    w["attention"] = (sctx * 2 * d.Hkv * d.hd * e + M * (d.Hq + 2 * d.Hkv) * d.hd * e,
                       sum(4.0 * d.Hq * B * (c + B) * d.hd for c in wl.ctx), d.N)
+    # the split partials are not algorithmic traffic: only the attention output counts
+    w["attn_combine"] = (M * d.Hq * d.hd * e, 0.0, d.N)
     w["o_gemm"] = (d.D * d.Hq * d.hd * e + M * d.Hq * d.hd * e + 2 * M * d.D * 4,
                    2.0 * M * d.D * d.Hq * d.hd, d.N)
     w["gateup_gemm"] = (2 * d.I * d.D * e + M * d.D * e + M * d.I * e, 2.0 * M * 2 * d.I * d.D, d.N)
@@ -99,6 +102,69 @@ def roof_entry(kind, d, wl, ms_per_launch, traffic):
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic, "kernel": kind,
             "launch_ms": round(ms_per_launch, 5), "algorithmic_bytes": byts}
+
+
+# Kernel kind of a dispatch from its (demangled) name, in draft-step order; the
+# output and down projections share an epilogue and alternate within a layer.
+KIND_PATTERNS = (("EpiQKV", "qkv_gemm"), ("attn_combine", "attn_combine"), ("attn_kernel", "attention"),
+                 ("EpiSwiGLU", "gateup_gemm"), ("EpiTop1", "lm_head"), ("lmhead_lds", "lm_head"),
+                 ("topk_merge", "topk_merge"), ("embed_kernel", "embed"))
+
+
+def kind_of_dispatch(name, prev):
+    if "EpiResidualNorm" in name:
+        return "down_gemm" if prev == "gateup_gemm" else "o_gemm"
+    for pat, kind in KIND_PATTERNS:
+        if pat in name:
+            return kind
+    return None
+
+
+def read_counter_csv(path, counter):
+    """[(kernel name, value)] per dispatch, in dispatch order, from a rocprofv3
+    counter_collection.csv."""
+    per = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            did = int(r["Dispatch_Id"])
+            name, v = per.get(did, (r["Kernel_Name"], 0.0))
+            per[did] = (name, v + float(r["Counter_Value"]))
+    return [per[k] for k in sorted(per)]
+
+
+def traffic_summary(fetch_csv, write_csv, copy_mib, workload):
+    """HBM bytes per launch per kernel kind from one FETCH_SIZE and one
+    WRITE_SIZE run (KiB per dispatch), each scaled by what the same counter
+    reads for the reference pass over copy_mib MiB (the last elementwise dispatch
+    of the run: copy_mib MiB read, copy_mib MiB written)."""
+    out = {}
+    for path, counter, key in ((fetch_csv, "FETCH_SIZE", "fetch"), (write_csv, "WRITE_SIZE", "write")):
+        disp = read_counter_csv(path, counter)
+        copies = [v for n, v in disp if "elementwise" in n]
+        if not copies or copies[-1] <= 0:
+            raise SystemExit(f"{path}: no reference copy dispatch with a {counter} value")
+        factor = copy_mib * 1024.0 / copies[-1]
+        out[f"{key}_factor"] = round(factor, 4)
+        prev = None
+        vals = {}
+        for name, v in disp:
+            kind = kind_of_dispatch(name, prev)
+            if kind is None:
+                continue
+            prev = kind
+            vals.setdefault(kind, []).append(v * factor * 1024.0)
+        out[key] = {k: (float(np.median(v)), len(v)) for k, v in vals.items()}
+    kernels = {}
+    for kind in out["fetch"]:
+        if kind not in out["write"]:
+            continue
+        fb, n = out["fetch"][kind]
+        wb, _ = out["write"][kind]
+        kernels[f"{workload}:{kind}"] = {"bytes_per_launch": int(fb + wb), "fetch_bytes": int(fb),
+                                         "write_bytes": int(wb), "dispatches": n}
+    return {"fetch_factor": out["fetch_factor"], "write_factor": out["write_factor"], "kernels": kernels}
 
 
 def source_sha():
@@ -290,7 +356,34 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_bs32")
     ap.add_argument("--companion", default="qwen3_8b_bs1", help="second workload reported under 'bs1' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, copy one buffer of this many MiB (reference dispatch for byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE) of a run with --copy-probe-mib; needs no GPU")
     args = ap.parse_args()
+    if args.traffic_from:
+        if not args.copy_probe_mib:
+            ap.error("--traffic-from needs the --copy-probe-mib of the profiled run")
+        t = traffic_summary(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib, args.workload)
+        p = os.path.join(ROOT, "profiles", "traffic.json")
+        old = {}
+        if os.path.exists(p):
+            try:
+                old = json.load(open(p))
+            except ValueError:
+                old = {}
+        kernels = old.get("kernels", {}) if old.get("source_sha") == source_sha() else {}
+        kernels.update(t["kernels"])
+        doc = {"source_sha": source_sha(), "copy_probe_mib": args.copy_probe_mib,
+               "factors": {**old.get("factors", {}),
+                           args.workload: {"fetch": t["fetch_factor"], "write": t["write_factor"]}},
+               "kernels": kernels}
+        os.makedirs(os.path.dirname(p), exist_ok=True)
+        with open(p, "w") as fh:
+            json.dump(doc, fh, indent=1, sort_keys=True)
+        print(json.dumps(doc["kernels"], indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the draft step shards by request across GPUs with no exchange; see DESIGN.md)",
@@ -315,6 +408,14 @@ def main():
         assert wc.dims == wl.dims, "companion must share the model shape"
         print(f"[bench] measuring {args.companion}", file=sys.stderr, flush=True)
         comp = measure(wc, w_dev, torch, args.steps, args.warmup, args.companion)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)  # one elementwise kernel: n bytes in, n bytes out
+        torch.cuda.synchronize()
+        del src, dst
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -25,7 +25,7 @@ EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fus
             "dflash_strerror", "dflash_last_error")
 
 KERNEL_KINDS = ("fuse_gemm", "fuse_norm", "ctx_kv_gemm", "embed", "norm", "qkv_gemm", "attention",
-                "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "accept")
+                "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "accept")
 
 
 class DflashError(RuntimeError):

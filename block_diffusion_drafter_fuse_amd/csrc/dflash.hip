@@ -385,8 +385,14 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
 
 // ------------------------------------------------------------------ attention
 
+// Split-KV partial kernel (combine = false) or the combine kernel (true).
 template <typename T, int HD, int QF>
-void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
+void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
+  if (combine) {
+    const int threads = a.meta.n_req * a.Hkv * a.G * a.B * (HD / 4);
+    hipLaunchKernelGGL((attn_combine_kernel<T, HD, QF * 16>), dim3(ceil_div(threads, 64)), dim3(64), 0, st, a);
+    return;
+  }
   // deeper ring where the copy count per wave allows it (vmcnt range)
   constexpr int NBUF = AttnStage<T, HD, QF, 2>::NIW * (kAttnRing - 2) < 64 ? kAttnRing : 2;
   const int lds = AttnStage<T, HD, QF, NBUF>::LDS;
@@ -397,20 +403,18 @@ void launch_attn(const AttnArgs<T>& a, int work, hipStream_t st) {
     attr_set = true;
   }
   hipLaunchKernelGGL(kern, dim3(work), dim3(64 * QF), lds, st, a);
-  const int threads = a.meta.n_req * a.Hkv * a.G * a.B * (HD / 4);
-  hipLaunchKernelGGL((attn_combine_kernel<T, HD, QF * 16>), dim3(ceil_div(threads, 64)), dim3(64), 0, st, a);
 }
 
 template <typename T>
-void attn_dispatch(const AttnArgs<T>& a, int work, int hd, int qf, hipStream_t st) {
+void attn_dispatch(const AttnArgs<T>& a, int work, int hd, int qf, bool combine, hipStream_t st) {
   if (hd == 128) {
-    if (qf == 1) launch_attn<T, 128, 1>(a, work, st);
-    else if (qf == 2) launch_attn<T, 128, 2>(a, work, st);
-    else launch_attn<T, 128, 4>(a, work, st);
+    if (qf == 1) launch_attn<T, 128, 1>(a, work, combine, st);
+    else if (qf == 2) launch_attn<T, 128, 2>(a, work, combine, st);
+    else launch_attn<T, 128, 4>(a, work, combine, st);
   } else {
-    if (qf == 1) launch_attn<T, 64, 1>(a, work, st);
-    else if (qf == 2) launch_attn<T, 64, 2>(a, work, st);
-    else launch_attn<T, 64, 4>(a, work, st);
+    if (qf == 1) launch_attn<T, 64, 1>(a, work, combine, st);
+    else if (qf == 2) launch_attn<T, 64, 2>(a, work, combine, st);
+    else launch_attn<T, 64, 4>(a, work, combine, st);
   }
 }
 
@@ -579,7 +583,11 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     aa.layer = l;
     {
       ProfScope ps(c, DFLASH_K_ATTENTION, st);
-      attn_dispatch<T>(aa, apl.work, d.hd, p.qf, st);
+      attn_dispatch<T>(aa, apl.work, d.hd, p.qf, false, st);
+    }
+    {
+      ProfScope ps(c, DFLASH_K_ATTN_COMBINE, st);
+      attn_dispatch<T>(aa, apl.work, d.hd, p.qf, true, st);
     }
     {
       ProfScope ps(c, DFLASH_K_O_GEMM, st);

@@ -193,7 +193,8 @@ enum dflash_kernel_kind {
   DFLASH_K_EMBED,           /* block assembly */
   DFLASH_K_NORM,            /* pre-attention / pre-FFN / final RMSNorm */
   DFLASH_K_QKV_GEMM,        /* block Q/K_b/V_b projection + RoPE */
-  DFLASH_K_ATTENTION,       /* KV-injected block attention (split + combine) */
+  DFLASH_K_ATTENTION,       /* KV-injected block attention, split-KV partials */
+  DFLASH_K_ATTN_COMBINE,    /* merge of the attention splits */
   DFLASH_K_O_GEMM,          /* output projection + residual */
   DFLASH_K_GATEUP_GEMM,     /* gate/up projection + SwiGLU */
   DFLASH_K_DOWN_GEMM,       /* down projection + residual */

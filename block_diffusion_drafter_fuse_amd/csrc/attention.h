@@ -256,31 +256,53 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
   }
 }
 
-// Merge the splits of every (r, g): one thread per (query row, 4 channels).
-template <typename T, int HD, int QR>
-__global__ __launch_bounds__(64) void attn_combine_kernel(const AttnArgs<T> a) {
+// Merge the splits of every (r, g).  SUB consecutive lanes share one
+// (query row, 4 channels) output: lane `sub` folds splits sub, sub+SUB, ...
+// with a running maximum, then the SUB partial states are merged with
+// shuffles in a fixed pattern, so results are deterministic.
+template <typename T, int HD, int QR, int SUB>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const AttnArgs<T> a) {
   const int GB = a.G * a.B;
   const int per_rg = GB * (HD / 4);
-  const int t = blockIdx.x * 64 + threadIdx.x;
-  const int rg = t / per_rg;
-  if (rg >= a.meta.n_req * a.Hkv) return;
-  const int rem = t - rg * per_rg;
-  const int qi = rem / (HD / 4), d4 = rem - qi * (HD / 4);
-  const int r = rg / a.Hkv, g = rg - r * a.Hkv;
-  const int S = a.meta.nsplit[r];
+  const long t = (long)blockIdx.x * 256 + threadIdx.x;
+  const int sub = (int)(t % SUB);
+  const long o = t / SUB;
+  const int rg = (int)(o / per_rg);
+  const bool live = rg < a.meta.n_req * a.Hkv;
+  const int rgc = live ? rg : 0;
+  const int rem = (int)(o - (long)rgc * per_rg);
+  const int qi = live ? rem / (HD / 4) : 0, d4 = live ? rem - qi * (HD / 4) : 0;
+  const int r = rgc / a.Hkv, g = rgc - r * a.Hkv;
+  const int S = live ? a.meta.nsplit[r] : 0;
   const int w0 = a.meta.work0[r] + g * S;
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[((size_t)(w0 + s) * QR + qi) * 2]);
-  float den = 0.f;
+  float M = -INFINITY, den = 0.f;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int s = 0; s < S; ++s) {
-    const float* ml = a.part_ml + ((size_t)(w0 + s) * QR + qi) * 2;
-    const float e = exp2f(ml[0] - M);
-    den += e * ml[1];
-    acc += e * *reinterpret_cast<const f32x4_t*>(a.part_o + ((size_t)(w0 + s) * QR + qi) * HD + d4 * 4);
+  for (int s = sub; s < S; s += SUB) {
+    const size_t pidx = (size_t)(w0 + s) * QR + qi;
+    const float mv = a.part_ml[pidx * 2], lv = a.part_ml[pidx * 2 + 1];
+    const f32x4_t ov = *reinterpret_cast<const f32x4_t*>(a.part_o + pidx * HD + d4 * 4);
+    const float Mn = fmaxf(M, mv);
+    const float rs = exp2f(M - Mn), e = exp2f(mv - Mn);
+    den = den * rs + e * lv;
+    acc = acc * rs + e * ov;
+    M = Mn;
   }
+#pragma unroll
+  for (int x = 1; x < SUB; x <<= 1) {
+    const float M2 = __shfl_xor(M, x);
+    const float d2 = __shfl_xor(den, x);
+    f32x4_t a2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a2[i] = __shfl_xor(acc[i], x);
+    const float Mn = fmaxf(M, M2);
+    const float r1 = M == -INFINITY ? 0.f : exp2f(M - Mn);
+    const float r2 = M2 == -INFINITY ? 0.f : exp2f(M2 - Mn);
+    den = den * r1 + d2 * r2;
+    acc = acc * r1 + a2 * r2;
+    M = Mn;
+  }
+  if (!live || sub != 0) return;
   const float inv = 1.0f / den;
   const int hl = qi / a.B, j = qi - hl * a.B;
   T* op = a.o + (size_t)(r * a.B + j) * (a.Hq * HD) + (size_t)(g * a.G + hl) * HD + d4 * 4;

@@ -48,7 +48,6 @@ constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
 constexpr int kAttnWorkMax = 4096;     // attention split work items per call
 constexpr int kAttnTargetWG = 2048;    // attention work-groups aimed for
 constexpr int kAttnMinChunk = 128;     // minimum context keys per split
-constexpr int kAttnRing = 2;           // attention stage ring depth
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
 constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (LDS: TB x waves x 1 KB)
@@ -93,10 +92,16 @@ int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
 // Few-token LM head: one 16-wave work-group per CU and 16-row block.
 int lm_chunks_small(int rowblocks) { return std::max(1, 256 / rowblocks); }
 
+// Top-1 LM head through the GEMM engines: one partial per 16-row tile (GEMV,
+// few rows) or per wave fragment row of the wide tiled GEMM (many rows).
+int lm_top1_chunks(int Mlm, int V) {
+  return Mlm <= kSkinnyMaxM ? ceil_div(V, 16) : ceil_div(V, TileWide::kFeatPerWave);
+}
+
 // LM-head partial-list entries a call needs (KTOP = 16 for top_k > 1).
 size_t lm_entries_for(int Mlm, int V, int top_k) {
-  if (top_k == 1 && Mlm > kSkinnyMaxM) return (size_t)ceil_div(V, TileWide::kFeatPerWave) * Mlm;
-  return (size_t)lm_chunks_small(ceil_div(Mlm, 16)) * Mlm * (top_k == 1 ? 1 : 16);
+  if (top_k == 1) return (size_t)lm_top1_chunks(Mlm, V) * Mlm;
+  return (size_t)lm_chunks_small(ceil_div(Mlm, 16)) * Mlm * 16;
 }
 
 int validate_dims(const dflash_dims* d) {
@@ -253,7 +258,7 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
                  hipStream_t st) {
   if (a.M <= 0 || w.ngroups <= 0) return;
   const int K = a.nk * a.kseg;
-  if constexpr (!Epi::kRow) {
+  {
     if (a.M <= kSkinnyMaxM) {
       // Activation-stationary GEMV: 16-row tiles, K split across the waves of
       // a work-group (LDS reduction; a cross-work-group split would need
@@ -389,12 +394,19 @@ void run_fuse(dflash_ctx* c, hipStream_t st, const FuseMeta& fm, int total, cons
 template <typename T, int HD, int QF>
 void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
   if (combine) {
-    const int threads = a.meta.n_req * a.Hkv * a.G * a.B * (HD / 4);
-    hipLaunchKernelGGL((attn_combine_kernel<T, HD, QF * 16>), dim3(ceil_div(threads, 64)), dim3(64), 0, st, a);
+    int smax = 1;
+    for (int r = 0; r < a.meta.n_req; ++r) smax = std::max(smax, a.meta.nsplit[r]);
+    const long outs = (long)a.meta.n_req * a.Hkv * a.G * a.B * (HD / 4);
+    auto go = [&](auto kern, int sub) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)ceil_div_l(outs * sub, 256)), dim3(256), 0, st, a);
+    };
+    // lanes per output only when the split loops are long (few outputs, many splits)
+    if (smax >= 16) go(attn_combine_kernel<T, HD, QF * 16, 8>, 8);
+    else go(attn_combine_kernel<T, HD, QF * 16, 1>, 1);
     return;
   }
-  // deeper ring where the copy count per wave allows it (vmcnt range)
-  constexpr int NBUF = AttnStage<T, HD, QF, 2>::NIW * (kAttnRing - 2) < 64 ? kAttnRing : 2;
+  // Two work-groups per CU: a ring of 2 stages of K/V each.
+  constexpr int NBUF = 2;
   const int lds = AttnStage<T, HD, QF, NBUF>::LDS;
   auto kern = attn_kernel<T, HD, QF, NBUF>;
   static bool attr_set = false;
@@ -485,22 +497,21 @@ void run_lmhead(dflash_ctx* c, hipStream_t st, int n_req, int top_k, int32_t* ou
   int nchunk;
   {
     ProfScope ps(c, DFLASH_K_LM_HEAD, st);
-    if (top_k == 1 && Mlm > kSkinnyMaxM) {
-      nchunk = ceil_div(d.V, TileWide::kFeatPerWave);
-      EpiTop1 epi{pv, pi, out_logits, Mlm, d.V};
+    if (top_k == 1) {
+      nchunk = lm_top1_chunks(Mlm, d.V);
+      EpiTop1 epi{pv, pi, out_logits, Mlm, d.V, nchunk};
       launch_gemm<T>(c, wop<T>({{c->w.w_lm, d.V}}, 0), a, nrm, epi, st);
     } else {
       const int rowblocks = ceil_div(Mlm, 16);
       nchunk = lm_chunks_small(rowblocks);
       LmArgs<T> la{a, nrm, static_cast<const T*>(c->w.w_lm), d.V, out_logits, pv, pi};
-      if (top_k == 1) launch_lm_small<T, 1>(la, nchunk, rowblocks, tile_ctr, st);
-      else launch_lm_small<T, 16>(la, nchunk, rowblocks, tile_ctr, st);
+      launch_lm_small<T, 16>(la, nchunk, rowblocks, tile_ctr, st);
     }
   }
   ProfScope ps(c, DFLASH_K_TOPK_MERGE, st);
   if (top_k == 1)
-    hipLaunchKernelGGL((topk_merge_kernel<1>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, Mlm, top_k, out_ids,
-                       out_vals, tile_ctr, 64);
+    hipLaunchKernelGGL(top1_merge_kernel, dim3(Mlm), dim3(1024), 0, st, pv, pi, nchunk, out_ids, out_vals, tile_ctr,
+                       64);
   else
     hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, Mlm, top_k,
                        out_ids, out_vals, tile_ctr, 64);

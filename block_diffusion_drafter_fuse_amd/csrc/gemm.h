@@ -446,10 +446,14 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
         for (int w2 = 1; w2 < NW; ++w2) sum[p] += red[(tl * NW + w2) * 64 + lane];
       }
       const int t = b0 + j * PT;
-      if constexpr (Epi::kPaired)
+      if constexpr (Epi::kRow) {
+        const int fb1[1] = {w.feature_of_group(t)};
+        epi.template apply_row<1>(m, m < a.M, 1, fb1, sum, sc, kg);
+      } else if constexpr (Epi::kPaired) {
         epi.apply2(m, m < a.M, w.feature_of_group(t) + 4 * kg, sum[0] * sc, sum[1] * sc);
-      else
+      } else {
         epi.apply1(m, m < a.M, w.feature_of_group(t) + 4 * kg, sum[0] * sc);
+      }
     }
     __syncthreads();
   }

@@ -40,7 +40,7 @@ struct LmArgs {
   const T* w;       // [V, D]
   int V;
   float* logits;    // nullable [M, V]
-  float* part_v;    // [nchunk][M][KTOP]
+  float* part_v;    // [M][nchunk][KTOP]
   int* part_i;
 };
 
@@ -135,8 +135,8 @@ __global__ __launch_bounds__(1024) void lmhead_lds_kernel(const LmArgs<T> p, int
     int head[NL];
 #pragma unroll
     for (int l = 0; l < NL; ++l) head[l] = 0;
-    float* ov = p.part_v + ((size_t)blockIdx.x * p.a.M + mr) * KTOP;
-    int* oi = p.part_i + ((size_t)blockIdx.x * p.a.M + mr) * KTOP;
+    float* ov = p.part_v + ((size_t)mr * gridDim.x + blockIdx.x) * KTOP;
+    int* oi = p.part_i + ((size_t)mr * gridDim.x + blockIdx.x) * KTOP;
     for (int k = 0; k < KTOP; ++k) {
       int best = -1;
       float bv = -INFINITY;
@@ -163,10 +163,10 @@ __global__ __launch_bounds__(1024) void lmhead_lds_kernel(const LmArgs<T> p, int
 struct EpiTop1 {
   static constexpr bool kPaired = false;
   static constexpr bool kRow = true;
-  float* part_v;   // [ceil(V / (16*FN))][M]
+  float* part_v;   // [M][nchunk], chunk = 16*FN vocabulary rows
   int* part_i;
   float* logits;   // nullable [M, V]
-  int M, V;
+  int M, V, nchunk;
   template <int FN>
   __device__ __forceinline__ void apply_row(int m, bool mvalid, int nvalid, const int (&fb)[FN],
                                             const f32x4_t (&acc)[FN], float sc, int kg) const {
@@ -194,7 +194,7 @@ struct EpiTop1 {
       }
     }
     if (mvalid && nvalid > 0 && (threadIdx.x & 63) < 16) {
-      const size_t idx = (size_t)(fb[0] / (16 * FN)) * M + m;
+      const size_t idx = (size_t)m * nchunk + fb[0] / (16 * FN);
       part_v[idx] = bv;
       part_i[idx] = bi;
     }
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* part_v, co
   const int total = nchunk * KTOP;
   for (int c = tid; c < total; c += 256) {
     const int ch = c / KTOP, k = c - ch * KTOP;
-    const size_t idx = ((size_t)ch * M + m) * KTOP + k;
+    const size_t idx = ((size_t)m * nchunk + ch) * KTOP + k;
     tk_insert<KTOP>(lv, li, part_v[idx], part_i[idx]);
   }
   __shared__ float sv[KTOP][256];
@@ -264,6 +264,51 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const float* part_v, co
       if (out_vals) out_vals[(size_t)m * top_k + k] = bv;
     }
     __syncthreads();
+  }
+}
+
+// Top-1 merge: one 1024-thread work-group per row scans the row's contiguous
+// partial list (coalesced), then reduces across the waves in LDS.
+__global__ __launch_bounds__(1024) void top1_merge_kernel(const float* part_v, const int* part_i, int nchunk,
+                                                          int* out_ids, float* out_vals, int* tile_ctr,
+                                                          int nctr) {
+  const int m = blockIdx.x;
+  if (m == 0 && threadIdx.x < nctr) tile_ctr[threadIdx.x] = 0;  // small LM-head tile counters, next call
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* pv = part_v + (size_t)m * nchunk;
+  const int* pi = part_i + (size_t)m * nchunk;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int c = tid; c < nchunk; c += 1024)
+    if (tk_better(pv[c], pi[c], bv, bi)) {
+      bv = pv[c];
+      bi = pi[c];
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float v2 = __shfl_xor(bv, o);
+    const int i2 = __shfl_xor(bi, o);
+    if (tk_better(v2, i2, bv, bi)) {
+      bv = v2;
+      bi = i2;
+    }
+  }
+  __shared__ float wv[16];
+  __shared__ int wi[16];
+  if (lane == 0) {
+    wv[wave] = bv;
+    wi[wave] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int nw = blockDim.x >> 6;
+    for (int w = 1; w < nw; ++w)
+      if (tk_better(wv[w], wi[w], bv, bi)) {
+        bv = wv[w];
+        bi = wi[w];
+      }
+    out_ids[m] = bi;
+    if (out_vals) out_vals[m] = bv;
   }
 }
 

@@ -11,7 +11,8 @@ Sources (web pages on the method; cited by page title and section):
     section 二 "注意力模式", section 三 (KV injection, fusion equation),
     section 四 (inference pseudocode; engineering note on cached projected KV).
   * "DFlow 完全拆解" (pinghaoyang.com.cn): the fusion equation in the section on
-    DFlash's recomputation window; the accept/reject split in the opening section.
+    DFlash's recomputation window; the accept/reject split in the opening section;
+    relay steps 1-3 and the inference-loop section (the relay, `oracle/dflow.py`).
   * DFlash system/training/deployment notes (blog.hotdry.top), section 2.
 
 Where the pages leave a step open, the reading taken is stated at the function.
@@ -22,6 +23,13 @@ and the worked examples stored under tests/golden/).  Forward values at the
 full model shapes are pinned only through those properties: the pages print no
 output values for any input.
 """
+from .dflow import (  # noqa: F401
+    RelayState,
+    block_inputs,
+    layer_norm,
+    relay_inputs,
+    relay_plan,
+)
 from .dflash import (  # noqa: F401
     ContextCache,
     OracleDrafter,

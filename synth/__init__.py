@@ -10,8 +10,11 @@ from .gen import (  # noqa: F401
     as_f32,
     bf16_bits_to_f32,
     f32_to_bf16_bits,
+    draw_accepted,
     make_anchors,
     make_hidden,
+    make_relay_weights,
+    make_suffix_hidden,
     make_targets,
     make_weights,
     draw_first_mismatch,

@@ -50,6 +50,7 @@ class Workload:
     n_new: List[int]
     seed: int
     note: str = ""
+    rounds: int = 1     # draft-verify rounds (the relay workload iterates)
 
 
 def _tiny(B=8, L=3) -> Dims:
@@ -97,7 +98,14 @@ def get_config(name: str) -> Workload:
         return Workload(QWEN3_8B, bs=32, ctx=ctx, n_new=n_new, seed=3,
                         note="Qwen3-8B-shaped drafter, bs 32 ragged, ctx ~ U{512..8192}, "
                              "tau_prev ~ clamped geometric mean 6.5")
+    if name == "dflow_relay":
+        # Tiny drafter with 5 tapped target layers and B = 16; 8 requests
+        # prefilled with 64 context tokens, then 64 draft-verify rounds with
+        # accepted counts drawn from U{0..15}.
+        return Workload(_tiny(B=16, L=5), bs=8, ctx=[64] * 8, n_new=[64] * 8, seed=5,
+                        note="DFlow relay on the tiny fp32 drafter, L 5, B 16, bs 8, 64 rounds",
+                        rounds=64)
     raise KeyError(name)
 
 
-CONFIGS = ("tiny", "qwen3_4b_bs1", "qwen3_8b_bs1", "qwen3_8b_bs32")
+CONFIGS = ("tiny", "qwen3_4b_bs1", "qwen3_8b_bs1", "qwen3_8b_bs32", "dflow_relay")

@@ -129,6 +129,14 @@ def make_weights(d: Dims, seed: int) -> dict:
     return w
 
 
+def make_relay_weights(d: Dims, seed: int) -> dict:
+    """Relay MLP weights in storage dtype: w1 [D, 3D], w2 [2D, D], ~N(0, 0.02).
+    Tensor indices start at 10000 so they never meet the drafter's."""
+    s = 1000 + seed
+    return {"w1": _fill((d.D, 3 * d.D), [s, 10000], 0.02, 0.0, d.dtype),
+            "w2": _fill((2 * d.D, d.D), [s, 10001], 0.02, 0.0, d.dtype)}
+
+
 def weights_as_f32(w: dict) -> dict:
     """Exact float32 view of the stored weights (bf16 bits are upcast)."""
     def cv(a):
@@ -170,6 +178,23 @@ def make_hidden(d: Dims, seed: int, req: int, start: int, n: int) -> List[np.nda
     else:
         list(_pool().map(work, jobs))
     return out
+
+
+def make_suffix_hidden(d: Dims, seed: int, req: int, rnd: int, n: int) -> List[np.ndarray]:
+    """Verifier features [n, Dt] per tapped layer for the n reusable rejected
+    positions of request `req` in round `rnd` (a stream of its own: these are
+    states of a branch that is not committed)."""
+    out = []
+    for l in range(d.L):
+        out.append(_fill((n, d.Dt), [2000 + seed, 88, req, rnd, l], 1.0, 0.0, d.dtype) if n
+                   else np.zeros((0, d.Dt), dtype=np.float32 if d.dtype == "f32" else np.uint16))
+    return out
+
+
+def draw_accepted(bs: int, rounds: int, B: int, seed: int) -> np.ndarray:
+    """Accepted candidate counts n ~ U{0..B-1} per (round, request)."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([3000 + seed, 7])))
+    return rng.integers(0, B, size=(rounds, bs))
 
 
 def make_anchors(d: Dims, seed: int, bs: int) -> np.ndarray:

@@ -21,11 +21,11 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",
 
 EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fuse_ctx",
             "dflash_draft_block", "dflash_accept", "dflash_slot_reset", "dflash_slot_len",
-            "dflash_read_cache", "dflash_profile_enable", "dflash_profile_read",
-            "dflash_strerror", "dflash_last_error")
+            "dflash_read_cache", "dflow_relay", "dflow_read_relay", "dflash_profile_enable",
+            "dflash_profile_read", "dflash_strerror", "dflash_last_error")
 
 KERNEL_KINDS = ("fuse_gemm", "fuse_norm", "ctx_kv_gemm", "embed", "norm", "qkv_gemm", "attention",
-                "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "accept")
+                "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "relay", "accept")
 
 
 class DflashError(RuntimeError):
@@ -54,6 +54,10 @@ class dflash_weights(ctypes.Structure):
         ("layers", ctypes.POINTER(dflash_layer_weights))]
 
 
+class dflow_relay_weights(ctypes.Structure):
+    _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
+
+
 _LIB = None
 
 
@@ -78,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.dflash_slot_reset.argtypes = [vp, i32, i32]
     L.dflash_slot_len.argtypes = [vp, i32, P(i32)]
     L.dflash_read_cache.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    L.dflow_relay.argtypes = [vp, vp, i32, P(i32), P(i32), vp, i32, vp, P(vp), P(dflow_relay_weights)]
+    L.dflow_read_relay.argtypes = [vp, vp, i32, vp, P(i32)]
     L.dflash_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
     L.dflash_profile_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.dflash_strerror.argtypes = [ctypes.c_int]
@@ -209,6 +215,21 @@ class Drafter:
         cnt = (ctypes.c_int32 * n)()
         _check(lib().dflash_profile_read(self.h, ms, cnt), "dflash_profile_read")
         return {KERNEL_KINDS[i]: (ms[i], cnt[i]) for i in range(n) if cnt[i]}
+
+    def relay(self, slots: Sequence[int], n_acc: Sequence[int], cand, cand_stride: int, bonus,
+              hidden: Sequence, w1, w2, stream=None):
+        """dflow_relay: hidden holds L device tensors [sum(max(0, B-2-n)), Dt]
+        (the reusable rejected-suffix features, grouped by request)."""
+        ptrs = (ctypes.c_void_p * max(1, len(hidden)))(*[_ptr(t) for t in hidden])
+        rw = dflow_relay_weights(_ptr(w1), _ptr(w2))
+        _check(lib().dflow_relay(self.h, _stream(stream), len(slots), _i32(slots), _i32(n_acc), _ptr(cand),
+                                 int(cand_stride), _ptr(bonus), ptrs, ctypes.byref(rw)), "dflow_relay")
+
+    def read_relay(self, slot: int, out, stream=None) -> int:
+        n = ctypes.c_int32()
+        _check(lib().dflow_read_relay(self.h, _stream(stream), int(slot), _ptr(out), ctypes.byref(n)),
+               "dflow_read_relay")
+        return n.value
 
     def read_cache(self, slot: int, layer: int, pos0: int, n: int, k_out, v_out, stream=None):
         _check(lib().dflash_read_cache(self.h, _stream(stream), int(slot), int(layer), int(pos0), int(n),

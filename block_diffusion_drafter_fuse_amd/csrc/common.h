@@ -88,6 +88,28 @@ __device__ __forceinline__ int fuse_req_of_row(const FuseMeta& fm, int m) {
   return r;
 }
 
+// Request metadata of one relay call (relay rows grouped by request).
+struct RelayMeta {
+  int n_req;
+  int row0[kMaxReq + 1];  // first relay row of request r
+  int slot[kMaxReq];
+  int nacc[kMaxReq];      // accepted candidates of request r's round
+};
+
+__device__ __forceinline__ int relay_req_of_row(const RelayMeta& rm, int m) {
+  int r = 0;
+  while (r + 1 < rm.n_req && m >= rm.row0[r + 1]) ++r;
+  return r;
+}
+
+// Relay rows a draft call reads: for request r, rows[(slot[r]*B + j)*D] hold
+// the inputs of block offsets j = 2 .. 1 + n[r] (n[r] = 0: none).
+struct DraftRelay {
+  const float* rows;
+  int slot[kMaxReq];
+  int n[kMaxReq];
+};
+
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
 __device__ __forceinline__ float wave_max(float v) {

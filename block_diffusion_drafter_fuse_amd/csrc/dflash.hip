@@ -65,12 +65,14 @@ int ceil_div_l(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 struct Plan {
   // pool
-  size_t kv_off, rope_off, pool_bytes;
+  size_t kv_off, rope_off, relay_off, pool_bytes;
   size_t head_stride, kv_stride, layer_stride, slot_stride;  // elements
   int ctx_pad;
   // workspace
   size_t x_off, u_off, ssq_off, q_off, kb_off, vbt_off, o_off, h_off;
-  size_t po_off, pml_off, lmv_off, lmi_off, hc_off, hclo_off, fssq_off, part_off, ctr_off, ws_bytes;
+  size_t po_off, pml_off, lmv_off, lmi_off, hc_off, hclo_off, fssq_off, part_off, ctr_off;
+  size_t rin_off, rlnh_off, rs_off, ws_bytes;
+  int relay_rows;  // relay rows one call can hold: max_batch * (B - 2)
   int BP;
   size_t lm_entries;
   int qf;
@@ -141,6 +143,8 @@ void make_plan(const dflash_dims* d, Plan* p) {
   off = align_up(off + p->slot_stride * d->max_slots * e);
   p->rope_off = off;
   off = align_up(off + (size_t)(d->max_ctx + d->B) * (d->hd / 2) * sizeof(float2));
+  p->relay_off = off;  // DFlow relay rows [max_slots][B][D] fp32
+  off = align_up(off + (size_t)d->max_slots * d->B * d->D * 4);
   p->pool_bytes = off;
 
   const int M = d->max_batch * d->B;
@@ -172,6 +176,10 @@ void make_plan(const dflash_dims* d, Plan* p) {
   p->fssq_off = off; off = align_up(off + (size_t)kFuseChunk * nslot * 4);
   p->part_off = off; off = align_up(off + kPartFloats * 4);
   p->ctr_off = off;  off = align_up(off + (size_t)kCounters * 4);
+  p->relay_rows = d->max_batch * std::max(0, d->B - 2);
+  p->rin_off = off;  off = align_up(off + (size_t)p->relay_rows * 3 * d->D * e);
+  p->rlnh_off = off; off = align_up(off + (size_t)p->relay_rows * d->D * 4);
+  p->rs_off = off;   off = align_up(off + (size_t)p->relay_rows * d->D * e);
   p->ws_bytes = off;
 }
 
@@ -200,6 +208,8 @@ struct dflash_ctx {
   char* pool;
   char* ws;
   std::vector<int> len;
+  std::vector<int> relay_n;    // DFlow relay rows stored per slot (offsets 2..1+n)
+  std::vector<int> relay_len;  // slot length they were stored at
   template <typename T> T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
 
@@ -521,7 +531,8 @@ void run_lmhead(dflash_ctx* c, hipStream_t st, int n_req, int top_k, int32_t* ou
 
 template <typename T>
 void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, const int32_t* anchor,
-               int top_k, int32_t* out_ids, float* out_vals, float* out_logits, const AttnPlan& apl) {
+               int top_k, int32_t* out_ids, float* out_vals, float* out_logits, const AttnPlan& apl,
+               const DraftRelay& rl) {
   const dflash_dims& d = c->d;
   const Plan& p = c->p;
   const int M = n_req * d.B;
@@ -547,7 +558,7 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     ProfScope ps(c, DFLASH_K_EMBED, st);
     hipLaunchKernelGGL((embed_kernel<T>), dim3(M), dim3(256), 0, st, static_cast<const T*>(c->w.embed),
                        static_cast<const T*>(c->w.e_mask), anchor, static_cast<const T*>(c->layers[0].g_attn), d.B,
-                       d.D, d.V, x, u, ssq);
+                       d.D, d.V, x, u, ssq, rl);
   }
 
   AttnArgs<T> aa{};
@@ -623,6 +634,41 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
 
 // ====================================================================== C ABI
 
+// ------------------------------------------------------------------ DFlow relay
+
+template <typename T>
+void run_relay(dflash_ctx* c, hipStream_t st, const RelayMeta& rm, int total, const void* const* hid,
+               const int32_t* cand, int cand_stride, const int32_t* bonus, const dflow_relay_weights* rw) {
+  const dflash_dims& d = c->d;
+  const Plan& p = c->p;
+  T* hc = c->wsp<T>(p.hc_off);
+  float* fssq = c->wsp<float>(p.fssq_off);
+  T* in = c->wsp<T>(p.rin_off);
+  float* lnh = c->wsp<float>(p.rlnh_off);
+  T* sbuf = c->wsp<T>(p.rs_off);
+  const NormIn none{nullptr, 0, 0.f, 0.f};
+  {
+    // relay step 1: the shared fusion projection of the suffix states
+    ProfScope ps(c, DFLASH_K_FUSE_GEMM, st);
+    AOperand<T> a{};
+    for (int l = 0; l < d.L; ++l) a.ptr[l] = static_cast<const T*>(hid[l]);
+    a.nk = d.L;
+    a.kseg = d.Dt;
+    a.lda = d.Dt;
+    a.M = total;
+    launch_gemm<T>(c, wop<T>({{c->w.w_c, d.D}}, 0), a, none,
+                   EpiNormOut<T>{hc, nullptr, static_cast<const T*>(c->w.g_c), fssq, d.D, d.D / 16}, st);
+  }
+  ProfScope ps(c, DFLASH_K_RELAY, st);
+  hipLaunchKernelGGL((relay_assemble_kernel<T>), dim3(total), dim3(256), 0, st, hc, fssq, d.D, d.rms_eps,
+                     static_cast<const T*>(c->w.embed), d.V, bonus, cand, cand_stride, d.B - 1, rm, in, lnh);
+  // relay step 3: [beta; gamma] = w2 SiLU(w1 [E(bonus); E(first rejection); h])
+  launch_gemm<T>(c, wop<T>({{rw->w1, d.D}}, 0), aop<T>(in, total, 3 * d.D), none, EpiSiLUOut<T>{sbuf, d.D}, st);
+  EpiRelayOut<T> eo{reinterpret_cast<float*>(c->pool + p.relay_off), lnh, static_cast<const T*>(c->w.e_mask),
+                    d.B, d.D, rm};
+  launch_gemm<T>(c, wop<T>({{rw->w2, 2 * d.D}}, d.D), aop<T>(sbuf, total, d.D), none, eo, st);
+}
+
 extern "C" {
 
 const char* dflash_strerror(int status) {
@@ -684,6 +730,8 @@ int dflash_create(const dflash_dims* dims, const dflash_weights* weights, void* 
   c->pool = static_cast<char*>(kv_pool);
   c->ws = static_cast<char*>(workspace);
   c->len.assign(dims->max_slots, 0);
+  c->relay_n.assign(dims->max_slots, 0);
+  c->relay_len.assign(dims->max_slots, -1);
 
   rc = DFLASH_OK;
   if (!hip_ok(hipMemsetAsync(kv_pool, 0, p.pool_bytes, nullptr), "hipMemsetAsync(pool)", &rc) ||
@@ -756,6 +804,7 @@ int dflash_slot_reset(dflash_ctx* ctx, int32_t slot, int32_t keep_len) {
   if (keep_len < 0 || keep_len > ctx->len[slot])
     return fail(DFLASH_EINVAL, "keep_len must be in 0..current length");
   ctx->len[slot] = keep_len;
+  ctx->relay_n[slot] = 0;
   return DFLASH_OK;
 }
 
@@ -832,12 +881,23 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32
   const int Mlm = n_req * (ctx->d.B - 1);
   if (lm_entries_for(Mlm, ctx->d.V, top_k) > ctx->p.lm_entries)
     return fail(DFLASH_ECAPACITY, "LM-head partial buffer too small");
+  // DFlow relay rows of this round (stored at the slot's current length)
+  DraftRelay rl{};
+  bool any = false;
+  for (int r = 0; r < n_req; ++r) {
+    const int s = slot[r];
+    rl.slot[r] = s;
+    rl.n[r] = (ctx->relay_n[s] > 0 && ctx->relay_len[s] == ctx->len[s]) ? ctx->relay_n[s] : 0;
+    any = any || rl.n[r] > 0;
+  }
+  rl.rows = any ? reinterpret_cast<const float*>(ctx->pool + ctx->p.relay_off) : nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (ctx->d.dtype == DFLASH_BF16)
-    run_draft<bf16_t>(ctx, st, n_req, slot, anchor, top_k, out_ids, out_vals, out_logits, apl);
+    run_draft<bf16_t>(ctx, st, n_req, slot, anchor, top_k, out_ids, out_vals, out_logits, apl, rl);
   else
-    run_draft<float>(ctx, st, n_req, slot, anchor, top_k, out_ids, out_vals, out_logits, apl);
+    run_draft<float>(ctx, st, n_req, slot, anchor, top_k, out_ids, out_vals, out_logits, apl, rl);
   if (!hip_ok(hipGetLastError(), "draft launch", &rc)) return rc;
+  for (int r = 0; r < n_req; ++r) ctx->relay_n[slot[r]] = 0;  // a relay lives for one round
   return DFLASH_OK;
 }
 
@@ -854,6 +914,70 @@ int dflash_accept(void* stream, int32_t n_req, int32_t B, const int32_t* cand, i
                      cand_stride, target, tau, bonus);
   int rc = DFLASH_OK;
   if (!hip_ok(hipGetLastError(), "accept launch", &rc)) return rc;
+  return DFLASH_OK;
+}
+
+int dflow_relay(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot, const int32_t* n_acc,
+                const int32_t* cand, int32_t cand_stride, const int32_t* bonus,
+                const void* const* tgt_hidden, const dflow_relay_weights* rw) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  int rc = check_slots(ctx, n_req, slot);
+  if (rc) return rc;
+  if (n_req == 0) return DFLASH_OK;
+  if (!n_acc) return fail(DFLASH_EINVAL, "n_acc is NULL");
+  const int B = ctx->d.B;
+  long long total = 0;
+  for (int r = 0; r < n_req; ++r) {
+    if (n_acc[r] < 0 || n_acc[r] > B - 1) return fail(DFLASH_EINVAL, "n_acc must be in 0..B-1");
+    total += std::max(0, B - 2 - n_acc[r]);
+  }
+  RelayMeta rm{};
+  rm.n_req = n_req;
+  int row = 0;
+  for (int r = 0; r < n_req; ++r) {
+    rm.row0[r] = row;
+    rm.slot[r] = slot[r];
+    rm.nacc[r] = n_acc[r];
+    row += std::max(0, B - 2 - n_acc[r]);
+  }
+  rm.row0[n_req] = row;
+  if (total > 0) {
+    if (!cand || !bonus) return fail(DFLASH_EINVAL, "cand and bonus must not be NULL");
+    if (cand_stride < 1) return fail(DFLASH_EINVAL, "cand_stride must be >= 1");
+    if (!rw || !rw->w1 || !rw->w2) return fail(DFLASH_EINVAL, "relay weights must not be NULL");
+    if (!tgt_hidden) return fail(DFLASH_EINVAL, "tgt_hidden is NULL");
+    for (int l = 0; l < ctx->d.L; ++l)
+      if (!tgt_hidden[l]) return fail(DFLASH_EINVAL, "a tgt_hidden layer pointer is NULL");
+    if (total > ctx->p.relay_rows) return fail(DFLASH_ECAPACITY, "relay rows exceed max_batch * (B - 2)");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (ctx->d.dtype == DFLASH_BF16)
+      run_relay<bf16_t>(ctx, st, rm, (int)total, tgt_hidden, cand, cand_stride, bonus, rw);
+    else
+      run_relay<float>(ctx, st, rm, (int)total, tgt_hidden, cand, cand_stride, bonus, rw);
+    if (!hip_ok(hipGetLastError(), "relay launch", &rc)) return rc;
+  }
+  for (int r = 0; r < n_req; ++r) {
+    ctx->relay_n[slot[r]] = std::max(0, B - 2 - n_acc[r]);
+    ctx->relay_len[slot[r]] = ctx->len[slot[r]];
+  }
+  return DFLASH_OK;
+}
+
+int dflow_read_relay(dflash_ctx* ctx, void* stream, int32_t slot, float* out, int32_t* count) {
+  g_last_error.clear();
+  if (!ctx || !out || !count) return fail(DFLASH_EINVAL, "NULL argument");
+  if (slot < 0 || slot >= ctx->d.max_slots) return fail(DFLASH_ECAPACITY, "slot out of range");
+  const int n = ctx->relay_len[slot] == ctx->len[slot] ? ctx->relay_n[slot] : 0;
+  *count = n;
+  if (n == 0) return DFLASH_OK;
+  const size_t D = ctx->d.D;
+  const float* src = reinterpret_cast<const float*>(ctx->pool + ctx->p.relay_off) + ((size_t)slot * ctx->d.B + 2) * D;
+  int rc = DFLASH_OK;
+  if (!hip_ok(hipMemcpyAsync(out + 2 * D, src, (size_t)n * D * sizeof(float), hipMemcpyDeviceToDevice,
+                             static_cast<hipStream_t>(stream)),
+              "relay read copy", &rc))
+    return rc;
   return DFLASH_OK;
 }
 

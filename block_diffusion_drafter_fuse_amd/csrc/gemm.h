@@ -301,6 +301,44 @@ struct EpiKVAppend {
   }
 };
 
+// DFlow relay MLP, first layer: s = T(SiLU(v)).
+template <typename T>
+struct EpiSiLUOut {
+  static constexpr bool kPaired = false;
+  static constexpr bool kRow = false;
+  T* s;
+  int ld;
+  __device__ __forceinline__ void apply1(int m, bool valid, int f, f32x4_t v) const {
+    if (valid) store4<T>(s + (size_t)m * ld + f, silu(v[0]), silu(v[1]), silu(v[2]), silu(v[3]));
+  }
+};
+
+// DFlow relay MLP, second layer over the virtual weight w2 with pair distance
+// D: a holds beta, b gamma for features f..f+3; x = e_mask + beta * LN(h) +
+// gamma is stored (fp32) for the slot's next block at offset 2 + (row index
+// within the request).
+template <typename T>
+struct EpiRelayOut {
+  static constexpr bool kPaired = true;
+  static constexpr bool kRow = false;
+  float* rows;         // [max_slots][B][D]
+  const float* lnh;    // [relay rows][D]
+  const T* e_mask;
+  int B, D;
+  RelayMeta meta;
+  __device__ __forceinline__ void apply2(int m, bool valid, int f, f32x4_t a, f32x4_t b) const {
+    if (!valid) return;
+    const int r = relay_req_of_row(meta, m);
+    const int j = 2 + m - meta.row0[r];
+    float* dst = rows + ((size_t)meta.slot[r] * B + j) * D + f;
+    const float* ln = lnh + (size_t)m * D + f;
+    f32x4_t x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = to_f<T>(e_mask[f + i]) + a[i] * ln[i] + b[i];
+    *reinterpret_cast<f32x4_t*>(dst) = x;
+  }
+};
+
 // ---------------------------------------------------------------- helpers for the GEMM kernels
 
 template <typename T>

@@ -6,33 +6,89 @@
 namespace dfl {
 
 // Block assembly: row r*B + j of the fp32 residual stream is the anchor's
-// token embedding (j == 0) or the shared mask embedding (j > 0).  Also writes
-// the first layer's normed-input operand u = T(x * g) and per-16-feature sums
-// of squares (the RMSNorm is completed by the consuming GEMM).
+// token embedding (j == 0), a DFlow relay row stored for the request's slot
+// (2 <= j < 2 + relay n), or the shared mask embedding.  Also writes the first
+// layer's normed-input operand u = T(x * g) and per-16-feature sums of squares
+// (the RMSNorm is completed by the consuming GEMM).
 template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const T* e_mask, const int* anchor,
                                                     const T* g, int B, int D, int V, float* x, T* u,
-                                                    float* ssq) {
+                                                    float* ssq, const DraftRelay rl) {
   const int m = blockIdx.x;
   const int r = m / B, j = m - r * B;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const T* src;
+  const T* src = nullptr;
+  const float* rsrc = nullptr;
   if (j == 0) {
     int a = anchor[r];
     a = a < 0 ? 0 : (a >= V ? V - 1 : a);
     src = embed + (size_t)a * D;
+  } else if (rl.rows && j >= 2 && j < 2 + rl.n[r]) {
+    rsrc = rl.rows + ((size_t)rl.slot[r] * B + j) * D;
   } else {
     src = e_mask;
   }
   const int nslot = D >> 4;
   for (int c = wave; c < (D >> 6); c += 4) {
     const int d = c * 64 + lane;
-    const float v = to_f<T>(src[d]);
+    const float v = rsrc ? rsrc[d] : to_f<T>(src[d]);
     x[(size_t)m * D + d] = v;
     u[(size_t)m * D + d] = from_f<T>(v * to_f<T>(g[d]));
     float ss = v * v;
     for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
     if ((lane & 15) == 0) ssq[(size_t)m * nslot + (d >> 4)] = ss;
+  }
+}
+
+// DFlow relay, per relay row m (one work-group): completes the RMSNorm of the
+// shared fusion projection (hc holds T(z * g_c), fssq the per-16-feature sums
+// of squares of z), then writes the relay MLP input row
+// [E(bonus); E(first rejection); h] (K = 3D, storage dtype) and LN(h) in fp32
+// (population variance, eps 1e-5, no affine).
+template <typename T>
+__global__ __launch_bounds__(256) void relay_assemble_kernel(const T* hc, const float* fssq, int D, float eps,
+                                                             const T* embed, int V, const int* bonus,
+                                                             const int* cand, int cand_stride, int Bm1,
+                                                             const RelayMeta rm, T* in, float* lnh) {
+  const int m = blockIdx.x;
+  const int r = relay_req_of_row(rm, m);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float red[2][4];
+  const int nslot = D >> 4;
+  // mean of z^2 from the slot sums
+  float ss = 0.f;
+  for (int i = tid; i < nslot; i += 256) ss += fssq[(size_t)m * nslot + i];
+  ss = wave_sum(ss);
+  if (lane == 0) red[0][wave] = ss;
+  __syncthreads();
+  const float rs = rsqrtf((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)D + eps);
+  // mean and variance of h = T(z*g) * rs
+  float s1 = 0.f;
+  for (int c = tid; c < D; c += 256) s1 += to_f<T>(hc[(size_t)m * D + c]) * rs;
+  s1 = wave_sum(s1);
+  if (lane == 0) red[1][wave] = s1;
+  __syncthreads();
+  const float mu = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (float)D;
+  float s2 = 0.f;
+  for (int c = tid; c < D; c += 256) {
+    const float dv = to_f<T>(hc[(size_t)m * D + c]) * rs - mu;
+    s2 += dv * dv;
+  }
+  s2 = wave_sum(s2);
+  __syncthreads();
+  if (lane == 0) red[0][wave] = s2;
+  __syncthreads();
+  const float rstd = rsqrtf((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)D + 1e-5f);
+  int b = bonus[r], y = cand[((size_t)r * Bm1 + rm.nacc[r]) * cand_stride];
+  b = b < 0 ? 0 : (b >= V ? V - 1 : b);
+  y = y < 0 ? 0 : (y >= V ? V - 1 : y);
+  T* row = in + (size_t)m * 3 * D;
+  for (int c = tid; c < D; c += 256) {
+    const float h = to_f<T>(hc[(size_t)m * D + c]) * rs;
+    row[c] = embed[(size_t)b * D + c];
+    row[D + c] = embed[(size_t)y * D + c];
+    row[2 * D + c] = from_f<T>(h);
+    lnh[(size_t)m * D + c] = (h - mu) * rstd;
   }
 }
 

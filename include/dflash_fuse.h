@@ -154,7 +154,10 @@ int dflash_fuse_ctx(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t*
  *                          (logit descending, id ascending)
  *   out_vals  nullable [n_req, B-1, top_k] float: the matching logits
  *   out_logits nullable [n_req, B-1, V] float: all logits (debug)
- * Slot lengths are not changed: the block's own K/V are transient. */
+ * Slot lengths are not changed: the block's own K/V are transient.
+ * Relay rows stored for a slot by dflow_relay at the slot's current length
+ * replace the mask embedding at their block offsets; every slot of the call
+ * then has its relay cleared (the relay lives for one round). */
 int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot,
                        const int32_t* anchor, int32_t top_k, int32_t* out_ids,
                        float* out_vals, float* out_logits);
@@ -185,6 +188,52 @@ int dflash_slot_len(const dflash_ctx* ctx, int32_t slot, int32_t* len);
 int dflash_read_cache(dflash_ctx* ctx, void* stream, int32_t slot, int32_t layer, int32_t pos0,
                       int32_t n, float* k_out, float* v_out);
 
+/* DFlow relay weights (storage dtype, row-major [out, in]): the two bias-free
+ * layers of the relay MLP with a SiLU between them.
+ *   w1 [D, 3D]  over the concatenation [E(bonus); E(first rejection); h]
+ *   w2 [2D, D]  rows 0..D-1 give beta, rows D..2D-1 give gamma */
+typedef struct dflow_relay_weights {
+  const void* w1;
+  const void* w2;
+} dflow_relay_weights;
+
+/* DFlow relay of the rejected suffix ("DFlow 完全拆解", relay steps 1-3 and the
+ * inference-loop section).  Call after the round's committed rows have been
+ * fused (dflash_fuse_ctx), so that each slot's length is the position of its
+ * next anchor (the bonus token).  For request r of the round just verified,
+ * with n = n_acc[r] accepted candidates (0..B-1), the reusable suffix is block
+ * offsets n+2 .. B-1 (the first rejection, offset n+1, is not reused):
+ * k_r = max(0, B-2-n) rows.  For each such row the verifier features h are
+ * projected with the shared W_c and RMSNorm (the fusion step), then
+ *   [beta; gamma] = w2 SiLU(w1 [E(bonus[r]); E(cand[r][n]); h])
+ *   x = e_mask + beta * LN(h) + gamma      (LN: no affine, eps 1e-5)
+ * and x is stored for the slot's next block at offset 2 .. B-1-n (the state of
+ * offset o serves the prediction of the next position, which is next-block
+ * offset o - n).  A request with k_r = 0 only clears its slot's relay.
+ *   slot [host, n_req]    distinct slot ids
+ *   n_acc [host, n_req]   accepted candidates of the round, 0..B-1
+ *   cand [n_req, B-1] int32 (device) with row stride cand_stride: the round's
+ *                         candidates (cand[r][n] is the first rejection)
+ *   bonus [n_req] int32 (device): the bonus tokens
+ *   tgt_hidden [host, L]  L device pointers, each [sum(k_r), Dt] in the storage
+ *                         dtype: verifier features of offsets n+2..B-1, grouped
+ *                         by request, in offset order (may be NULL if all
+ *                         k_r = 0)
+ *   rw                    relay MLP weights
+ * Stored rows are bound to the slot and its current length: the next
+ * dflash_draft_block on the slot at that length uses them; a draft at another
+ * length, dflash_slot_reset or the next dflow_relay drops them.  Uses the
+ * workspace. */
+int dflow_relay(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot, const int32_t* n_acc,
+                const int32_t* cand, int32_t cand_stride, const int32_t* bonus,
+                const void* const* tgt_hidden, const dflow_relay_weights* rw);
+
+/* Copy the relay rows currently stored for a slot into out [B, D] float
+ * (device; row j is block offset j, rows without relay are left untouched)
+ * and return their count in *count [host] (they occupy offsets 2..count+1).
+ * For inspection and tests. */
+int dflow_read_relay(dflash_ctx* ctx, void* stream, int32_t slot, float* out, int32_t* count);
+
 /* Kernel kinds, for per-kernel timing. */
 enum dflash_kernel_kind {
   DFLASH_K_FUSE_GEMM = 0,   /* context fusion GEMM W_c [H^(l1);...] */
@@ -200,6 +249,7 @@ enum dflash_kernel_kind {
   DFLASH_K_DOWN_GEMM,       /* down projection + residual */
   DFLASH_K_LM_HEAD,         /* LM head with fused top-k */
   DFLASH_K_TOPK_MERGE,      /* top-k merge */
+  DFLASH_K_RELAY,           /* DFlow relay: assembly and the relay MLP GEMMs */
   DFLASH_K_ACCEPT,          /* acceptance scan (stateless call: never timed) */
   DFLASH_K_COUNT
 };

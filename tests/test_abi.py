@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(dfa.LIB_PATH), reason="librar
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:dflash|dflow)_[a-z_]+)\s*\(", src)))
 
 
 def test_header_declares_the_abi():
@@ -125,3 +125,13 @@ def test_strerror():
     assert L.dflash_strerror(0) == b"ok"
     assert L.dflash_strerror(-3) == b"capacity exceeded"
     assert L.dflash_strerror(42) == b"unknown status"
+
+
+def test_relay_rejects_null_ctx_and_arguments():
+    L = dfa.lib()
+    slots = (ctypes.c_int32 * 1)(0)
+    nacc = (ctypes.c_int32 * 1)(3)
+    rw = dfa.dflow_relay_weights(None, None)
+    assert L.dflow_relay(None, None, 1, slots, nacc, None, 1, None, None, ctypes.byref(rw)) == -1
+    n = ctypes.c_int32()
+    assert L.dflow_read_relay(None, None, 0, None, ctypes.byref(n)) == -1

@@ -21,11 +21,11 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",
 
 EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fuse_ctx",
             "dflash_draft_block", "dflash_accept", "dflash_slot_reset", "dflash_slot_len",
-            "dflash_read_cache", "dflow_relay", "dflow_read_relay", "dflash_profile_enable",
+            "dflash_read_cache", "dflow_relay", "dflow_read_relay", "dflash2_select", "dflash_profile_enable",
             "dflash_profile_read", "dflash_strerror", "dflash_last_error")
 
 KERNEL_KINDS = ("fuse_gemm", "fuse_norm", "ctx_kv_gemm", "embed", "norm", "qkv_gemm", "attention",
-                "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "relay", "accept")
+                "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "relay", "select", "accept")
 
 
 class DflashError(RuntimeError):
@@ -58,6 +58,10 @@ class dflow_relay_weights(ctypes.Structure):
     _fields_ = [("w1", ctypes.c_void_p), ("w2", ctypes.c_void_p)]
 
 
+class dflash2_selector_weights(ctypes.Structure):
+    _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("w_h", ctypes.c_void_p), ("rank", ctypes.c_int32)]
+
+
 _LIB = None
 
 
@@ -84,6 +88,7 @@ def lib() -> ctypes.CDLL:
     L.dflash_read_cache.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
     L.dflow_relay.argtypes = [vp, vp, i32, P(i32), P(i32), vp, i32, vp, P(vp), P(dflow_relay_weights)]
     L.dflow_read_relay.argtypes = [vp, vp, i32, vp, P(i32)]
+    L.dflash2_select.argtypes = [vp, vp, i32, vp, vp, vp, i32, P(dflash2_selector_weights), vp, vp]
     L.dflash_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
     L.dflash_profile_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.dflash_strerror.argtypes = [ctypes.c_int]
@@ -224,6 +229,16 @@ class Drafter:
         rw = dflow_relay_weights(_ptr(w1), _ptr(w2))
         _check(lib().dflow_relay(self.h, _stream(stream), len(slots), _i32(slots), _i32(n_acc), _ptr(cand),
                                  int(cand_stride), _ptr(bonus), ptrs, ctypes.byref(rw)), "dflow_relay")
+
+    def select(self, n_req: int, anchor, cand, cand_logits, k: int, tables: dict, out_path, out_scores=None,
+               stream=None):
+        """dflash2_select over the most recent draft_block call's final hidden
+        states; tables holds device tensors a, b [V, rank] and w_h [rank, D]."""
+        sw = dflash2_selector_weights(_ptr(tables["a"]), _ptr(tables["b"]), _ptr(tables["w_h"]),
+                                      int(tables["a"].shape[1]))
+        _check(lib().dflash2_select(self.h, _stream(stream), int(n_req), _ptr(anchor), _ptr(cand),
+                                    _ptr(cand_logits), int(k), ctypes.byref(sw), _ptr(out_path), _ptr(out_scores)),
+               "dflash2_select")
 
     def read_relay(self, slot: int, out, stream=None) -> int:
         n = ctypes.c_int32()

@@ -71,7 +71,7 @@ struct Plan {
   // workspace
   size_t x_off, u_off, ssq_off, q_off, kb_off, vbt_off, o_off, h_off;
   size_t po_off, pml_off, lmv_off, lmi_off, hc_off, hclo_off, fssq_off, part_off, ctr_off;
-  size_t rin_off, rlnh_off, rs_off, ws_bytes;
+  size_t rin_off, rlnh_off, rs_off, sel_off, ws_bytes;
   int relay_rows;  // relay rows one call can hold: max_batch * (B - 2)
   int BP;
   size_t lm_entries;
@@ -180,6 +180,7 @@ void make_plan(const dflash_dims* d, Plan* p) {
   p->rin_off = off;  off = align_up(off + (size_t)p->relay_rows * 3 * d->D * e);
   p->rlnh_off = off; off = align_up(off + (size_t)p->relay_rows * d->D * 4);
   p->rs_off = off;   off = align_up(off + (size_t)p->relay_rows * d->D * e);
+  p->sel_off = off;  off = align_up(off + (size_t)Mlm * 256 * 4);  // selector gates [rows][rank <= 256]
   p->ws_bytes = off;
 }
 
@@ -210,6 +211,7 @@ struct dflash_ctx {
   std::vector<int> len;
   std::vector<int> relay_n;    // DFlow relay rows stored per slot (offsets 2..1+n)
   std::vector<int> relay_len;  // slot length they were stored at
+  int last_draft_n = 0;        // requests of the most recent draft (its final hidden states are in the workspace)
   template <typename T> T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
 
@@ -669,6 +671,24 @@ void run_relay(dflash_ctx* c, hipStream_t st, const RelayMeta& rm, int total, co
   launch_gemm<T>(c, wop<T>({{rw->w2, 2 * d.D}}, d.D), aop<T>(sbuf, total, d.D), none, eo, st);
 }
 
+// ------------------------------------------------------------------ DFlash 2 selector
+
+template <typename T>
+void run_select(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* anchor, const int32_t* cand,
+                const float* ul, int k, const dflash2_selector_weights* sw, int32_t* out_path, float* out_scores) {
+  const dflash_dims& d = c->d;
+  const Plan& p = c->p;
+  const int Mlm = n_req * (d.B - 1);
+  float* gates = c->wsp<float>(p.sel_off);
+  ProfScope ps(c, DFLASH_K_SELECT, st);
+  // H(h_t) = sigmoid(w_h h_t) over the LM head's operand (the final normed hidden states)
+  launch_gemm<T>(c, wop<T>({{sw->w_h, sw->rank}}, 0), aop<T>(c->wsp<T>(p.u_off), Mlm, d.D, d.B),
+                 norm_in(c->wsp<float>(p.ssq_off), d.D, d.rms_eps), EpiSigmoidOut{gates, sw->rank}, st);
+  hipLaunchKernelGGL((select_kernel<T>), dim3(n_req), dim3(256), 0, st, anchor, cand, ul, k, d.B - 1,
+                     static_cast<const T*>(sw->a), static_cast<const T*>(sw->b), sw->rank, gates, d.V, out_path,
+                     out_scores);
+}
+
 extern "C" {
 
 const char* dflash_strerror(int status) {
@@ -898,6 +918,7 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32
     run_draft<float>(ctx, st, n_req, slot, anchor, top_k, out_ids, out_vals, out_logits, apl, rl);
   if (!hip_ok(hipGetLastError(), "draft launch", &rc)) return rc;
   for (int r = 0; r < n_req; ++r) ctx->relay_n[slot[r]] = 0;  // a relay lives for one round
+  ctx->last_draft_n = n_req;
   return DFLASH_OK;
 }
 
@@ -978,6 +999,26 @@ int dflow_read_relay(dflash_ctx* ctx, void* stream, int32_t slot, float* out, in
                              static_cast<hipStream_t>(stream)),
               "relay read copy", &rc))
     return rc;
+  return DFLASH_OK;
+}
+
+int dflash2_select(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* anchor, const int32_t* cand,
+                   const float* cand_logits, int32_t k, const dflash2_selector_weights* sw, int32_t* out_path,
+                   float* out_scores) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  if (n_req <= 0 || n_req != ctx->last_draft_n)
+    return fail(DFLASH_EINVAL, "n_req must equal that of the most recent dflash_draft_block call");
+  if (k < 1 || k > kSelMaxK) return fail(DFLASH_EUNSUPPORTED, "k must be in 1..16");
+  if (ctx->d.B - 1 > kSelMaxT) return fail(DFLASH_EUNSUPPORTED, "B must be at most 16");
+  if (!anchor || !cand || !cand_logits || !out_path) return fail(DFLASH_EINVAL, "NULL argument");
+  if (!sw || !sw->a || !sw->b || !sw->w_h) return fail(DFLASH_EINVAL, "selector tables must not be NULL");
+  if (sw->rank < 64 || sw->rank > 256 || sw->rank % 64) return fail(DFLASH_EUNSUPPORTED, "rank must be 64, 128, 192 or 256");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (ctx->d.dtype == DFLASH_BF16) run_select<bf16_t>(ctx, st, n_req, anchor, cand, cand_logits, k, sw, out_path, out_scores);
+  else run_select<float>(ctx, st, n_req, anchor, cand, cand_logits, k, sw, out_path, out_scores);
+  int rc = DFLASH_OK;
+  if (!hip_ok(hipGetLastError(), "select launch", &rc)) return rc;
   return DFLASH_OK;
 }
 

@@ -339,6 +339,21 @@ struct EpiRelayOut {
   }
 };
 
+// DFlash 2 selector gate: g = sigmoid(v), fp32.
+struct EpiSigmoidOut {
+  static constexpr bool kPaired = false;
+  static constexpr bool kRow = false;
+  float* g;
+  int ld;
+  __device__ __forceinline__ void apply1(int m, bool valid, int f, f32x4_t v) const {
+    if (!valid) return;
+    f32x4_t o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = 1.0f / (1.0f + __expf(-v[i]));
+    *reinterpret_cast<f32x4_t*>(g + (size_t)m * ld + f) = o;
+  }
+};
+
 // ---------------------------------------------------------------- helpers for the GEMM kernels
 
 template <typename T>

@@ -92,6 +92,55 @@ __global__ __launch_bounds__(256) void relay_assemble_kernel(const T* hc, const 
   }
 }
 
+// DFlash 2 path selector, one work-group per request: every pair table
+// S_t(a, b) = U_t(b) + <A(a) * g_t, B(b)> of the block is built in LDS
+// (position t = 0 pairs the anchor with its candidates), then one lane walks
+// the greedy best successors (ties to the lower rank).
+constexpr int kSelMaxT = 15, kSelMaxK = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void select_kernel(const int* anchor, const int* cand, const float* ul, int k,
+                                                     int Tn, const T* ta, const T* tb, int R, const float* gates,
+                                                     int V, int* out_path, float* out_scores) {
+  constexpr int EPV = 16 / (int)sizeof(T);  // table elements per 16-byte load
+  __shared__ float tab[kSelMaxT * kSelMaxK * kSelMaxK];
+  const int r = blockIdx.x;
+  const int kk = k * k, ntab = Tn * kk;
+  for (int e = threadIdx.x; e < ntab; e += blockDim.x) {
+    const int t = e / kk, rem = e - t * kk, i = rem / k, j = rem - i * k;
+    int a = t == 0 ? anchor[r] : cand[((size_t)r * Tn + t - 1) * k + i];
+    int b = cand[((size_t)r * Tn + t) * k + j];
+    a = a < 0 ? 0 : (a >= V ? V - 1 : a);
+    b = b < 0 ? 0 : (b >= V ? V - 1 : b);
+    const float* g = gates + ((size_t)r * Tn + t) * R;
+    const T* pa = ta + (size_t)a * R;
+    const T* pb = tb + (size_t)b * R;
+    float s = 0.f;
+    for (int c = 0; c < R; c += EPV) {
+      const uint4 va = ld16(pa + c), vb = ld16(pb + c);
+      const T* ea = reinterpret_cast<const T*>(&va);
+      const T* eb = reinterpret_cast<const T*>(&vb);
+#pragma unroll
+      for (int x = 0; x < EPV; ++x) s += to_f<T>(ea[x]) * g[c + x] * to_f<T>(eb[x]);
+    }
+    tab[e] = ul[((size_t)r * Tn + t) * k + j] + s;
+  }
+  __syncthreads();
+  if (out_scores)
+    for (int e = threadIdx.x; e < ntab; e += blockDim.x) out_scores[(size_t)r * ntab + e] = tab[e];
+  if (threadIdx.x == 0) {
+    int prev = 0;
+    for (int t = 0; t < Tn; ++t) {
+      const float* row = tab + t * kk + (t == 0 ? 0 : prev) * k;
+      int best = 0;
+      for (int j = 1; j < k; ++j)
+        if (row[j] > row[best]) best = j;
+      out_path[(size_t)r * Tn + t] = cand[((size_t)r * Tn + t) * k + best];
+      prev = best;
+    }
+  }
+}
+
 // RoPE table: tab[pos][i] = (cos, sin)(pos * base^(-2i/hd)), computed in
 // double and rounded to float.
 __global__ void rope_table_kernel(float2* tab, int npos, int half, double base, int hd) {

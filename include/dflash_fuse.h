@@ -234,6 +234,39 @@ int dflow_relay(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slo
  * For inspection and tests. */
 int dflow_read_relay(dflash_ctx* ctx, void* stream, int32_t slot, float* out, int32_t* count);
 
+/* DFlash 2 path-selector tables (storage dtype, row-major).
+ *   a   [V, rank]  compact embedding of the previous token
+ *   b   [V, rank]  compact embedding of the next token
+ *   w_h [rank, D]  gate projection: H(h) = sigmoid(w_h h)
+ *   rank           a multiple of 64, at most 256 */
+typedef struct dflash2_selector_weights {
+  const void* a;
+  const void* b;
+  const void* w_h;
+  int32_t rank;
+} dflash2_selector_weights;
+
+/* DFlash 2 path selector ("DFlash 2：正确 token 已在候选里", the first-insight
+ * section).  For request r and drafted position t (block offset t, 1..B-1)
+ * with candidates c_t[0..k-1] and their drafter logits U_t, every adjacent
+ * pair is scored
+ *   S_t(a, b) = U_t(b) + < a_tab[a] * H(h_t), b_tab[b] >,  H(h) = sigmoid(w_h h)
+ * where h_t is the final normed hidden state of position t and a runs over
+ * c_{t-1} (over the anchor alone for t = 1); then the greedy walk takes
+ * y_1 = argmax_b S_1(anchor, b), y_t = argmax_b S_t(y_{t-1}, b) (ties to the
+ * lower rank).  h_t comes from the most recent dflash_draft_block call on this
+ * ctx, which must have had the same n_req (same request order); later
+ * dflash_fuse_ctx / dflow_relay calls do not disturb it.
+ *   anchor [n_req] int32 (device)
+ *   cand [n_req, B-1, k] int32 (device), k in 1..16, rank order per position
+ *   cand_logits [n_req, B-1, k] float (device): U_t of those candidates
+ *   out_path [n_req, B-1] int32 (device): the chosen token per position
+ *   out_scores nullable [n_req, B-1, k, k] float (device): S_t(c_{t-1}[i], c_t[j])
+ *              at [t-1][i][j]; for t = 1 every row i holds S_1(anchor, c_1[j]). */
+int dflash2_select(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* anchor, const int32_t* cand,
+                   const float* cand_logits, int32_t k, const dflash2_selector_weights* sw, int32_t* out_path,
+                   float* out_scores);
+
 /* Kernel kinds, for per-kernel timing. */
 enum dflash_kernel_kind {
   DFLASH_K_FUSE_GEMM = 0,   /* context fusion GEMM W_c [H^(l1);...] */
@@ -250,6 +283,7 @@ enum dflash_kernel_kind {
   DFLASH_K_LM_HEAD,         /* LM head with fused top-k */
   DFLASH_K_TOPK_MERGE,      /* top-k merge */
   DFLASH_K_RELAY,           /* DFlow relay: assembly and the relay MLP GEMMs */
+  DFLASH_K_SELECT,          /* DFlash 2 selector: gate GEMM, pair scores and walk */
   DFLASH_K_ACCEPT,          /* acceptance scan (stateless call: never timed) */
   DFLASH_K_COUNT
 };

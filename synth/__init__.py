@@ -14,6 +14,7 @@ from .gen import (  # noqa: F401
     make_anchors,
     make_hidden,
     make_relay_weights,
+    make_selector_weights,
     make_suffix_hidden,
     make_targets,
     make_weights,

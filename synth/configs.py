@@ -105,7 +105,12 @@ def get_config(name: str) -> Workload:
         return Workload(_tiny(B=16, L=5), bs=8, ctx=[64] * 8, n_new=[64] * 8, seed=5,
                         note="DFlow relay on the tiny fp32 drafter, L 5, B 16, bs 8, 64 rounds",
                         rounds=64)
+    if name == "dflash2_select":
+        # Tiny drafter with B = 16, 16 requests prefilled with 64 context tokens;
+        # top-16 candidates per position feed the path selector.
+        return Workload(_tiny(B=16), bs=16, ctx=[64] * 16, n_new=[64] * 16, seed=6,
+                        note="DFlash 2 path selector on the tiny fp32 drafter, B 16, bs 16")
     raise KeyError(name)
 
 
-CONFIGS = ("tiny", "qwen3_4b_bs1", "qwen3_8b_bs1", "qwen3_8b_bs32", "dflow_relay")
+CONFIGS = ("tiny", "qwen3_4b_bs1", "qwen3_8b_bs1", "qwen3_8b_bs32", "dflow_relay", "dflash2_select")

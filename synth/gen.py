@@ -137,6 +137,17 @@ def make_relay_weights(d: Dims, seed: int) -> dict:
             "w2": _fill((2 * d.D, d.D), [s, 10001], 0.02, 0.0, d.dtype)}
 
 
+def make_selector_weights(d: Dims, seed: int, rank: int = 256) -> dict:
+    """Path-selector tables in storage dtype: a, b [V, rank] ~ N(0, 0.2) (so the
+    pairwise term is on the scale of the logit gaps and the walk does not reduce
+    to the per-position argmax), w_h [rank, D] ~ N(0, 1/sqrt(D)) (gate
+    pre-activations of unit scale).  Tensor indices start at 20000."""
+    s = 1000 + seed
+    return {"a": _fill((d.V, rank), [s, 20000], 0.2, 0.0, d.dtype),
+            "b": _fill((d.V, rank), [s, 20001], 0.2, 0.0, d.dtype),
+            "w_h": _fill((rank, d.D), [s, 20002], float(1.0 / np.sqrt(d.D)), 0.0, d.dtype)}
+
+
 def weights_as_f32(w: dict) -> dict:
     """Exact float32 view of the stored weights (bf16 bits are upcast)."""
     def cv(a):

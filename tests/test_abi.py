@@ -18,7 +18,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(dfa.LIB_PATH), reason="librar
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b((?:dflash|dflow)_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b((?:dflash2?|dflow)_[a-z_]+)\s*\(", src)))
 
 
 def test_header_declares_the_abi():

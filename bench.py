@@ -311,6 +311,107 @@ def measure(wl, w_dev, torch, steps, warmup, label):
     return out
 
 
+def measure_relay(wl, w_dev, torch, steps, warmup):
+    """dflow_relay on the workload's shape: every request relays the reusable
+    rejected suffix of a round that accepted tau_prev - 1 candidates (rows
+    max(0, B-2-n)); inputs resident in HBM.  Timed per call with events, and
+    per kernel kind with the library's event timing."""
+    import block_diffusion_drafter_fuse_amd as dfa
+    import synth
+    d, bs, B = wl.dims, wl.bs, wl.dims.B
+    n_acc = [int(t) - 1 for t in wl.n_new]
+    k = [max(0, B - 2 - n) for n in n_acc]
+    rows = sum(k)
+    rw = {n: dfa.to_device(v) for n, v in synth.make_relay_weights(d, wl.seed).items()}
+    dr = dfa.Drafter(d, w_dev, 64, bs, bs)
+    parts = [synth.make_suffix_hidden(d, wl.seed, r, 0, k[r]) for r in range(bs)]
+    hid = [dfa.to_device(np.ascontiguousarray(np.concatenate([p[l] for p in parts], 0))) for l in range(d.L)]
+    rng = np.random.default_rng(wl.seed)
+    cand = torch.tensor(rng.integers(0, d.V, size=(bs, B - 1)).astype(np.int32), device="cuda")
+    bonus = torch.tensor(rng.integers(0, d.V, size=bs).astype(np.int32), device="cuda")
+    slots = list(range(bs))
+
+    def call():
+        dr.relay(slots, n_acc, cand, 1, bonus, hid, rw["w1"], rw["w2"])
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    dr.profile_enable(["fuse_gemm", "relay"], 16 * (steps + 1))
+    for _ in range(steps):
+        call()
+    prof = dr.profile_read()
+    dr.profile_enable([], 0)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    e = elt(d)
+    byts = e * (d.D * d.L * d.Dt + 3 * d.D * d.D + 2 * d.D * d.D) + rows * (d.L * d.Dt * e + 2 * d.D * e + d.D * 4)
+    flops = 2.0 * rows * (d.D * d.L * d.Dt + 3 * d.D * d.D + 2 * d.D * d.D)
+    bd = {kk: round(v[0] / steps, 4) for kk, v in prof.items()}
+    dr.close()
+    del dr
+    torch.cuda.synchronize()
+    return {"workload": f"{wl.dims.name} relay, bs {bs}, {rows} suffix rows", "ms_per_call": round(ms, 4),
+            "rows": rows, "algorithmic_bytes": byts, "algorithmic_flops": flops,
+            "hbm_roof_frac": round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "mfma_roof_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+            "breakdown_ms": bd,
+            "note": "fuse_gemm = suffix projection through the shared W_c; relay = assembly + MLP GEMMs"}
+
+
+def measure_select(wl, w_dev, torch, steps, warmup):
+    """dflash2_select on the workload's batch: the gates come from one draft of
+    the batch (context-free, so only the block feeds it); the top-16 candidate
+    lists and logits are seeded synthetic inputs.  Timed per call with events."""
+    import block_diffusion_drafter_fuse_amd as dfa
+    import synth
+    d, bs, B, K = wl.dims, wl.bs, wl.dims.B, 16
+    tabs = {n: dfa.to_device(v) for n, v in synth.make_selector_weights(d, wl.seed).items()}
+    dr = dfa.Drafter(d, w_dev, 64, bs, bs)
+    slots = list(range(bs))
+    anchor = torch.tensor(synth.make_anchors(d, wl.seed, bs), device="cuda")
+    ids = torch.zeros((bs, B - 1, 1), dtype=torch.int32, device="cuda")
+    dr.draft_block(slots, anchor, 1, ids)
+    rng = np.random.default_rng(wl.seed)
+    cand = torch.tensor(rng.integers(0, d.V, size=(bs, B - 1, K)).astype(np.int32), device="cuda")
+    ul = torch.tensor(np.sort(rng.standard_normal((bs, B - 1, K)).astype(np.float32), -1)[..., ::-1].copy(),
+                      device="cuda")
+    path = torch.zeros((bs, B - 1), dtype=torch.int32, device="cuda")
+
+    def call():
+        dr.select(bs, anchor, cand, ul, K, tabs, path)
+
+    for _ in range(warmup):
+        call()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    e = elt(d)
+    R = 256
+    rows = bs * (B - 1)
+    byts = e * (R * d.D) + rows * d.D * e + rows * K * 8 + rows * (K + 1) * 2 * R * e
+    dr.close()
+    del dr
+    torch.cuda.synchronize()
+    return {"workload": f"{wl.dims.name} selector, bs {bs}, top-{K}, rank {R}", "ms_per_call": round(ms, 4),
+            "algorithmic_bytes": byts, "hbm_roof_frac": round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+            "note": "gate GEMM over the draft's final hidden rows + pair tables + greedy walk; "
+                    "the draft's top-16 LM head is not included"}
+
+
 def cpu_baseline(wl, w_np, budget_s=20.0):
     """The float64 oracle, as it stands, on one request of the workload (the
     one with the shortest context): fuse its new rows, draft its block, accept.
@@ -356,6 +457,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_bs32")
     ap.add_argument("--companion", default="qwen3_8b_bs1", help="second workload reported under 'bs1' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-relay", action="store_true",
+                    help="skip the DFlow relay and DFlash 2 selector measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy one buffer of this many MiB (reference dispatch for byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -408,6 +511,12 @@ def main():
         assert wc.dims == wl.dims, "companion must share the model shape"
         print(f"[bench] measuring {args.companion}", file=sys.stderr, flush=True)
         comp = measure(wc, w_dev, torch, args.steps, args.warmup, args.companion)
+    relay = select = None
+    if not args.no_relay:
+        print(f"[bench] measuring the DFlow relay at {args.workload}", file=sys.stderr, flush=True)
+        relay = measure_relay(wl, w_dev, torch, args.steps, args.warmup)
+        print(f"[bench] measuring the DFlash 2 selector at {args.workload}", file=sys.stderr, flush=True)
+        select = measure_select(wl, w_dev, torch, args.steps, args.warmup)
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
@@ -446,6 +555,10 @@ def main():
     if comp:
         line["bs1"] = {k: comp[k] for k in ("workload", "drafted_tokens_per_s", "blocks_per_s", "ms_per_step",
                                             "step_hbm_roof_frac", "roofline", "breakdown_ms")}
+    if relay:
+        line["relay"] = relay
+    if select:
+        line["select"] = select
     print(json.dumps(line), flush=True)
 
 

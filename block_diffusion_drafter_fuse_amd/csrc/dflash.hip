@@ -49,10 +49,12 @@ constexpr int kAttnWorkMax = 4096;     // attention split work items per call
 constexpr int kAttnTargetWG = 2048;    // attention work-groups aimed for
 constexpr int kAttnMinChunk = 128;     // minimum context keys per split
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
+constexpr int kNarrowMaxGroups = 64;   // weights of at most 1024 rows also take the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
 constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (LDS: TB x waves x 1 KB)
 constexpr bool kGemvPF = false;        // prefetch the next tile's weights before the current MFMAs
 constexpr int kGemvWGs = 256;          // skinny GEMM work-groups per 16-token block
+constexpr int kGemvXcds = 8;           // XCDs; work-group i runs on XCD i mod 8
 constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, unroll
 constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
 constexpr size_t kPartFloats = size_t(16) << 20;  // split-K partials (64 MB)
@@ -96,8 +98,13 @@ int lm_chunks_small(int rowblocks) { return std::max(1, 256 / rowblocks); }
 
 // Top-1 LM head through the GEMM engines: one partial per 16-row tile (GEMV,
 // few rows) or per wave fragment row of the wide tiled GEMM (many rows).
+// Which GEMM engine serves M rows against a weight of ngroups 16-row groups:
+// few rows, or a narrow weight (it stays in L2 across the 16-row blocks),
+// take the activation-stationary GEMV; the rest the tiled GEMM.
+bool uses_gemv(int M, int ngroups) { return M <= kSkinnyMaxM || ngroups <= kNarrowMaxGroups; }
+
 int lm_top1_chunks(int Mlm, int V) {
-  return Mlm <= kSkinnyMaxM ? ceil_div(V, 16) : ceil_div(V, TileWide::kFeatPerWave);
+  return uses_gemv(Mlm, ceil_div(V, 16)) ? ceil_div(V, 16) : ceil_div(V, TileWide::kFeatPerWave);
 }
 
 // LM-head partial-list entries a call needs (KTOP = 16 for top_k > 1).
@@ -180,7 +187,8 @@ void make_plan(const dflash_dims* d, Plan* p) {
   p->rin_off = off;  off = align_up(off + (size_t)p->relay_rows * 3 * d->D * e);
   p->rlnh_off = off; off = align_up(off + (size_t)p->relay_rows * d->D * 4);
   p->rs_off = off;   off = align_up(off + (size_t)p->relay_rows * d->D * e);
-  p->sel_off = off;  off = align_up(off + (size_t)Mlm * 256 * 4);  // selector gates [rows][rank <= 256]
+  // selector gates [rows][rank <= 256], then pair tables [rows][16][16]
+  p->sel_off = off;  off = align_up(off + (size_t)Mlm * 256 * 4 * 2);
   p->ws_bytes = off;
 }
 
@@ -271,7 +279,7 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
   if (a.M <= 0 || w.ngroups <= 0) return;
   const int K = a.nk * a.kseg;
   {
-    if (a.M <= kSkinnyMaxM) {
+    if (uses_gemv(a.M, w.ngroups)) {
       // Activation-stationary GEMV: 16-row tiles, K split across the waves of
       // a work-group (LDS reduction; a cross-work-group split would need
       // device-scope fences, which write back and invalidate the XCD's L2).
@@ -284,14 +292,22 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
       if (Epi::kPaired) tpw += tpw & 1;
       const int nwg = ceil_div(w.ngroups, tpw);
       const int lds = kGemvTB * nw * 64 * 16;
-      auto kern = gemv_as_kernel<T, KSW, ALO, kGemvTB, kGemvPF, Epi>;
-      static bool attr_set = false;
-      if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kGemvTB * 16 * 64 * 16);
-        attr_set = true;
-      }
-      hipLaunchKernelGGL(kern, dim3(nwg, mt), dim3(64 * nw), lds, st, w, a, nrm, epi, tpw);
+      // row blocks kept on one XCD each once there are enough to go round
+      const bool xr = mt >= kGemvXcds;
+      auto launch = [&](auto kern, dim3 grid) {
+        static bool attr_set = false;
+        if (!attr_set) {
+          (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kGemvTB * 16 * 64 * 16);
+          attr_set = true;
+        }
+        hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, st, w, a, nrm, epi, tpw);
+      };
+      if (xr)
+        launch(gemv_as_kernel<T, KSW, ALO, kGemvTB, kGemvPF, true, Epi>,
+               dim3(kGemvXcds * nwg * ceil_div(mt, kGemvXcds)));
+      else
+        launch(gemv_as_kernel<T, KSW, ALO, kGemvTB, kGemvPF, false, Epi>, dim3(nwg, mt));
       return;
     }
   }
@@ -684,9 +700,11 @@ void run_select(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* anchor,
   // H(h_t) = sigmoid(w_h h_t) over the LM head's operand (the final normed hidden states)
   launch_gemm<T>(c, wop<T>({{sw->w_h, sw->rank}}, 0), aop<T>(c->wsp<T>(p.u_off), Mlm, d.D, d.B),
                  norm_in(c->wsp<float>(p.ssq_off), d.D, d.rms_eps), EpiSigmoidOut{gates, sw->rank}, st);
-  hipLaunchKernelGGL((select_kernel<T>), dim3(n_req), dim3(256), 0, st, anchor, cand, ul, k, d.B - 1,
-                     static_cast<const T*>(sw->a), static_cast<const T*>(sw->b), sw->rank, gates, d.V, out_path,
-                     out_scores);
+  float* tables = out_scores ? out_scores : gates + (size_t)Mlm * kSelMaxR;
+  hipLaunchKernelGGL((select_tables_kernel<T>), dim3(n_req, d.B - 1), dim3(256), 0, st, anchor, cand, ul, k,
+                     d.B - 1, static_cast<const T*>(sw->a), static_cast<const T*>(sw->b), sw->rank, gates, d.V,
+                     tables);
+  hipLaunchKernelGGL(select_walk_kernel, dim3(n_req), dim3(256), 0, st, cand, tables, k, d.B - 1, out_path);
 }
 
 extern "C" {

@@ -397,8 +397,16 @@ __device__ __forceinline__ void run_epilogue(const Epi& epi, int m, bool mvalid,
 // run spread over the waves (a paired epilogue takes two consecutive tiles).
 // When K spans several chunks the activations are reloaded per chunk (such
 // GEMMs have one or two tiles per work-group).
+//
+// Work-group placement: with XR false the grid is (tile range, 16-row block)
+// and weights stream past L2 (every row block of a tile range reads them
+// once).  With XR true (many row blocks against a narrow weight) the grid is
+// one-dimensional and the work-groups of a row block all run on one XCD
+// (work-group i runs on XCD i mod 8), so each activation block is fetched
+// into one L2 only; the weight, which every XCD then reads, is loaded with
+// ordinary caching.
 
-template <typename T, int KSW, bool ALO, int TB, bool PF, class Epi>
+template <typename T, int KSW, bool ALO, int TB, bool PF, bool XR, class Epi>
 __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, const AOperand<T> a,
                                                         const NormIn nrm, const Epi epi, int tiles_per_wg) {
   using MM = Mma<T>;
@@ -409,10 +417,18 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
   const int NW = blockDim.x >> 6;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int t_begin = blockIdx.x * tiles_per_wg;
+  int tg = blockIdx.x, mb = blockIdx.y;
+  if constexpr (XR) {
+    const int nwg = (w.ngroups + tiles_per_wg - 1) / tiles_per_wg;
+    const int j = blockIdx.x >> 3, q = j / nwg;
+    tg = j - q * nwg;
+    mb = q * 8 + (blockIdx.x & 7);
+    if (mb * 16 >= a.M) return;
+  }
+  const int t_begin = tg * tiles_per_wg;
   const int t_end = min(w.ngroups, t_begin + tiles_per_wg);
   if (t_begin >= t_end) return;
-  const int m0 = blockIdx.y * 16;
+  const int m0 = mb * 16;
   const int K = a.nk * a.kseg;
   const int nks = K / KS;
   const int span = NW * KSW;
@@ -440,7 +456,10 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
 #pragma unroll
     for (int j = 0; j < KSW; ++j) {
       const int ks = c * span + wave * KSW + j;
-      wf[j] = ks < nks ? ld16_stream(wp + (size_t)ks * KS) : make_uint4(0, 0, 0, 0);
+      if constexpr (XR)
+        wf[j] = ks < nks ? ld16(wp + (size_t)ks * KS) : make_uint4(0, 0, 0, 0);
+      else
+        wf[j] = ks < nks ? ld16_stream(wp + (size_t)ks * KS) : make_uint4(0, 0, 0, 0);
     }
   };
 

@@ -92,53 +92,79 @@ __global__ __launch_bounds__(256) void relay_assemble_kernel(const T* hc, const 
   }
 }
 
-// DFlash 2 path selector, one work-group per request: every pair table
-// S_t(a, b) = U_t(b) + <A(a) * g_t, B(b)> of the block is built in LDS
-// (position t = 0 pairs the anchor with its candidates), then one lane walks
-// the greedy best successors (ties to the lower rank).
-constexpr int kSelMaxT = 15, kSelMaxK = 16;
+// DFlash 2 path selector.  select_tables_kernel: one work-group per (request,
+// drafted position t) stages the k previous-token rows of A (the anchor's row
+// alone for t = 0), the k candidate rows of B and the gate g_t in LDS, then
+// thread (i, j) forms S_t(a_i, b_j) = U_t(b_j) + <A(a_i) * g_t, B(b_j)>.
+// select_walk_kernel: one wave per request walks the greedy best successors
+// (ties to the lower rank).
+constexpr int kSelMaxT = 15, kSelMaxK = 16, kSelMaxR = 256;
 
 template <typename T>
-__global__ __launch_bounds__(256) void select_kernel(const int* anchor, const int* cand, const float* ul, int k,
-                                                     int Tn, const T* ta, const T* tb, int R, const float* gates,
-                                                     int V, int* out_path, float* out_scores) {
+__global__ __launch_bounds__(256) void select_tables_kernel(const int* anchor, const int* cand, const float* ul,
+                                                            int k, int Tn, const T* ta, const T* tb, int R,
+                                                            const float* gates, int V, float* tables) {
+  __shared__ float sa[kSelMaxK][kSelMaxR + 1];
+  __shared__ float sb[kSelMaxK][kSelMaxR + 1];
+  __shared__ float sg[kSelMaxR];
+  const int r = blockIdx.x, t = blockIdx.y;
+  const int na = t == 0 ? 1 : k;
+  const float* g = gates + ((size_t)r * Tn + t) * R;
+  for (int c = threadIdx.x; c < R; c += blockDim.x) sg[c] = g[c];
   constexpr int EPV = 16 / (int)sizeof(T);  // table elements per 16-byte load
-  __shared__ float tab[kSelMaxT * kSelMaxK * kSelMaxK];
-  const int r = blockIdx.x;
-  const int kk = k * k, ntab = Tn * kk;
-  for (int e = threadIdx.x; e < ntab; e += blockDim.x) {
-    const int t = e / kk, rem = e - t * kk, i = rem / k, j = rem - i * k;
-    int a = t == 0 ? anchor[r] : cand[((size_t)r * Tn + t - 1) * k + i];
-    int b = cand[((size_t)r * Tn + t) * k + j];
-    a = a < 0 ? 0 : (a >= V ? V - 1 : a);
-    b = b < 0 ? 0 : (b >= V ? V - 1 : b);
-    const float* g = gates + ((size_t)r * Tn + t) * R;
-    const T* pa = ta + (size_t)a * R;
-    const T* pb = tb + (size_t)b * R;
-    float s = 0.f;
-    for (int c = 0; c < R; c += EPV) {
-      const uint4 va = ld16(pa + c), vb = ld16(pb + c);
-      const T* ea = reinterpret_cast<const T*>(&va);
-      const T* eb = reinterpret_cast<const T*>(&vb);
+  const int cpr = R / EPV;                   // 16-byte chunks per row
+  for (int e = threadIdx.x; e < (na + k) * cpr; e += blockDim.x) {
+    const int row = e / cpr, c = (e - row * cpr) * EPV;
+    int id;
+    if (row < na) id = t == 0 ? anchor[r] : cand[((size_t)r * Tn + t - 1) * k + row];
+    else id = cand[((size_t)r * Tn + t) * k + row - na];
+    id = id < 0 ? 0 : (id >= V ? V - 1 : id);
+    const uint4 v = ld16((row < na ? ta : tb) + (size_t)id * R + c);
+    const T* ev = reinterpret_cast<const T*>(&v);
+    float* dst = row < na ? &sa[row][c] : &sb[row - na][c];
 #pragma unroll
-      for (int x = 0; x < EPV; ++x) s += to_f<T>(ea[x]) * g[c + x] * to_f<T>(eb[x]);
-    }
-    tab[e] = ul[((size_t)r * Tn + t) * k + j] + s;
+    for (int x = 0; x < EPV; ++x) dst[x] = to_f<T>(ev[x]);
   }
   __syncthreads();
-  if (out_scores)
-    for (int e = threadIdx.x; e < ntab; e += blockDim.x) out_scores[(size_t)r * ntab + e] = tab[e];
-  if (threadIdx.x == 0) {
-    int prev = 0;
-    for (int t = 0; t < Tn; ++t) {
-      const float* row = tab + t * kk + (t == 0 ? 0 : prev) * k;
-      int best = 0;
-      for (int j = 1; j < k; ++j)
-        if (row[j] > row[best]) best = j;
-      out_path[(size_t)r * Tn + t] = cand[((size_t)r * Tn + t) * k + best];
-      prev = best;
+  const int i = threadIdx.x / k, j = threadIdx.x - i * k;
+  if (i >= k) return;
+  const int ia = t == 0 ? 0 : i;
+  float s = 0.f;
+  for (int c = 0; c < R; ++c) s += sa[ia][c] * sg[c] * sb[j][c];
+  tables[(((size_t)r * Tn + t) * k + i) * k + j] = ul[((size_t)r * Tn + t) * k + j] + s;
+}
+
+__global__ __launch_bounds__(256) void select_walk_kernel(const int* cand, const float* tables, int k, int Tn,
+                                                          int* out_path) {
+  __shared__ float tab[kSelMaxT * kSelMaxK * kSelMaxK];
+  const int r = blockIdx.x;
+  const int n = Tn * k * k;
+  for (int e = threadIdx.x; e < n; e += blockDim.x) tab[e] = tables[(size_t)r * n + e];
+  __syncthreads();
+  if (threadIdx.x >= 64) return;
+  // one wave: lane j < k holds candidate j of the row; argmax over 16 lanes
+  // with ties to the lower rank; lane t keeps the rank chosen at position t,
+  // and the candidate ids are gathered after the walk (no global access
+  // inside the dependent chain)
+  const int lane = threadIdx.x;
+  int prev = 0, mine = 0;
+  for (int t = 0; t < Tn; ++t) {
+    const float* row = tab + (t * k + (t == 0 ? 0 : prev)) * k;
+    float v = lane < k ? row[lane] : -INFINITY;
+    int bi = lane < k ? lane : kSelMaxK;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const float v2 = __shfl_xor(v, o);
+      const int i2 = __shfl_xor(bi, o);
+      if (v2 > v || (v2 == v && i2 < bi)) {
+        v = v2;
+        bi = i2;
+      }
     }
+    prev = __shfl(bi, 0);
+    if (lane == t) mine = prev;
   }
+  if (lane < Tn) out_path[(size_t)r * Tn + lane] = cand[((size_t)r * Tn + lane) * k + mine];
 }
 
 // RoPE table: tab[pos][i] = (cos, sin)(pos * base^(-2i/hd)), computed in

@@ -36,6 +36,9 @@ struct WOperand {
     const int per = pair >> 4;
     return (pi / per) * 2 * pair + (pi % per) * 16 + half * pair;
   }
+  // Row f of the virtual weight.  Segments hold whole 16-row groups, so a
+  // caller passes the first row of a group (wave-uniform: the segment search
+  // then runs on scalar kernel-argument loads) and adds the row in the group.
   __device__ __forceinline__ const T* row(int f, int K) const {
     int s = 0;
     while (s + 1 < nseg && f >= end[s]) ++s;
@@ -76,6 +79,15 @@ __device__ __forceinline__ float norm_scale(const NormIn& n, int arow, int kg) {
   const float* p = n.ssq + (size_t)arow * n.nslot + kg * q;
   float s = 0.f;
   int j = 0;
+  // eight independent 16-byte loads in flight per batch (a one-load-at-a-time
+  // loop costs a memory latency per 4 slots)
+  for (; j + 32 <= q; j += 32) {
+    f32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4_t*>(p + j + 4 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += (v[u][0] + v[u][1]) + (v[u][2] + v[u][3]);
+  }
   for (; j + 4 <= q; j += 4) {
     const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + j);
     s += (v[0] + v[1]) + (v[2] + v[3]);
@@ -415,7 +427,9 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
   extern __shared__ __align__(16) char lds_raw[];
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds_raw);  // [TB][NW][64]
   const int NW = blockDim.x >> 6;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index as a scalar: the K segment of an activation fragment is then
+  // picked with scalar loads instead of a per-lane load of the argument block
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   int tg = blockIdx.x, mb = blockIdx.y;
   if constexpr (XR) {
@@ -451,7 +465,7 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
       }
     }
   };
-  auto wrow = [&](int t) { return w.row(w.feature_of_group(t) + r16, K) + kg * EPL; };
+  auto wrow = [&](int t) { return w.row(w.feature_of_group(t), K) + (size_t)r16 * K + kg * EPL; };
   auto load_w = [&](const T* wp, int c, uint4 (&wf)[KSW]) {
 #pragma unroll
     for (int j = 0; j < KSW; ++j) {
@@ -464,7 +478,22 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
   };
 
   if (nchunks == 1) load_a(0);
-  const float sc = norm_scale(nrm, arow, kg);
+  // Row norm: with nslot a multiple of 16 x NW (up to two 16-byte loads per
+  // lane) the waves split the slots, each lane loads its share now and the
+  // sums meet in LDS at the first barrier, so the scale costs no latency of
+  // its own; otherwise every wave reduces the whole row up front.
+  __shared__ float nsum[16 * 64];
+  const int c4 = nrm.ssq ? nrm.nslot / (16 * NW) : 0;
+  const bool nsplit = c4 >= 1 && c4 <= 2 && c4 * 16 * NW == nrm.nslot;
+  f32x4_t nv0 = {0.f, 0.f, 0.f, 0.f}, nv1 = {0.f, 0.f, 0.f, 0.f};
+  float sc = 1.0f;
+  if (nsplit) {
+    const float* p = nrm.ssq + (size_t)arow * nrm.nslot + (wave * 4 + kg) * 4 * c4;
+    nv0 = *reinterpret_cast<const f32x4_t*>(p);
+    if (c4 == 2) nv1 = *reinterpret_cast<const f32x4_t*>(p + 4);
+  } else {
+    sc = norm_scale(nrm, arow, kg);
+  }
   for (int b0 = t_begin; b0 < t_end; b0 += TB) {
     const int bt = min(TB, t_end - b0);
     const int items = bt * nchunks;  // (tile, chunk) in order
@@ -506,7 +535,17 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
         }
       }
     }
+    const bool first = b0 == t_begin;
+    if (nsplit && first)
+      nsum[wave * 64 + lane] = ((nv0[0] + nv0[1]) + (nv0[2] + nv0[3])) + ((nv1[0] + nv1[1]) + (nv1[2] + nv1[3]));
     __syncthreads();
+    if (nsplit && first) {
+      float ss = 0.f;
+      for (int w2 = 0; w2 < NW; ++w2) ss += nsum[w2 * 64 + lane];
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      sc = 1.0f / sqrtf(ss * nrm.inv_d + nrm.eps);
+    }
     // reduce + epilogue: unit j (a tile, or a pair of tiles) handled by wave j % NW
     constexpr int PT = Epi::kPaired ? 2 : 1;
     for (int j = wave; j * PT < bt; j += NW) {

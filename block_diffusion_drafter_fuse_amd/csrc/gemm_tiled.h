@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
   t /= sk.SK;
   const int bm = t % MT, bn = t / MT;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, kg = lane >> 4;
   const int wm = wave / WN, wn = wave % WN;
   const int K = a.nk * a.kseg;
@@ -106,10 +106,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
       m = m < a.M ? m : a.M - 1;
       src[i] = reinterpret_cast<const char*>(a.ptr[0] + (size_t)a.row(m) * a.lda + plane * a.lo_off) + cchunk * 16;
     } else {
+      // the 16-row group of these 8 rows is wave-uniform (AR is a multiple of 16)
       const int wr = row - AR;
-      const int gi = ngroups_tile0 + wr / 16;
-      const int f = gi < w.ngroups ? w.feature_of_group(gi) + (wr & 15) : (wr & 15);
-      src[i] = reinterpret_cast<const char*>(w.row(f, K)) + cchunk * 16;
+      const int gi = ngroups_tile0 + ((NWV * i + wave) * 8 - AR) / 16;
+      const T* g = gi < w.ngroups ? w.row(w.feature_of_group(gi), K) : w.ptr[0];
+      src[i] = reinterpret_cast<const char*>(g + (size_t)(wr & 15) * K) + cchunk * 16;
     }
   }
   // Activation segment base offset for stage st (segments are stage-aligned).
@@ -212,8 +213,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
     if (tid == 0) *ticket = __hip_atomic_fetch_add(sk.ctr + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*ticket != sk.SK - 1) return;
+    // the sum runs over every split in index order (the own partial is read
+    // back too), so the result does not depend on which split arrived last
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int x = 0; x < sk.SK; ++x) {
-      if (x == s) continue;
       const float* px = pt + (size_t)x * (NWV * WTILE);
 #pragma unroll
       for (int i = 0; i < FM; ++i)

@@ -15,7 +15,8 @@ Sources (web pages on the method; cited by page title and section):
     relay steps 1-3 and the inference-loop section (the relay, `oracle/dflow.py`).
   * DFlash system/training/deployment notes (blog.hotdry.top), section 2.
   * "DFlash 2：正确 token 已在候选里，选一条连贯的路就好": the path selector
-    (first insight section; `oracle/dflash2.py`).
+    (first insight section) and the two-tap dynamic convolution (second
+    insight section), both in `oracle/dflash2.py`.
 
 Where the pages leave a step open, the reading taken is stated at the function.
 
@@ -25,7 +26,16 @@ and the worked examples stored under tests/golden/).  Forward values at the
 full model shapes are pinned only through those properties: the pages print no
 output values for any input.
 """
-from .dflash2 import gate as selector_gate, pair_scores, select_path, walk  # noqa: F401
+from .dflash2 import (  # noqa: F401
+    CONV_SITES,
+    conv_param_count,
+    draft_block_conv,
+    gate as selector_gate,
+    pair_scores,
+    select_path,
+    two_tap_conv,
+    walk,
+)
 from .dflow import (  # noqa: F401
     RelayState,
     block_inputs,

@@ -160,7 +160,7 @@ class ContextCache:
 # --------------------------------------------------------------------------
 
 def draft_block(w: dict, d, cache: ContextCache, anchor: int,
-                block_inputs: Optional[np.ndarray] = None) -> dict:
+                block_inputs: Optional[np.ndarray] = None, conv=None) -> dict:
     """One-pass block draft over the cached context.
 
     DFlash page, section 二 (block [anchor, mask x (B-1)]; one forward pass, no
@@ -174,6 +174,11 @@ def draft_block(w: dict, d, cache: ContextCache, anchor: int,
     a final RMSNorm precedes the shared LM head; block offset j sits at
     absolute position ctx + j.
 
+    conv: None, or per layer four callables [B, D] -> [B, D] applied at the
+    DFlash 2 convolution sites (normed attention input, attention output
+    before the residual add, normed FFN input, FFN output before the residual
+    add); see oracle.dflash2.draft_block_conv.
+
     Returns dict with "logits" [B-1, V], "hidden" [B, D] (final residual
     stream) and "x0" [B, D] (block input)."""
     B = d.B
@@ -184,8 +189,10 @@ def draft_block(w: dict, d, cache: ContextCache, anchor: int,
     x0 = x.copy()
     ctx = cache.length
     pos = np.arange(ctx, ctx + B)
+    ident = (lambda v: v,) * 4
     for l, layer in enumerate(w["layers"]):
-        u = rms_norm(x, layer["g_attn"], d.rms_eps)
+        c_attn_in, c_attn_out, c_ffn_in, c_ffn_out = ident if conv is None else conv[l]
+        u = c_attn_in(rms_norm(x, layer["g_attn"], d.rms_eps))
         q = (u @ _f64(layer["w_q"]).T).reshape(B, d.Hq, d.hd).transpose(1, 0, 2)
         kb = (u @ _f64(layer["w_kb"]).T).reshape(B, d.Hkv, d.hd).transpose(1, 0, 2)
         vb = (u @ _f64(layer["w_vb"]).T).reshape(B, d.Hkv, d.hd).transpose(1, 0, 2)
@@ -195,9 +202,9 @@ def draft_block(w: dict, d, cache: ContextCache, anchor: int,
         K = np.concatenate([cache.K[l], kb], axis=1)
         V = np.concatenate([cache.V[l], vb], axis=1)
         o = block_attention(q, K, V, d.G)
-        x = x + o @ _f64(layer["w_o"]).T
-        u = rms_norm(x, layer["g_ffn"], d.rms_eps)
-        x = x + swiglu_ffn(u, layer)
+        x = x + c_attn_out(o @ _f64(layer["w_o"]).T)
+        u = c_ffn_in(rms_norm(x, layer["g_ffn"], d.rms_eps))
+        x = x + c_ffn_out(swiglu_ffn(u, layer))
     h = rms_norm(x[1:], w["g_final"], d.rms_eps)
     logits = h @ _f64(w["w_lm"]).T
     return {"logits": logits, "hidden": x, "x0": x0}

@@ -1,12 +1,13 @@
-"""Float64 NumPy oracle of the DFlash 2 path selector (test infrastructure only).
+"""Float64 NumPy oracle of the DFlash 2 additions (test infrastructure only):
+the path selector and the two-tap dynamic depthwise convolution.
 
-Source: "DFlash 2：正确 token 已在候选里，选一条连贯的路就好" — the section on
-the first insight (selection is cheaper than prediction: keep the top-16
-candidates of every position, score every adjacent candidate pair with a
-low-rank bilinear term, then walk the precomputed scores greedily along the
-best successor), Tables 1-2 (top-16 recall, the selector's cost).
+Source: "DFlash 2：正确 token 已在候选里，选一条连贯的路就好".
 
-Readings (the page leaves them open):
+Path selector — the section on the first insight (selection is cheaper than
+prediction: keep the top-16 candidates of every position, score every
+adjacent candidate pair with a low-rank bilinear term, then walk the
+precomputed scores greedily along the best successor), Tables 1-2 (top-16
+recall, the selector's cost).  Readings (the page leaves them open):
   * U_t(b) is the drafter's raw logit of candidate b at position t.
   * H(h_t) = sigmoid(W_H h_t), W_H [256, D], h_t the final normed hidden state
     of position t (the LM head's input); the page calls H a gate from the
@@ -14,6 +15,22 @@ Readings (the page leaves them open):
   * The first drafted position scores its candidates against the anchor
     (a = the last verified token).
   * Ties go to the lower candidate rank.
+
+Two-tap convolution — the section on the second insight (suffix decay is a
+local problem): Conv_k(x)_t = k_{t,0} * x_t + k_{t,1} * x_{t-1} along the
+block, the taps being a base kernel plus a small correction computed from the
+current hidden state, one correction per 16 channels, the block's first
+position reading the last verified token; inserted before and after the
+attention and FFN sub-layers of every layer (16.5M extra parameters at the
+5-layer drafter).  Readings:
+  * k_{t,j}[c] = kbase_j[c] + (W_j x_t)[c // 16] with W_j [D/16, D], linear,
+    no bias; x_t is the convolution's own input row.
+  * Block offsets are numbered from the anchor: the first drafted position
+    (offset 1) reads the anchor (offset 0), the last verified token; the
+    anchor has no left neighbour in the block and its left tap reads zero.
+  * Four sites per layer: the normed attention input, the attention output
+    (after W_o) before the residual add, the normed FFN input, and the FFN
+    output before the residual add.
 """
 from __future__ import annotations
 
@@ -50,6 +67,43 @@ def walk(first: np.ndarray, tables: List[np.ndarray]) -> List[int]:
     for tab in tables:
         path.append(int(np.argmax(tab[path[-1]])))
     return path
+
+
+CONV_SITES = ("attn_in", "attn_out", "ffn_in", "ffn_out")
+
+
+def two_tap_conv(x: np.ndarray, w: np.ndarray, kbase: np.ndarray) -> np.ndarray:
+    """Two-tap dynamic depthwise convolution along the block.
+
+    x [B, D] rows in block-offset order; w [2 * D/16, D] holds W_0 (first D/16
+    rows) and W_1; kbase [2, D].  Returns y [B, D] with
+    y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1}, x_{-1} = 0."""
+    x = _f64(x)
+    B, D = x.shape
+    G = D // 16
+    z = x @ _f64(w).T
+    k0 = _f64(kbase[0])[None] + np.repeat(z[:, :G], 16, axis=1)
+    k1 = _f64(kbase[1])[None] + np.repeat(z[:, G:], 16, axis=1)
+    left = np.zeros_like(x)
+    left[1:] = x[:-1]
+    return k0 * x + k1 * left
+
+
+def draft_block_conv(w: dict, d, cache, anchor: int, conv, block_inputs=None) -> dict:
+    """The DFlash draft forward with the two-tap convolution at the four sites
+    of every layer.  conv: per layer a dict site -> {"w", "kbase"}."""
+    from .dflash import draft_block
+
+    def hook(site):
+        return lambda v: two_tap_conv(v, site["w"], site["kbase"])
+    hooks = [tuple(hook(layer[s]) for s in CONV_SITES) for layer in conv]
+    return draft_block(w, d, cache, anchor, block_inputs, conv=hooks)
+
+
+def conv_param_count(D: int, layers: int) -> int:
+    """Extra parameters of the convolution: per site two correction matrices
+    [D/16, D] and the two base kernels [D]."""
+    return layers * len(CONV_SITES) * (2 * (D // 16) * D + 2 * D)
 
 
 def select_path(anchor: int, cand: np.ndarray, u: np.ndarray, A: np.ndarray, Bt: np.ndarray,

@@ -9,9 +9,11 @@ from .configs import CONFIGS, Dims, Workload, get_config  # noqa: F401
 from .gen import (  # noqa: F401
     as_f32,
     bf16_bits_to_f32,
+    conv_weights_as_f32,
     f32_to_bf16_bits,
     draw_accepted,
     make_anchors,
+    make_conv_weights,
     make_hidden,
     make_relay_weights,
     make_selector_weights,

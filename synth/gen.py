@@ -148,6 +148,34 @@ def make_selector_weights(d: Dims, seed: int, rank: int = 256) -> dict:
             "w_h": _fill((rank, d.D), [s, 20002], float(1.0 / np.sqrt(d.D)), 0.0, d.dtype)}
 
 
+def make_conv_weights(d: Dims, seed: int) -> list:
+    """Two-tap convolution weights in storage dtype, per layer and site
+    (attn_in, attn_out, ffn_in, ffn_out): w [2 * D/16, D] ~ N(0, 0.1/sqrt(D))
+    (tap corrections of about 0.1 on unit-scale rows), kbase [2, D] with the
+    current tap 1 + N(0, 0.05) and the left tap 0.25 + N(0, 0.05) (a clearly
+    non-zero neighbour mix).  Tensor indices start at 21000."""
+    s = 1000 + seed
+    sites = ("attn_in", "attn_out", "ffn_in", "ffn_out")
+    out = []
+    for l in range(d.N):
+        layer = {}
+        for i, site in enumerate(sites):
+            t = 21000 + 8 * (4 * l + i)
+            k0 = _fill((1, d.D), [s, t + 1], 0.05, 1.0, d.dtype)
+            k1 = _fill((1, d.D), [s, t + 2], 0.05, 0.25, d.dtype)
+            layer[site] = {"w": _fill((2 * (d.D // 16), d.D), [s, t], float(0.1 / np.sqrt(d.D)), 0.0, d.dtype),
+                           "kbase": np.ascontiguousarray(np.concatenate([k0, k1], axis=0))}
+        out.append(layer)
+    return out
+
+
+def conv_weights_as_f32(cw: list) -> list:
+    """Exact float32 view of make_conv_weights' output."""
+    def cv(a):
+        return bf16_bits_to_f32(a) if a.dtype == np.uint16 else a
+    return [{site: {k: cv(v) for k, v in t.items()} for site, t in layer.items()} for layer in cw]
+
+
 def weights_as_f32(w: dict) -> dict:
     """Exact float32 view of the stored weights (bf16 bits are upcast)."""
     def cv(a):

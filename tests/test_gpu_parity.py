@@ -201,7 +201,7 @@ def test_gpu_accept_bitexact():
 
 # ------------------------------------------------------------------ full size
 
-def _full_size_case(wl, sample_reqs, label):
+def _full_size_case(wl, sample_reqs, label, repeat=False):
     d = wl.dims
     log(f"case {label}: generating weights")
     w_np = synth.make_weights(d, wl.seed)
@@ -218,6 +218,11 @@ def _full_size_case(wl, sample_reqs, label):
     g.fuse(slots, wl.n_new, hidden_rows(d, wl.seed, [(r, pre[r], wl.n_new[r]) for r in range(bs)]))
     anchors = synth.make_anchors(d, wl.seed, bs)
     ids, vals, lg = g.draft(slots, anchors, top_k=1, logits=True)
+    if repeat:
+        # split-K partial sums and attention splits are combined in a fixed
+        # order: a second draft of the same block is bitwise identical
+        ids2, vals2, lg2 = g.draft(slots, anchors, top_k=1, logits=True)
+        assert np.array_equal(ids, ids2) and np.array_equal(lg, lg2), f"{label}: repeated draft differs"
     log(f"case {label}: oracle on requests {sample_reqs}")
     o = oracle.OracleDrafter(synth.weights_as_f32(w_np), d)
     worst = 0.0
@@ -250,4 +255,4 @@ def test_gpu_qwen3_8b_bs1():
 def test_gpu_qwen3_8b_bs32_sampled():
     wl = synth.get_config("qwen3_8b_bs32")
     order = np.argsort(wl.ctx)
-    _full_size_case(wl, [int(order[0]), int(order[len(order) // 2])], "qwen3_8b_bs32")
+    _full_size_case(wl, [int(order[0]), int(order[len(order) // 2])], "qwen3_8b_bs32", repeat=True)

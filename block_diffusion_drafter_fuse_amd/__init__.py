@@ -21,11 +21,13 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",
 
 EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fuse_ctx",
             "dflash_draft_block", "dflash_accept", "dflash_slot_reset", "dflash_slot_len",
-            "dflash_read_cache", "dflow_relay", "dflow_read_relay", "dflash2_select", "dflash_profile_enable",
+            "dflash_read_cache", "dflow_relay", "dflow_read_relay", "dflash2_select", "dflash2_conv_attach",
+            "dflash_profile_enable",
             "dflash_profile_read", "dflash_strerror", "dflash_last_error")
 
 KERNEL_KINDS = ("fuse_gemm", "fuse_norm", "ctx_kv_gemm", "embed", "norm", "qkv_gemm", "attention",
-                "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "relay", "select", "accept")
+                "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "relay", "select", "conv",
+                "accept")
 
 
 class DflashError(RuntimeError):
@@ -62,6 +64,17 @@ class dflash2_selector_weights(ctypes.Structure):
     _fields_ = [("a", ctypes.c_void_p), ("b", ctypes.c_void_p), ("w_h", ctypes.c_void_p), ("rank", ctypes.c_int32)]
 
 
+class dflash2_conv_site(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_void_p), ("kbase", ctypes.c_void_p)]
+
+
+CONV_SITES = ("attn_in", "attn_out", "ffn_in", "ffn_out")
+
+
+class dflash2_conv_layer(ctypes.Structure):
+    _fields_ = [(n, dflash2_conv_site) for n in CONV_SITES]
+
+
 _LIB = None
 
 
@@ -89,6 +102,7 @@ def lib() -> ctypes.CDLL:
     L.dflow_relay.argtypes = [vp, vp, i32, P(i32), P(i32), vp, i32, vp, P(vp), P(dflow_relay_weights)]
     L.dflow_read_relay.argtypes = [vp, vp, i32, vp, P(i32)]
     L.dflash2_select.argtypes = [vp, vp, i32, vp, vp, vp, i32, P(dflash2_selector_weights), vp, vp]
+    L.dflash2_conv_attach.argtypes = [vp, P(dflash2_conv_layer)]
     L.dflash_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
     L.dflash_profile_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.dflash_strerror.argtypes = [ctypes.c_int]
@@ -239,6 +253,20 @@ class Drafter:
         _check(lib().dflash2_select(self.h, _stream(stream), int(n_req), _ptr(anchor), _ptr(cand),
                                     _ptr(cand_logits), int(k), ctypes.byref(sw), _ptr(out_path), _ptr(out_scores)),
                "dflash2_select")
+
+    def conv_attach(self, layers=None):
+        """dflash2_conv_attach: layers is a list of N dicts site -> {"w", "kbase"}
+        (device tensors, kept alive here), or None to detach."""
+        if layers is None:
+            self._conv = None
+            _check(lib().dflash2_conv_attach(self.h, None), "dflash2_conv_attach")
+            return
+        arr = (dflash2_conv_layer * self.d.N)()
+        for l in range(self.d.N):
+            for s in CONV_SITES:
+                setattr(arr[l], s, dflash2_conv_site(_ptr(layers[l][s]["w"]), _ptr(layers[l][s]["kbase"])))
+        _check(lib().dflash2_conv_attach(self.h, arr), "dflash2_conv_attach")
+        self._conv = (layers, arr)
 
     def read_relay(self, slot: int, out, stream=None) -> int:
         n = ctypes.c_int32()

@@ -27,6 +27,7 @@
 #include "../../include/dflash_fuse.h"
 #include "attention.h"
 #include "common.h"
+#include "conv.h"
 #include "gemm.h"
 #include "gemm_tiled.h"
 #include "lmhead.h"
@@ -73,7 +74,7 @@ struct Plan {
   // workspace
   size_t x_off, u_off, ssq_off, q_off, kb_off, vbt_off, o_off, h_off;
   size_t po_off, pml_off, lmv_off, lmi_off, hc_off, hclo_off, fssq_off, part_off, ctr_off;
-  size_t rin_off, rlnh_off, rs_off, sel_off, ws_bytes;
+  size_t rin_off, rlnh_off, rs_off, sel_off, cv_off, ob_off, zc_off, ws_bytes;
   int relay_rows;  // relay rows one call can hold: max_batch * (B - 2)
   int BP;
   size_t lm_entries;
@@ -96,13 +97,13 @@ int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
 // Few-token LM head: one 16-wave work-group per CU and 16-row block.
 int lm_chunks_small(int rowblocks) { return std::max(1, 256 / rowblocks); }
 
-// Top-1 LM head through the GEMM engines: one partial per 16-row tile (GEMV,
-// few rows) or per wave fragment row of the wide tiled GEMM (many rows).
 // Which GEMM engine serves M rows against a weight of ngroups 16-row groups:
 // few rows, or a narrow weight (it stays in L2 across the 16-row blocks),
 // take the activation-stationary GEMV; the rest the tiled GEMM.
 bool uses_gemv(int M, int ngroups) { return M <= kSkinnyMaxM || ngroups <= kNarrowMaxGroups; }
 
+// Top-1 LM head through the GEMM engines: one partial per 16-row tile (GEMV,
+// few rows) or per wave fragment row of the wide tiled GEMM (many rows).
 int lm_top1_chunks(int Mlm, int V) {
   return uses_gemv(Mlm, ceil_div(V, 16)) ? ceil_div(V, 16) : ceil_div(V, TileWide::kFeatPerWave);
 }
@@ -189,6 +190,10 @@ void make_plan(const dflash_dims* d, Plan* p) {
   p->rs_off = off;   off = align_up(off + (size_t)p->relay_rows * d->D * e);
   // selector gates [rows][rank <= 256], then pair tables [rows][16][16]
   p->sel_off = off;  off = align_up(off + (size_t)Mlm * 256 * 4 * 2);
+  // two-tap convolution: convolved GEMM operand, sub-layer output, tap corrections
+  p->cv_off = off;   off = align_up(off + (size_t)M * d->D * e);
+  p->ob_off = off;   off = align_up(off + (size_t)M * d->D * e);
+  p->zc_off = off;   off = align_up(off + (size_t)M * (d->D / 8) * 4);
   p->ws_bytes = off;
 }
 
@@ -220,6 +225,7 @@ struct dflash_ctx {
   std::vector<int> relay_n;    // DFlow relay rows stored per slot (offsets 2..1+n)
   std::vector<int> relay_len;  // slot length they were stored at
   int last_draft_n = 0;        // requests of the most recent draft (its final hidden states are in the workspace)
+  std::vector<dflash2_conv_layer> conv;  // DFlash 2 two-tap convolution, empty when detached
   template <typename T> T* wsp(size_t off) const { return reinterpret_cast<T*>(ws + off); }
 };
 
@@ -601,9 +607,42 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   aa.meta = apl.meta;
 
   const int qd = d.Hq * d.hd, kd = d.Hkv * d.hd;
+  const bool conv = !c->conv.empty();
+  T* cv = c->wsp<T>(p.cv_off);
+  T* ob = c->wsp<T>(p.ob_off);
+  float* zc = c->wsp<float>(p.zc_off);
+  // One convolution site: tap corrections z = [W_0; W_1] x on the GEMM engine
+  // (row-scaled for a normed site), then the tap mix.  Normed sites read the
+  // folded RMSNorm operand (u, ssq) and write the convolved operand cv;
+  // residual sites read the sub-layer output ob and update h, u and ssq.
+  auto conv_site = [&](const dflash2_conv_site& cs, bool normed, const T* g_next_norm) {
+    ProfScope ps(c, DFLASH_K_CONV, st);
+    const T* in = normed ? u : ob;
+    launch_gemm<T>(c, wop<T>({{cs.w, d.D / 8}}, 0), aop<T>(in, M, d.D), normed ? nrm : none,
+                   EpiStore<float>{zc, d.D / 8}, st);
+    ConvMixArgs<T> ca{};
+    ca.in = in;
+    ca.ssq = ssq;
+    ca.inv_d = 1.0f / (float)d.D;
+    ca.eps = d.rms_eps;
+    ca.z = zc;
+    ca.kbase = static_cast<const T*>(cs.kbase);
+    ca.B = d.B;
+    ca.D = d.D;
+    ca.y = cv;
+    ca.h = x;
+    ca.u = u;
+    ca.g = g_next_norm;
+    ca.ssq_out = ssq;
+    if (normed)
+      hipLaunchKernelGGL((conv_mix_kernel<T, false>), dim3(M), dim3(256), 0, st, ca);
+    else
+      hipLaunchKernelGGL((conv_mix_kernel<T, true>), dim3(M), dim3(256), 0, st, ca);
+  };
   for (int l = 0; l < d.N; ++l) {
     const dflash_layer_weights& lw = c->layers[l];
     const T* g_next = static_cast<const T*>(l + 1 < d.N ? c->layers[l + 1].g_attn : c->w.g_final);
+    if (conv) conv_site(c->conv[l].attn_in, true, nullptr);
     EpiQKV<T> eq{};
     eq.q = q;
     eq.kb = kb;
@@ -617,8 +656,8 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     eq.meta = dm;
     {
       ProfScope ps(c, DFLASH_K_QKV_GEMM, st);
-      launch_gemm<T>(c, wop<T>({{lw.w_q, qd}, {lw.w_kb, kd}, {lw.w_vb, kd}}, d.hd / 2), aop<T>(u, M, d.D), nrm,
-                     eq, st);
+      launch_gemm<T>(c, wop<T>({{lw.w_q, qd}, {lw.w_kb, kd}, {lw.w_vb, kd}}, d.hd / 2),
+                     aop<T>(conv ? cv : u, M, d.D), conv ? none : nrm, eq, st);
     }
     aa.layer = l;
     {
@@ -631,19 +670,30 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     }
     {
       ProfScope ps(c, DFLASH_K_O_GEMM, st);
-      launch_gemm<T>(c, wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), none,
-                     EpiResidualNorm<T>{x, u, static_cast<const T*>(lw.g_ffn), ssq, d.D, nslot}, st);
+      if (conv)
+        launch_gemm<T>(c, wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), none, EpiStore<T>{ob, d.D}, st);
+      else
+        launch_gemm<T>(c, wop<T>({{lw.w_o, d.D}}, 0), aop<T>(o, M, qd), none,
+                       EpiResidualNorm<T>{x, u, static_cast<const T*>(lw.g_ffn), ssq, d.D, nslot}, st);
+    }
+    if (conv) {
+      conv_site(c->conv[l].attn_out, false, static_cast<const T*>(lw.g_ffn));
+      conv_site(c->conv[l].ffn_in, true, nullptr);
     }
     {
       ProfScope ps(c, DFLASH_K_GATEUP_GEMM, st);
-      launch_gemm<T>(c, wop<T>({{lw.w_gate, d.I}, {lw.w_up, d.I}}, d.I), aop<T>(u, M, d.D), nrm,
-                     EpiSwiGLU<T>{h, d.I}, st);
+      launch_gemm<T>(c, wop<T>({{lw.w_gate, d.I}, {lw.w_up, d.I}}, d.I), aop<T>(conv ? cv : u, M, d.D),
+                     conv ? none : nrm, EpiSwiGLU<T>{h, d.I}, st);
     }
     {
       ProfScope ps(c, DFLASH_K_DOWN_GEMM, st);
-      launch_gemm<T>(c, wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), none,
-                     EpiResidualNorm<T>{x, u, g_next, ssq, d.D, nslot}, st);
+      if (conv)
+        launch_gemm<T>(c, wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), none, EpiStore<T>{ob, d.D}, st);
+      else
+        launch_gemm<T>(c, wop<T>({{lw.w_down, d.D}}, 0), aop<T>(h, M, d.I), none,
+                       EpiResidualNorm<T>{x, u, g_next, ssq, d.D, nslot}, st);
     }
+    if (conv) conv_site(c->conv[l].ffn_out, false, g_next);
   }
   run_lmhead<T>(c, st, n_req, top_k, out_ids, out_vals, out_logits);
 }
@@ -1037,6 +1087,23 @@ int dflash2_select(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* 
   else run_select<float>(ctx, st, n_req, anchor, cand, cand_logits, k, sw, out_path, out_scores);
   int rc = DFLASH_OK;
   if (!hip_ok(hipGetLastError(), "select launch", &rc)) return rc;
+  return DFLASH_OK;
+}
+
+int dflash2_conv_attach(dflash_ctx* ctx, const dflash2_conv_layer* layers) {
+  g_last_error.clear();
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  if (!layers) {
+    ctx->conv.clear();
+    return DFLASH_OK;
+  }
+  if (ctx->d.D % 256) return fail(DFLASH_EUNSUPPORTED, "the two-tap convolution needs D % 256 == 0");
+  for (int l = 0; l < ctx->d.N; ++l) {
+    const dflash2_conv_site* s[4] = {&layers[l].attn_in, &layers[l].attn_out, &layers[l].ffn_in, &layers[l].ffn_out};
+    for (const dflash2_conv_site* x : s)
+      if (!x->w || !x->kbase) return fail(DFLASH_EINVAL, "convolution tensors must not be NULL");
+  }
+  ctx->conv.assign(layers, layers + ctx->d.N);
   return DFLASH_OK;
 }
 

@@ -366,6 +366,19 @@ struct EpiSigmoidOut {
   }
 };
 
+// Plain store of features f..f+3 of row m in OutT (fp32 or the storage type).
+template <typename OutT>
+struct EpiStore {
+  static constexpr bool kPaired = false;
+  static constexpr bool kRow = false;
+  OutT* out;
+  int ld;
+  __device__ __forceinline__ void apply1(int m, bool valid, int f, f32x4_t v) const {
+    if (!valid) return;
+    store4<OutT>(out + (size_t)m * ld + f, v[0], v[1], v[2], v[3]);
+  }
+};
+
 // ---------------------------------------------------------------- helpers for the GEMM kernels
 
 template <typename T>

@@ -267,6 +267,39 @@ int dflash2_select(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* 
                    const float* cand_logits, int32_t k, const dflash2_selector_weights* sw, int32_t* out_path,
                    float* out_scores);
 
+/* DFlash 2 two-tap dynamic convolution weights of one site (storage dtype,
+ * row-major):
+ *   w     [2 * D/16, D]  rows 0..D/16-1: W_0 (current-row tap correction),
+ *                        rows D/16..2*D/16-1: W_1 (left-row tap correction)
+ *   kbase [2, D]         base kernels of the current and the left tap */
+typedef struct dflash2_conv_site {
+  const void* w;
+  const void* kbase;
+} dflash2_conv_site;
+
+/* The four sites of one drafter layer: the normed attention input, the
+ * attention output (after w_o) before its residual add, the normed FFN input,
+ * and the FFN output (after w_down) before its residual add. */
+typedef struct dflash2_conv_layer {
+  dflash2_conv_site attn_in;
+  dflash2_conv_site attn_out;
+  dflash2_conv_site ffn_in;
+  dflash2_conv_site ffn_out;
+} dflash2_conv_layer;
+
+/* DFlash 2 two-tap dynamic depthwise convolution ("DFlash 2：正确 token 已在候选里",
+ * the second-insight section).  Attaches (layers != NULL: a [host] array of N
+ * entries, copied; the device tensors must outlive the attachment) or detaches
+ * (layers == NULL) the convolution.  While attached, every dflash_draft_block
+ * applies at each site, along the block offsets t = 0..B-1 of every request,
+ *   y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1},
+ *   k_{t,j}[c] = kbase[j][c] + (W_j x_t)[c / 16],   x_{-1} = 0,
+ * where x is the site's input (the anchor at offset 0 is the last verified
+ * token; the first drafted offset reads it).  Requires D % 256 == 0
+ * (EUNSUPPORTED otherwise); EINVAL on a NULL tensor.  Host-only call: no
+ * device work, takes effect from the next draft. */
+int dflash2_conv_attach(dflash_ctx* ctx, const dflash2_conv_layer* layers);
+
 /* Kernel kinds, for per-kernel timing. */
 enum dflash_kernel_kind {
   DFLASH_K_FUSE_GEMM = 0,   /* context fusion GEMM W_c [H^(l1);...] */
@@ -284,6 +317,7 @@ enum dflash_kernel_kind {
   DFLASH_K_TOPK_MERGE,      /* top-k merge */
   DFLASH_K_RELAY,           /* DFlow relay: assembly and the relay MLP GEMMs */
   DFLASH_K_SELECT,          /* DFlash 2 selector: gate GEMM, pair scores and walk */
+  DFLASH_K_CONV,            /* DFlash 2 two-tap convolution: tap-correction GEMM and the tap mix */
   DFLASH_K_ACCEPT,          /* acceptance scan (stateless call: never timed) */
   DFLASH_K_COUNT
 };

@@ -279,7 +279,27 @@ class Workbench:
         return ms, wall / steps * 1e3, kern
 
 
-def measure(wl, w_dev, torch, steps, warmup, label):
+def measure_conv(wb, steps, warmup, label):
+    """The same step with the DFlash 2 two-tap convolution attached at all four
+    sites of every layer (seeded synthetic weights); the convolution's own
+    kernels (tap-correction GEMMs and tap mixes) are timed with events."""
+    import synth
+    d = wb.d
+    cw = synth.make_conv_weights(d, wb.wl.seed)
+    dev = [{s: {k: wb.dfa.to_device(v) for k, v in t.items()} for s, t in layer.items()} for layer in cw]
+    wb.dr.conv_attach(dev)
+    ms, _, kern = wb.timed(steps, warmup, "conv")
+    wb.dr.conv_attach(None)
+    e = elt(d)
+    byts = 4 * d.N * ((d.D // 8) * d.D + 2 * d.D) * e
+    return {"workload": f"{label} step with the two-tap convolution",
+            "ms_per_step": round(ms, 4), "conv_ms_per_step": round(kern[0] * kern[1] / steps, 4),
+            "conv_launches_per_step": kern[1] // steps, "conv_weight_bytes": byts,
+            "note": "4 sites x N layers: tap-correction GEMM on the GEMV engine + tap mix; "
+                    "ms_per_step is the whole step with the convolution attached"}
+
+
+def measure(wl, w_dev, torch, steps, warmup, label, conv=False):
     wb = Workbench(wl, w_dev, torch)
     wb.prepare_targets()
     for _ in range(2):
@@ -305,6 +325,9 @@ def measure(wl, w_dev, torch, steps, warmup, label):
         "roofline": roof_entry(dom, d, wl, kern[0], traffic_for(dom, label)),
     }
     out["roofline"]["launches_timed"] = kern[1]
+    if conv:
+        out["conv"] = measure_conv(wb, steps, warmup, label)
+        out["conv"]["overhead_frac"] = round(out["conv"]["ms_per_step"] / ms - 1.0, 4)
     wb.dr.close()
     del wb
     torch.cuda.synchronize()
@@ -458,7 +481,7 @@ def main():
     ap.add_argument("--companion", default="qwen3_8b_bs1", help="second workload reported under 'bs1' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-relay", action="store_true",
-                    help="skip the DFlow relay and DFlash 2 selector measurements")
+                    help="skip the DFlow relay and the DFlash 2 selector and convolution measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy one buffer of this many MiB (reference dispatch for byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -504,7 +527,7 @@ def main():
     w_np = synth.make_weights(wl.dims, wl.seed)
     w_dev = dfa.Drafter.upload_weights(w_np)
     print(f"[bench] measuring {args.workload}", file=sys.stderr, flush=True)
-    main_res = measure(wl, w_dev, torch, args.steps, args.warmup, args.workload)
+    main_res = measure(wl, w_dev, torch, args.steps, args.warmup, args.workload, conv=not args.no_relay)
     comp = None
     if args.companion:
         wc = synth.get_config(args.companion)
@@ -557,6 +580,8 @@ def main():
                                             "step_hbm_roof_frac", "roofline", "breakdown_ms")}
     if relay:
         line["relay"] = relay
+    if "conv" in main_res:
+        line["conv"] = main_res["conv"]
     if select:
         line["select"] = select
     print(json.dumps(line), flush=True)

@@ -18,6 +18,8 @@
 // K splits and M tiles of one weight tile back to back, which keeps that
 // weight tile in the XCD's L2.
 #pragma once
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace dfl {
@@ -185,6 +187,23 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
           acc[i][j] = MM::step(wf[j], af[i], acc[i][j]);
           if constexpr (ALO) acc[i][j] = MM::step(wf[j], al[i], acc[i][j]);
         }
+    }
+    if constexpr (std::is_same<T, bf16_t>::value && !ALO && KPS == 2) {
+      // Instruction order for the stage: the first k-step's fragment reads,
+      // then the second k-step's reads spread between the first k-step's
+      // MFMAs (so the LDS works while the matrix cores do), then the rest.
+      // Left to itself the compiler waits on each small batch of reads
+      // right before the MFMAs that use it.
+      constexpr int R = FM + FN, MK = FM * FN, Q = MK / R > 0 ? MK / R : 1;
+      constexpr int REST = MK - Q * R > 0 ? MK - Q * R : 0;
+      __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS reads
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, Q, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, REST, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, MK, 0);
     }
     buf = buf + 1 == NBUF ? 0 : buf + 1;
   }

@@ -30,6 +30,7 @@
 #include "conv.h"
 #include "gemm.h"
 #include "gemm_tiled.h"
+#include "gemv_stream.h"
 #include "lmhead.h"
 #include "misc.h"
 
@@ -56,6 +57,8 @@ constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (L
 constexpr bool kGemvPF = false;        // prefetch the next tile's weights before the current MFMAs
 constexpr int kGemvWGs = 256;          // skinny GEMM work-groups per 16-token block
 constexpr int kGemvXcds = 8;           // XCDs; work-group i runs on XCD i mod 8
+constexpr int kRsNbuf = 6;             // row-streaming GEMV ring depth (stages of 16 KB)
+constexpr int kRsMaxSplit = 8;         // K ranges of the row-streaming GEMV
 constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, unroll
 constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
 constexpr size_t kPartFloats = size_t(16) << 20;  // split-K partials (64 MB)
@@ -279,12 +282,61 @@ void launch_tiled(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, con
                      nblocks);
 }
 
+// Row-streaming GEMV plan: K ranges and tiles per work-group for about one
+// work-group per CU, fewest stages per work-group (ties: fewer K ranges).
+// Returns false where the kernel does not apply (rows not whole 1 KB stages,
+// too many stages for the held activations of a row epilogue, tile sums
+// beyond LDS, or partials beyond the workspace).
+struct RsPlan {
+  int nsplit, nst, red2, tpw, nwg, lds;
+};
+template <typename T, bool ALO, class Epi>
+bool plan_rs(const WOperand<T>& w, const AOperand<T>& a, int mt, RsPlan* out) {
+  const long row_bytes = (long)a.nk * a.kseg * (long)sizeof(T);
+  if (row_bytes % kRsStage != 0 || (Epi::kPaired && w.pair % 8 != 0)) return false;
+  const int nst_all = (int)(row_bytes / kRsStage);
+  const int ah = gemv_rs_ah(ALO);
+  const int ks_min = ceil_div(nst_all, ah);
+  const int ks_max = Epi::kRow ? 1 : std::min(nst_all, kRsMaxSplit);
+  long best = -1;
+  for (int ks = ks_min; ks <= ks_max; ++ks) {
+    const int per = std::max(1, kTiledSlots / (ks * mt));
+    const int tpw = ceil_div(w.ngroups, per);
+    const int nst = ceil_div(nst_all, ks);
+    const int red2 = nst < 2 || nst_all - (ceil_div(nst_all, nst) - 1) * nst < 2;
+    const int lds = gemv_rs_lds(kRsNbuf, red2, tpw);
+    if (lds > kRsLdsMax) continue;
+    if (ks > 1 && ((long)mt * w.ngroups > kCounters - 64 || (size_t)mt * w.ngroups * ks * 256 > kPartFloats)) continue;
+    const long cost = (long)tpw * nst;
+    if (best < 0 || cost < best) {
+      best = cost;
+      *out = RsPlan{ceil_div(nst_all, nst), nst, red2, tpw, ceil_div(w.ngroups, tpw), lds};
+    }
+  }
+  return best >= 0;
+}
+
 template <typename T, bool ALO = false, class Epi>
 void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
                  hipStream_t st) {
   if (a.M <= 0 || w.ngroups <= 0) return;
   const int K = a.nk * a.kseg;
   {
+    const int mt = ceil_div(a.M, 16);
+    RsPlan rp;
+    if (uses_gemv(a.M, w.ngroups) && mt < kGemvXcds && plan_rs<T, ALO, Epi>(w, a, mt, &rp)) {
+      // Row-streaming GEMV (few token blocks against a wide weight).
+      auto kern = gemv_rs_kernel<T, kRsNbuf, ALO, Epi::kPaired, Epi>;
+      static bool attr_set = false;
+      if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  kRsLdsMax);
+        attr_set = true;
+      }
+      const RsSplit sp{rp.nsplit, rp.nst, rp.red2, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off)};
+      hipLaunchKernelGGL(kern, dim3(rp.nwg, rp.nsplit * mt), dim3(1024), rp.lds, st, w, a, nrm, sp, epi, rp.tpw);
+      return;
+    }
     if (uses_gemv(a.M, w.ngroups)) {
       // Activation-stationary GEMV: 16-row tiles, K split across the waves of
       // a work-group (LDS reduction; a cross-work-group split would need

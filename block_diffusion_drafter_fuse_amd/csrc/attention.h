@@ -6,19 +6,20 @@
 // of the slot followed by the block's own K_b/V_b.  There is no mask.  The
 // context is cut into splits of `chunk` keys (a multiple of 64); the last
 // split also takes the block keys.  One work-group per split holds QF waves,
-// one per 16 query rows.  Keys are consumed in stages of 64: a stage's K rows
-// and V^T tile are copied global -> LDS asynchronously (16 bytes per lane, no
-// register round trip) into a ring of NBUF buffers, one barrier per stage, so
-// every K/V byte crosses the vector-memory path once per work-group.  Each
+// one per 16 query rows.  Keys are consumed in stages of STG (a multiple of the
+// cache's V^T tile): a stage's K rows and V^T tiles are copied global -> LDS
+// asynchronously (16 bytes per lane, no register round trip) into a ring of
+// NBUF buffers, one barrier per stage, so every K/V byte crosses the
+// vector-memory path once per work-group.  Each
 // wave computes S^T = K Q^T and O^T += V^T P^T with MFMA and keeps an online
 // softmax per query column, then stores its partial (max, sum, O).  The
 // combine kernel merges the splits of every (r, g) in split order, so results
 // are deterministic.
 //
 // Layouts: Q, K_b rows [M, heads*hd]; V_b transposed vbT[(r*Hkv+g)*hd + d][64]
-// (zero padded past B); cache keys [pos][hd] and values in 64-key tiles
-// [pos/64][hd][64] per (slot, layer, head), so a stage's V^T is one contiguous
-// block.  Within a 16*NT-key MFMA step a lane holds 4*NT consecutive keys of
+// (zero padded past B); cache keys [pos][hd] and values in kVTile-key tiles
+// [pos/kVTile][hd][kVTile] per (slot, layer, head), so a stage's V^T is one
+// contiguous block.  Within a 16*NT-key MFMA step a lane holds 4*NT consecutive keys of
 // one query column, which is exactly the key run it needs as the P^T operand
 // of the next MFMA.  LDS rows are unpadded; 16-byte chunk c of row r sits at
 // slot c ^ f(r), with f chosen so that the 8 rows one fragment read touches
@@ -28,7 +29,8 @@
 
 namespace dfl {
 
-constexpr int kAttnStage = 64;  // keys per LDS stage (and per V^T cache tile)
+constexpr int kAttnStage = 64;  // split lengths are multiples of this (and of every stage size)
+constexpr float kAttnSlack = 8.f;  // log2 headroom before a query's reference maximum moves
 
 struct AttnMeta {
   int n_req;
@@ -54,12 +56,14 @@ struct AttnArgs {
   AttnMeta meta;
 };
 
-template <typename T, int HD, int QF, int NBUF>
+template <typename T, int HD, int QF, int NBUF, int STG>
 struct AttnStage {
-  static constexpr int KRB = HD * (int)sizeof(T);          // K row bytes
-  static constexpr int VRB = kAttnStage * (int)sizeof(T);  // V^T row bytes
-  static constexpr int KBYTES = kAttnStage * KRB;
-  static constexpr int VBYTES = HD * VRB;
+  static_assert(STG % kVTile == 0 && kAttnStage % STG == 0, "stages of whole V^T tiles");
+  static constexpr int KRB = HD * (int)sizeof(T);      // K row bytes
+  static constexpr int VRB = kVTile * (int)sizeof(T);  // V^T row bytes within a tile
+  static constexpr int TILEB = HD * VRB;               // V^T tile bytes
+  static constexpr int KBYTES = STG * KRB;
+  static constexpr int VBYTES = (STG / kVTile) * TILEB;
   static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int KI = KBYTES / 1024;  // copy instructions (1 KB each) per stage
   static constexpr int VI = VBYTES / 1024;
@@ -68,26 +72,51 @@ struct AttnStage {
   static_assert((KI + VI) % QF == 0 && KI % QF == 0, "copy blocks split evenly over the waves");
 };
 
-// Swizzle of K rows: the rows of one bank cycle are {4*NT*j + 4t + (0..3)}
-// for j = 0, 1 (NT = 2) or four consecutive pairs (NT = 1).
-template <int NT>
+// LDS swizzles.  A 16-byte fragment read is served 16 lanes (256 bytes) per
+// cycle, so the 16 rows one read touches at a given chunk must land on 16
+// distinct 16-byte slots of the 256-byte bank window.
+//
+// K rows (KCH chunks of 16 bytes): chunk c of row r sits at c ^ kswz(r).  With
+// 256-byte rows every row starts the window, so kswz must differ over the 16
+// rows of a read: {4*NT*j + 4t + (0..3)}, j = 0..3 (NT = 2), or 16 consecutive
+// rows (NT = 1).  With 128-byte rows two rows share the window (row parity
+// picks the half) and 3 bits suffice.
+template <int NT, int KCH>
 __device__ __forceinline__ int attn_kswz(int row) {
-  return (row & 3) | (((row >> (NT == 2 ? 3 : 2)) & 1) << 2);
+  if constexpr (KCH >= 16) {
+    if constexpr (NT == 2) return (row & 3) | (((row >> 3) & 3) << 2);
+    return row & 15;
+  } else {
+    if constexpr (NT == 2) return ((row >> 1) & 1) | (((row >> 3) & 3) << 1);
+    return (row >> 1) & 7;
+  }
 }
 
-template <typename T, int HD, int QF, int NBUF>
-__global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
+// V^T rows (head-dim index d) of VCH 16-byte chunks: a read touches rows
+// d..d+15 at one chunk.  64-byte rows: four rows share the window (d & 3
+// picks the quarter), chunk c at c ^ ((d >> 2) & 3).  128-byte rows: two rows
+// share it, chunk c at c ^ ((d >> 1) & 7).
+template <int VCH>
+__device__ __forceinline__ int attn_vswz(int row) {
+  return VCH >= 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
+}
+
+// WPE: waves per SIMD the register allocation must allow (the kernel is
+// bound by how many work-groups a CU holds: each one's stage waits and its
+// dependent S -> softmax -> P.V chain are hidden by the others).
+template <typename T, int HD, int QF, int NBUF, int STG, int WPE>
+__global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a) {
   using MM = Mma<T>;
-  using SG = AttnStage<T, HD, QF, NBUF>;
+  using SG = AttnStage<T, HD, QF, NBUF, STG>;
   constexpr int KS = MM::KSTEP;  // keys per P.V step
   constexpr int EPL = MM::EPL;
   constexpr int NT = KS / 16;    // S^T tiles per P.V step
   constexpr int HS = HD / KS;    // k-steps over the head dim
   constexpr int DF = HD / 16;    // output d fragments
   constexpr int QR = QF * 16;
-  constexpr int PVS = kAttnStage / KS;  // P.V steps per stage
+  constexpr int PVS = STG / KS;  // P.V steps per stage
   constexpr int KCH = SG::KRB / 16, VCH = SG::VRB / 16;  // 16-byte chunks per row
-  static_assert(KCH >= 8 && VCH >= 8, "swizzle needs 8 chunks per row");
+  static_assert(KCH >= 8 && VCH >= 4, "swizzle needs 8 chunks per K row, 4 per V^T row");
 
   extern __shared__ __align__(16) char lds[];
   const int tid = threadIdx.x;
@@ -113,11 +142,24 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
 #pragma unroll
     for (int h = 0; h < HS; ++h) qf[h] = valid ? ld16(qp + h * KS) : make_uint4(0, 0, 0, 0);
   }
+  // Padding loads after the query fragments: the compiler waits for a
+  // fragment with a count of the loads it issued after it; the padding keeps
+  // that count at or above the copies in flight at the first stage (which it
+  // does not see), so the first stage does not wait for the whole prologue.
+  constexpr int NPAD = (NBUF - 1) * (SG::NIW);
+  uint32_t pad[NPAD];
+  {
+    asm volatile("" ::: "memory");
+    const char* pp = reinterpret_cast<const char*>(a.q) + (lane & 7) * 4;
+#pragma unroll
+    for (int i = 0; i < NPAD; ++i) pad[i] = *reinterpret_cast<const uint32_t*>(pp + i * 64);
+    asm volatile("" ::: "memory");
+  }
 
   // Stages: context keys [kbeg, kend) of this split, then (last split) the block.
   const int kbeg = s * a.chunk;
   const int kend = min(ctx, kbeg + a.chunk);
-  const int nctx = kend > kbeg ? (kend - kbeg + kAttnStage - 1) / kAttnStage : 0;
+  const int nctx = kend > kbeg ? (kend - kbeg + STG - 1) / STG : 0;
   const int nst = nctx + (s == S - 1 ? 1 : 0);
   const T* hb = a.pool + (size_t)a.meta.slot[r] * a.slot_stride + (size_t)a.layer * a.layer_stride +
                 (size_t)g * a.head_stride;
@@ -128,7 +170,7 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
   // (j < KI) or V^T rows; each lane one 16-byte chunk of one row.
   auto issue = [&](int i, int b) {
     const bool blk = i >= nctx;
-    const int k0 = blk ? 0 : kbeg + i * kAttnStage;  // multiple of 64
+    const int k0 = blk ? 0 : kbeg + i * STG;  // multiple of STG
     char* base = lds + b * SG::BUF;
 #pragma unroll
     for (int ii = 0; ii < SG::NIW; ++ii) {
@@ -136,15 +178,17 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
       if (j < SG::KI) {
         constexpr int RPI = 1024 / SG::KRB;
         const int row = j * RPI + lane / KCH;
-        const int chunk = (lane % KCH) ^ attn_kswz<NT>(row);
+        const int chunk = (lane % KCH) ^ attn_kswz<NT, KCH>(row);
         const T* src = blk ? bkb + (size_t)min(row, a.B - 1) * kd : hb + (size_t)(k0 + row) * HD;
         dma16(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
       } else {
         constexpr int RPI = 1024 / SG::VRB;
-        const int row = (j - SG::KI) * RPI + lane / VCH;  // head-dim index d
-        const int chunk = (lane % VCH) ^ (row & 7);
-        const T* src = blk ? bvt + (size_t)row * a.BP
-                           : hb + a.kv_stride + ((size_t)(k0 / kAttnStage) * HD + row) * kAttnStage;
+        const int row = (j - SG::KI) * RPI + lane / VCH;  // tile-major V^T row: tile row / HD, d row % HD
+        const int d = row % HD;
+        const int chunk = (lane % VCH) ^ attn_vswz<VCH>(d);
+        // the block has one V^T tile (B <= 16 keys); later tiles of its stage
+        // re-read it (their keys are masked)
+        const T* src = blk ? bvt + (size_t)d * a.BP : hb + a.kv_stride + ((size_t)(k0 / kVTile) * HD + row) * kVTile;
         dma16(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
       }
     }
@@ -161,18 +205,8 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
 
   int buf = 0;
   for (int i = 0; i < nst; ++i) {
-    const int younger = min(NBUF - 2, nst - 1 - i);
-    static_assert(NBUF >= 2 && NBUF <= 4 && SG::NIW * (NBUF - 2) < 64, "ring depth");
-    if constexpr (NBUF == 4) {
-      if (younger >= 2) wait_vmcnt<2 * SG::NIW>();
-      else if (younger == 1) wait_vmcnt<SG::NIW>();
-      else wait_vmcnt<0>();
-    } else if constexpr (NBUF == 3) {
-      if (younger >= 1) wait_vmcnt<SG::NIW>();
-      else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    static_assert(NBUF >= 2 && SG::NIW * (NBUF - 2) < 64, "ring depth");
+    wait_items<SG::NIW, NBUF - 2>(min(NBUF - 2, nst - 1 - i));
     ring_barrier();
     if (i + NBUF - 1 < nst) {
       int nb = buf + NBUF - 1;
@@ -180,70 +214,113 @@ __global__ __launch_bounds__(64 * QF) void attn_kernel(const AttnArgs<T> a) {
       issue(i + NBUF - 1, nb);
     }
     const bool blk = i >= nctx;
-    const int klim = blk ? a.B : kend - (kbeg + i * kAttnStage);  // valid keys in this stage
+    const int klim = blk ? a.B : kend - (kbeg + i * STG);  // valid keys in this stage
     const char* kl = lds + buf * SG::BUF;
     const char* vl = kl + SG::KBYTES;
+    // S^T for every key of the stage first (the P.V steps' MFMA chains
+    // interleave), then one online-softmax update for the whole stage.
+    float sv[PVS][NT][4];
+    float mx = -INFINITY;
+    // (no branch on the valid key count here: the PVS*NT independent MFMA
+    // chains must sit in one block to interleave; masked keys are cheap)
+    f32x4_t cs[PVS][NT];
 #pragma unroll
-    for (int p = 0; p < PVS; ++p) {
-      const int kb0 = p * KS;  // stage-local first key of this P.V step
-      if (kb0 >= klim) break;
-      float sv[NT][4];
-      float mx = -INFINITY;
+    for (int h = 0; h < HS; ++h)
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int krow = kb0 + (r16 >> 2) * (4 * NT) + 4 * t + (r16 & 3);
-        const char* kr = kl + krow * SG::KRB;
-        const int ksw = attn_kswz<NT>(krow);
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+      for (int p = 0; p < PVS; ++p)
 #pragma unroll
-        for (int h = 0; h < HS; ++h)
-          c = MM::step(*reinterpret_cast<const uint4*>(kr + (((h * 4 + kg) ^ ksw) << 4)), qf[h], c);
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int key = kb0 + kg * (4 * NT) + 4 * t + ii;
-          const float x = key < klim ? c[ii] * a.scale_log2 : -INFINITY;
-          sv[t][ii] = x;
-          mx = fmaxf(mx, x);
+        for (int t = 0; t < NT; ++t) {
+          const int krow = p * KS + (r16 >> 2) * (4 * NT) + 4 * t + (r16 & 3);
+          const uint4 kf =
+              *reinterpret_cast<const uint4*>(kl + krow * SG::KRB + (((h * 4 + kg) ^ attn_kswz<NT, KCH>(krow)) << 4));
+          cs[p][t] = MM::step(kf, qf[h], h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : cs[p][t]);
         }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow, mx);
-      const float alpha = exp2f(mrow - mnew);
-      float ps = 0.f;
-      float pr[NT][4];
+    if (klim >= STG) {  // full stage: no key to mask
+#pragma unroll
+      for (int p = 0; p < PVS; ++p)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            sv[p][t][ii] = cs[p][t][ii] * a.scale_log2;
+            mx = fmaxf(mx, sv[p][t][ii]);
+          }
+    } else {
+#pragma unroll
+      for (int p = 0; p < PVS; ++p)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int key = p * KS + kg * (4 * NT) + 4 * t + ii;
+            sv[p][t][ii] = key < klim ? cs[p][t][ii] * a.scale_log2 : -INFINITY;
+            mx = fmaxf(mx, sv[p][t][ii]);
+          }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // The reference maximum of a query column moves only when a score exceeds
+    // it by more than kAttnSlack (log2 units): probabilities are then at most
+    // 2^kAttnSlack, and l and O, which share the reference, are rescaled
+    // together, so the result is unchanged in exact arithmetic.  The rescale
+    // of O is skipped when no column of the wave moves (the common case once
+    // the first keys have been seen).
+    if (__any(mx > mrow + kAttnSlack)) {
+      const float mnew = mx > mrow + kAttnSlack ? mx : mrow;  // finite: every stage holds a valid key
+      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+      lrow *= alpha;
+      mrow = mnew;
+#pragma unroll
+      for (int d = 0; d < DF; ++d) o[d] *= alpha;
+    }
+    float ps = 0.f;
+#pragma unroll
+    for (int p = 0; p < PVS; ++p)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          pr[t][ii] = exp2f(sv[t][ii] - mnew);
-          ps += pr[t][ii];
+          // hardware exp2: arguments are <= kAttnSlack; results below 2^-126
+          // flush to zero, far below the weight of any contributing key
+          sv[p][t][ii] = __builtin_amdgcn_exp2f(sv[p][t][ii] - mrow);
+          ps += sv[p][t][ii];
         }
-      ps += __shfl_xor(ps, 16);
-      ps += __shfl_xor(ps, 32);
-      lrow = lrow * alpha + ps;
-      mrow = mnew;
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    lrow += ps;
+#pragma unroll
+    for (int p = 0; p < PVS; ++p) {
+      const int kb0 = p * KS;
+      if (kb0 >= klim) break;
       uint4 pp;
       if constexpr (NT == 1) {
-        pp = make_uint4(__float_as_uint(pr[0][0]), __float_as_uint(pr[0][1]), __float_as_uint(pr[0][2]),
-                        __float_as_uint(pr[0][3]));
+        pp = make_uint4(__float_as_uint(sv[p][0][0]), __float_as_uint(sv[p][0][1]), __float_as_uint(sv[p][0][2]),
+                        __float_as_uint(sv[p][0][3]));
       } else {
-        pp.x = (uint32_t)f2bf(pr[0][0]) | ((uint32_t)f2bf(pr[0][1]) << 16);
-        pp.y = (uint32_t)f2bf(pr[0][2]) | ((uint32_t)f2bf(pr[0][3]) << 16);
-        pp.z = (uint32_t)f2bf(pr[1][0]) | ((uint32_t)f2bf(pr[1][1]) << 16);
-        pp.w = (uint32_t)f2bf(pr[1][2]) | ((uint32_t)f2bf(pr[1][3]) << 16);
+        pp.x = (uint32_t)f2bf(sv[p][0][0]) | ((uint32_t)f2bf(sv[p][0][1]) << 16);
+        pp.y = (uint32_t)f2bf(sv[p][0][2]) | ((uint32_t)f2bf(sv[p][0][3]) << 16);
+        pp.z = (uint32_t)f2bf(sv[p][1][0]) | ((uint32_t)f2bf(sv[p][1][1]) << 16);
+        pp.w = (uint32_t)f2bf(sv[p][1][2]) | ((uint32_t)f2bf(sv[p][1][3]) << 16);
       }
-      const int vchunk = (kb0 + kg * 4 * NT) * (int)sizeof(T) / 16;
+      const int vkey = kb0 + kg * 4 * NT;  // first of this lane's keys
+      const char* vt = vl + (vkey / kVTile) * SG::TILEB;
+      const int vchunk = (vkey % kVTile) * (int)sizeof(T) / 16;
 #pragma unroll
       for (int d = 0; d < DF; ++d) {
         const int vrow = d * 16 + r16;
-        const uint4 vf = *reinterpret_cast<const uint4*>(vl + vrow * SG::VRB + ((vchunk ^ (vrow & 7)) << 4));
-        o[d] = MM::step(vf, pp, o[d] * alpha);
+        const uint4 vf = *reinterpret_cast<const uint4*>(vt + vrow * SG::VRB + ((vchunk ^ attn_vswz<VCH>(vrow)) << 4));
+        o[d] = MM::step(vf, pp, o[d]);
       }
     }
     buf = buf + 1 == NBUF ? 0 : buf + 1;
   }
 
+  {
+    uint32_t x = 0;
+#pragma unroll
+    for (int i = 0; i < NPAD; ++i) x |= pad[i];
+    asm volatile("" ::"v"(x));
+  }
   float* po = a.part_o + (size_t)w * QR * HD;
   float* pml = a.part_ml + (size_t)w * QR * 2;
   const int qrow = f * 16 + r16;

@@ -14,6 +14,7 @@ constexpr int kMaxReq = 64;     // requests per call
 constexpr int kMaxLayers = 16;  // drafter layers
 constexpr int kMaxSeg = 40;     // weight segments of one virtual GEMM operand
 constexpr int kMaxKSeg = 16;    // activation segments along K (tapped layers)
+constexpr int kVTile = 32;      // keys per V^T tile of the context cache ([hd][kVTile] per tile)
 
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
 

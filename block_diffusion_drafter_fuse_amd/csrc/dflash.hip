@@ -50,6 +50,9 @@ constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
 constexpr int kAttnWorkMax = 4096;     // attention split work items per call
 constexpr int kAttnTargetWG = 2048;    // attention work-groups aimed for
 constexpr int kAttnMinChunk = 128;     // minimum context keys per split
+constexpr int kAttnNbuf = 2;           // attention K/V ring depth
+constexpr int kAttnStg = 64;           // attention keys per stage
+constexpr int kAttnWpe = 1;            // attention waves per SIMD the registers must allow
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
 constexpr int kNarrowMaxGroups = 64;   // weights of at most 1024 rows also take the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
@@ -161,7 +164,7 @@ void make_plan(const dflash_dims* d, Plan* p) {
   const int M = d->max_batch * d->B;
   const int Mlm = d->max_batch * (d->B - 1);
   const int nslot = d->D / 16;
-  p->BP = kAttnStage;  // block V^T padded to one attention stage
+  p->BP = kVTile;  // block V^T padded to one V^T tile
   p->qf = ceil_div((d->Hq / d->Hkv) * d->B, 16);
   if (p->qf == 3) p->qf = 4;
   off = 0;
@@ -491,10 +494,13 @@ void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
     else go(attn_combine_kernel<T, HD, QF * 16, 1>, 1);
     return;
   }
-  // Two work-groups per CU: a ring of 2 stages of K/V each.
-  constexpr int NBUF = 2;
-  const int lds = AttnStage<T, HD, QF, NBUF>::LDS;
-  auto kern = attn_kernel<T, HD, QF, NBUF>;
+  // Two work-groups per CU, each with a ring of NBUF stages of K/V (fewer
+  // where a stage takes many copy instructions per wave).
+  constexpr int STG = kAttnStg;
+  constexpr int NIW = AttnStage<T, HD, QF, 2, STG>::NIW;
+  constexpr int NBUF = std::min(kAttnNbuf, 2 + 63 / NIW);
+  const int lds = AttnStage<T, HD, QF, NBUF, STG>::LDS;
+  auto kern = attn_kernel<T, HD, QF, NBUF, STG, kAttnWpe>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);

@@ -271,8 +271,8 @@ struct EpiQKV {
 // Context projections of the fusion step: virtual weight
 // [W_kc^0; W_vc^0; W_kc^1; W_vc^1; ...], pair distance hd/2.  Keys are rotated
 // at their absolute positions and written row-major into the slot's cache;
-// values are written transposed in 64-key tiles (cache layout
-// [Hkv][ctx_pad/64][hd][64]).
+// values are written transposed in kVTile-key tiles (cache layout
+// [Hkv][ctx_pad/kVTile][hd][kVTile]).
 template <typename T>
 struct EpiKVAppend {
   static constexpr bool kPaired = true;
@@ -300,11 +300,11 @@ struct EpiKVAppend {
       store4<T>(dst, a[0], a[1], a[2], a[3]);
       store4<T>(dst + half, b[0], b[1], b[2], b[3]);
     } else {
-      T* tile = base + (size_t)(pos >> 6) * hd * 64 + (pos & 63);
+      T* tile = base + (size_t)(pos / kVTile) * hd * kVTile + (pos % kVTile);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        tile[(size_t)(c + i) * 64] = from_f<T>(a[i]);
-        tile[(size_t)(c + half + i) * 64] = from_f<T>(b[i]);
+        tile[(size_t)(c + i) * kVTile] = from_f<T>(a[i]);
+        tile[(size_t)(c + half + i) * kVTile] = from_f<T>(b[i]);
       }
     }
   }

@@ -48,6 +48,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most y * IPI vector-memory instructions of this wave are
+// outstanding (y in 0 .. MAXY, runtime; each case a compile-time count).
+template <int IPI, int MAXY>
+__device__ __forceinline__ void wait_items(int y) {
+  if constexpr (MAXY <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (y >= MAXY) {
+      wait_vmcnt<MAXY * IPI>();
+      return;
+    }
+    wait_items<IPI, MAXY - 1>(y);
+  }
+}
+
 // Work-group barrier for the stage ring: the wave's LDS reads are complete
 // (so a buffer may be refilled after it) and no memory access is moved across.
 // Outstanding asynchronous copies are not waited for here.

@@ -51,21 +51,6 @@ __host__ __device__ constexpr int gemv_rs_lds(int nbuf, bool red2, int tiles) {
   return nbuf * 16 * kRsStage + gemv_rs_red_bytes(red2) + tiles * 1024 + 16 * 64 * 4;
 }
 
-// Wait until at most y * IPI vector-memory instructions of this wave are
-// outstanding (y in 0 .. MAXY, runtime; each case a compile-time count).
-template <int IPI, int MAXY>
-__device__ __forceinline__ void wait_items(int y) {
-  if constexpr (MAXY <= 0) {
-    wait_vmcnt<0>();
-  } else {
-    if (y >= MAXY) {
-      wait_vmcnt<MAXY * IPI>();
-      return;
-    }
-    wait_items<IPI, MAXY - 1>(y);
-  }
-}
-
 struct RsSplit {
   int nsplit;   // K ranges (grid.y = nsplit x token blocks)
   int nst;      // stages per K range (the last range may be shorter)

@@ -192,7 +192,7 @@ __global__ void accept_kernel(int n_req, int B, const int* cand, int cand_stride
 }
 
 // Read back cached K/V of one (slot, layer) into fp32 [Hkv][n][hd]; values
-// are stored in 64-key tiles [pos/64][hd][64] per head.
+// are stored in kVTile-key tiles [pos/kVTile][hd][kVTile] per head.
 template <typename T>
 __global__ void read_cache_kernel(const T* kbase, const T* vtbase, size_t head_stride, int hd, int Hkv,
                                   int pos0, int n, float* kout, float* vout) {
@@ -204,7 +204,7 @@ __global__ void read_cache_kernel(const T* kbase, const T* vtbase, size_t head_s
   const int p = rem / hd, d = rem - p * hd;
   kout[idx] = to_f<T>(kbase[(size_t)g * head_stride + (size_t)(pos0 + p) * hd + d]);
   const int pos = pos0 + p;
-  vout[idx] = to_f<T>(vtbase[(size_t)g * head_stride + ((size_t)(pos >> 6) * hd + d) * 64 + (pos & 63)]);
+  vout[idx] = to_f<T>(vtbase[(size_t)g * head_stride + ((size_t)(pos / kVTile) * hd + d) * kVTile + (pos % kVTile)]);
 }
 
 }  // namespace dfl

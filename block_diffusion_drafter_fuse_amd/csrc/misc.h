@@ -11,12 +11,52 @@ namespace dfl {
 // layer's normed-input operand u = T(x * g) and per-16-feature sums of squares
 // (the RMSNorm is completed by the consuming GEMM).
 template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p), b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[i] = a[i];
+    v[4 + i] = b[i];
+  }
+}
+template <>
+__device__ __forceinline__ void load8<bf16_t>(const bf16_t* p, float (&v)[8]) {
+  const uint4 q = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf2f((bf16_t)(w[i] & 0xffff));
+    v[2 * i + 1] = bf2f((bf16_t)(w[i] >> 16));
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[8]);
+template <>
+__device__ __forceinline__ void store8<float>(float* p, const float (&v)[8]) {
+  *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+  *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+}
+template <>
+__device__ __forceinline__ void store8<bf16_t>(bf16_t* p, const float (&v)[8]) {
+  uint4 q;
+  q.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  q.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  q.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  q.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = q;
+}
+
+// One work-group per block row; thread t handles features 8t .. 8t+7 (and
+// +8*blockDim ...), all loads of a thread issued before any store.
+template <typename T>
 __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const T* e_mask, const int* anchor,
                                                     const T* g, int B, int D, int V, float* x, T* u,
                                                     float* ssq, const DraftRelay rl) {
+  constexpr int PT = 2;  // 8-feature groups per thread and pass (D <= 4096 in one pass)
   const int m = blockIdx.x;
   const int r = m / B, j = m - r * B;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const T* src = nullptr;
   const float* rsrc = nullptr;
   if (j == 0) {
@@ -29,14 +69,40 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const T* e_m
     src = e_mask;
   }
   const int nslot = D >> 4;
-  for (int c = wave; c < (D >> 6); c += 4) {
-    const int d = c * 64 + lane;
-    const float v = rsrc ? rsrc[d] : to_f<T>(src[d]);
-    x[(size_t)m * D + d] = v;
-    u[(size_t)m * D + d] = from_f<T>(v * to_f<T>(g[d]));
-    float ss = v * v;
-    for (int o = 1; o < 16; o <<= 1) ss += __shfl_xor(ss, o);
-    if ((lane & 15) == 0) ssq[(size_t)m * nslot + (d >> 4)] = ss;
+  const int ngrp = D >> 3;
+  for (int g0 = 0; g0 < ngrp; g0 += PT * blockDim.x) {
+    float v[PT][8], gg[PT][8];
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int gi = g0 + q * blockDim.x + threadIdx.x;
+      if (gi < ngrp) {
+        if (rsrc)
+          load8<float>(rsrc + gi * 8, v[q]);
+        else
+          load8<T>(src + gi * 8, v[q]);
+        load8<T>(g + gi * 8, gg[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < PT; ++q) {
+      const int gi = g0 + q * blockDim.x + threadIdx.x;
+      // partner thread (gi ^ 1) holds the other half of the 16-feature slot;
+      // ngrp is even and pairs never straddle the bound
+      float ss = 0.f, un[8];
+      if (gi < ngrp) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ss += v[q][i] * v[q][i];
+          un[i] = v[q][i] * gg[q][i];
+        }
+      }
+      ss += __shfl_xor(ss, 1);
+      if (gi < ngrp) {
+        store8<float>(x + (size_t)m * D + gi * 8, v[q]);
+        store8<T>(u + (size_t)m * D + gi * 8, un);
+        if ((gi & 1) == 0) ssq[(size_t)m * nslot + (gi >> 1)] = ss;
+      }
+    }
   }
 }
 

@@ -14,7 +14,8 @@ seeded synthetic data.  The same line carries the bs 1 Qwen3-8B-shaped step
 blocks/s x B.
 
 `roofline` reports the kernel with the largest time share, timed live with HIP
-events recorded by the library on the launch stream during the timed steps;
+events recorded by the library on the launch stream over a second pass of the
+timed steps (the step time itself comes from an uninstrumented pass);
 its achieved rate is the kernel's algorithmic bytes (HBM-bound kernels) or
 flops (MFMA-bound) per launch divided by its mean launch time.
 `cpu_baseline` times the float64 CPU oracle on one request of the same
@@ -253,12 +254,14 @@ class Workbench:
         return {k: (ms / steps, cnt // steps) for k, (ms, cnt) in res.items()}
 
     def timed(self, steps, warmup, kind):
+        """Step time over `steps` uninstrumented steps, then (kind given) the
+        mean duration of that kernel kind from the library's HIP events around
+        each of its launches over a second pass of the same `steps` steps.  The
+        passes are separate because an event pair around a launch idles the GPU
+        for a few microseconds, which would inflate the step time."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
-        torch.cuda.synchronize()
-        if kind:
-            self.dr.profile_enable([kind], 64 * (steps + 1))
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -272,6 +275,10 @@ class Workbench:
         ms = start.elapsed_time(stop) / steps
         kern = None
         if kind:
+            self.dr.profile_enable([kind], 64 * (steps + 1))
+            for _ in range(steps):
+                self.step()
+            torch.cuda.synchronize()
             res = self.dr.profile_read()
             self.dr.profile_enable([], 0)
             tot, cnt = res.get(kind, (0.0, 0))

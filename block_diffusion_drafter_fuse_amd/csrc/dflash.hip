@@ -94,6 +94,7 @@ struct TileCfg {
   static constexpr int kFeatPerWave = BN / WN;  // features of one wave's fragment row
 };
 using TileStd = TileCfg<128, 128, 2, 4, 3>;   // general
+using TileS192 = TileCfg<128, 192, 4, 2, 3>;  // general, 32 x 96 per wave, where it fills the CUs better
 using TileWide = TileCfg<256, 256, 2, 4, 2>;  // many tokens against a wide weight (and the LM head)
 using TileW192 = TileCfg<256, 192, 4, 2, 2>;  // same, 64 x 96 per wave, where it fills the CUs better
 // Relative time of one work-group tile (measured on the 512 x 24576 x 4096
@@ -323,6 +324,15 @@ bool plan_rs(const WOperand<T>& w, const AOperand<T>& a, int mt, RsPlan* out) {
   return best >= 0;
 }
 
+// Work-group tile area per CU slot, summed over whole waves of one work-group
+// per CU, for a tile shape with the split-K rule of launch_tiled.
+template <class C>
+long tiled_cost(int M, int ngroups, int nst) {
+  const int tiles = ceil_div(M, C::BM) * ceil_div(ngroups, C::BN / 16);
+  const int SK = std::max(1, std::min(kTiledSlots / tiles, nst / 8));
+  return (long)ceil_div(tiles * SK, kTiledSlots) * C::BM * C::BN / SK;
+}
+
 template <typename T, bool ALO = false, class Epi>
 void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
                  hipStream_t st) {
@@ -388,8 +398,13 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
     else
       launch_tiled<TileWide, T, false>(c, w, a, nrm, epi, st);
   }
-  else
-    launch_tiled<TileStd, T, false>(c, w, a, nrm, epi, st);
+  else {
+    const int nst = K * (int)sizeof(T) / 128;
+    if (tiled_cost<TileS192>(a.M, w.ngroups, nst) < tiled_cost<TileStd>(a.M, w.ngroups, nst))
+      launch_tiled<TileS192, T, false>(c, w, a, nrm, epi, st);
+    else
+      launch_tiled<TileStd, T, false>(c, w, a, nrm, epi, st);
+  }
 }
 
 template <typename T>

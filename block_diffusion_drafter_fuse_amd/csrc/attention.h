@@ -257,8 +257,7 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
             mx = fmaxf(mx, sv[p][t][ii]);
           }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(xor16_max(mx));
     // The reference maximum of a query column moves only when a score exceeds
     // it by more than kAttnSlack (log2 units): probabilities are then at most
     // 2^kAttnSlack, and l and O, which share the reference, are rescaled
@@ -285,9 +284,7 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
           sv[p][t][ii] = __builtin_amdgcn_exp2f(sv[p][t][ii] - mrow);
           ps += sv[p][t][ii];
         }
-    ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
-    lrow += ps;
+    lrow += xor32_sum(xor16_sum(ps));
 #pragma unroll
     for (int p = 0; p < PVS; ++p) {
       const int kb0 = p * KS;

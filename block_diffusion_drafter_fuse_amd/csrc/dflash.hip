@@ -48,11 +48,11 @@ int fail(int code, const std::string& msg) {
 constexpr size_t kAlign = 256;
 constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
 constexpr int kAttnWorkMax = 4096;     // attention split work items per call
-constexpr int kAttnTargetWG = 2048;    // attention work-groups aimed for
+constexpr int kAttnTargetWG = 512;     // attention work-groups aimed for
 constexpr int kAttnMinChunk = 128;     // minimum context keys per split
 constexpr int kAttnNbuf = 2;           // attention K/V ring depth
-constexpr int kAttnStg = 64;           // attention keys per stage
-constexpr int kAttnWpe = 1;            // attention waves per SIMD the registers must allow
+constexpr int kAttnStg = 32;           // attention keys per stage
+constexpr int kAttnWpe = 4;            // attention waves per SIMD the registers must allow
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
 constexpr int kNarrowMaxGroups = 64;   // weights of at most 1024 rows also take the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
@@ -527,7 +527,10 @@ void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
   constexpr int NIW = AttnStage<T, HD, QF, 2, STG>::NIW;
   constexpr int NBUF = std::min(kAttnNbuf, 2 + 63 / NIW);
   const int lds = AttnStage<T, HD, QF, NBUF, STG>::LDS;
-  auto kern = attn_kernel<T, HD, QF, NBUF, STG, kAttnWpe>;
+  // register cap for four work-groups per CU only where the kernel still fits
+  // without spilling much (bf16, head dim 128, four query fragments)
+  constexpr int WPE = std::is_same<T, bf16_t>::value && HD == 128 && QF == 4 ? kAttnWpe : 1;
+  auto kern = attn_kernel<T, HD, QF, NBUF, STG, WPE>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);

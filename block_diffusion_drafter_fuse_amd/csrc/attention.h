@@ -56,7 +56,7 @@ struct AttnArgs {
   AttnMeta meta;
 };
 
-template <typename T, int HD, int QF, int NBUF, int STG>
+template <typename T, int HD, int NWV, int NBUF, int STG>
 struct AttnStage {
   static_assert(STG % kVTile == 0 && kAttnStage % STG == 0, "stages of whole V^T tiles");
   static constexpr int KRB = HD * (int)sizeof(T);      // K row bytes
@@ -67,9 +67,9 @@ struct AttnStage {
   static constexpr int BUF = KBYTES + VBYTES;
   static constexpr int KI = KBYTES / 1024;  // copy instructions (1 KB each) per stage
   static constexpr int VI = VBYTES / 1024;
-  static constexpr int NIW = (KI + VI) / QF;  // per wave
+  static constexpr int NIW = (KI + VI) / NWV;  // per wave
   static constexpr int LDS = NBUF * BUF;
-  static_assert((KI + VI) % QF == 0 && KI % QF == 0, "copy blocks split evenly over the waves");
+  static_assert((KI + VI) % NWV == 0 && KI % NWV == 0, "copy blocks split evenly over the waves");
 };
 
 // LDS swizzles.  A 16-byte fragment read is served 16 lanes (256 bytes) per
@@ -101,13 +101,16 @@ __device__ __forceinline__ int attn_vswz(int row) {
   return VCH >= 8 ? ((row >> 1) & 7) : ((row >> 2) & 3);
 }
 
-// WPE: waves per SIMD the register allocation must allow (the kernel is
-// bound by how many work-groups a CU holds: each one's stage waits and its
-// dependent S -> softmax -> P.V chain are hidden by the others).
-template <typename T, int HD, int QF, int NBUF, int STG, int WPE>
-__global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a) {
+// QW: query fragments (16 query rows each) per wave; the QF/QW waves share
+// the stage copies, and every K or V^T fragment a wave reads from LDS feeds QW
+// MFMAs (the LDS reads per key fall by QW).  WPE: waves per SIMD the register
+// allocation must allow.
+template <typename T, int HD, int QF, int QW, int NBUF, int STG, int WPE>
+__global__ __launch_bounds__(64 * (QF / QW), WPE) void attn_kernel(const AttnArgs<T> a) {
   using MM = Mma<T>;
-  using SG = AttnStage<T, HD, QF, NBUF, STG>;
+  constexpr int NWV = QF / QW;
+  static_assert(QF % QW == 0, "whole query fragments per wave");
+  using SG = AttnStage<T, HD, NWV, NBUF, STG>;
   constexpr int KS = MM::KSTEP;  // keys per P.V step
   constexpr int EPL = MM::EPL;
   constexpr int NT = KS / 16;    // S^T tiles per P.V step
@@ -132,15 +135,17 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
   const int qd = a.Hq * HD, kd = a.Hkv * HD;
   const int GB = a.G * a.B;
 
-  // Query fragment of this wave (B operand: columns = query rows).
-  uint4 qf[HS];
-  {
-    const int qi = f * 16 + r16;
+  // Query fragments of this wave (B operands: columns = query rows);
+  // fragment q covers query rows 16 (f QW + q) ...
+  uint4 qf[QW][HS];
+#pragma unroll
+  for (int q = 0; q < QW; ++q) {
+    const int qi = (f * QW + q) * 16 + r16;
     const bool valid = qi < GB;
     const int hl = valid ? qi / a.B : 0, j = valid ? qi - hl * a.B : 0;
     const T* qp = a.q + (size_t)(r * a.B + j) * qd + (size_t)(g * a.G + hl) * HD + kg * EPL;
 #pragma unroll
-    for (int h = 0; h < HS; ++h) qf[h] = valid ? ld16(qp + h * KS) : make_uint4(0, 0, 0, 0);
+    for (int h = 0; h < HS; ++h) qf[q][h] = valid ? ld16(qp + h * KS) : make_uint4(0, 0, 0, 0);
   }
   // Padding loads after the query fragments: the compiler waits for a
   // fragment with a count of the loads it issued after it; the padding keeps
@@ -166,7 +171,7 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
   const T* bkb = a.kb + (size_t)(r * a.B) * kd + (size_t)g * HD;
   const T* bvt = a.vbT + (size_t)(r * a.Hkv + g) * HD * a.BP;
 
-  // Copy of stage i into buffer b: instruction j = f + QF*ii covers K rows
+  // Copy of stage i into buffer b: instruction j = f + NWV*ii covers K rows
   // (j < KI) or V^T rows; each lane one 16-byte chunk of one row.
   auto issue = [&](int i, int b) {
     const bool blk = i >= nctx;
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
     char* base = lds + b * SG::BUF;
 #pragma unroll
     for (int ii = 0; ii < SG::NIW; ++ii) {
-      const int j = f + QF * ii;
+      const int j = f + NWV * ii;
       if (j < SG::KI) {
         constexpr int RPI = 1024 / SG::KRB;
         const int row = j * RPI + lane / KCH;
@@ -194,10 +199,17 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
     }
   };
 
-  f32x4_t o[DF];
+  f32x4_t o[QW][DF];
 #pragma unroll
-  for (int d = 0; d < DF; ++d) o[d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrow = -INFINITY, lrow = 0.f;
+  for (int q = 0; q < QW; ++q)
+#pragma unroll
+    for (int d = 0; d < DF; ++d) o[q][d] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrow[QW], lrow[QW];
+#pragma unroll
+  for (int q = 0; q < QW; ++q) {
+    mrow[q] = -INFINITY;
+    lrow[q] = 0.f;
+  }
 
 #pragma unroll
   for (int p = 0; p < NBUF - 1; ++p)
@@ -217,13 +229,11 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
     const int klim = blk ? a.B : kend - (kbeg + i * STG);  // valid keys in this stage
     const char* kl = lds + buf * SG::BUF;
     const char* vl = kl + SG::KBYTES;
-    // S^T for every key of the stage first (the P.V steps' MFMA chains
-    // interleave), then one online-softmax update for the whole stage.
-    float sv[PVS][NT][4];
-    float mx = -INFINITY;
-    // (no branch on the valid key count here: the PVS*NT independent MFMA
-    // chains must sit in one block to interleave; masked keys are cheap)
-    f32x4_t cs[PVS][NT];
+    // S^T for every key of the stage first (the MFMA chains interleave; one K
+    // fragment read feeds the QW query fragments), then one online-softmax
+    // update per query column for the whole stage.  No branch on the valid
+    // key count here: masked keys are cheap.
+    f32x4_t cs[QW][PVS][NT];
 #pragma unroll
     for (int h = 0; h < HS; ++h)
 #pragma unroll
@@ -233,71 +243,82 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
           const int krow = p * KS + (r16 >> 2) * (4 * NT) + 4 * t + (r16 & 3);
           const uint4 kf =
               *reinterpret_cast<const uint4*>(kl + krow * SG::KRB + (((h * 4 + kg) ^ attn_kswz<NT, KCH>(krow)) << 4));
-          cs[p][t] = MM::step(kf, qf[h], h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : cs[p][t]);
+#pragma unroll
+          for (int q = 0; q < QW; ++q)
+            cs[q][p][t] = MM::step(kf, qf[q][h], h == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : cs[q][p][t]);
         }
-    if (klim >= STG) {  // full stage: no key to mask
+    float sv[QW][PVS][NT][4];
+#pragma unroll
+    for (int q = 0; q < QW; ++q) {
+      float mx = -INFINITY;
+      if (klim >= STG) {  // full stage: no key to mask
+#pragma unroll
+        for (int p = 0; p < PVS; ++p)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              sv[q][p][t][ii] = cs[q][p][t][ii] * a.scale_log2;
+              mx = fmaxf(mx, sv[q][p][t][ii]);
+            }
+      } else {
+#pragma unroll
+        for (int p = 0; p < PVS; ++p)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+              const int key = p * KS + kg * (4 * NT) + 4 * t + ii;
+              sv[q][p][t][ii] = key < klim ? cs[q][p][t][ii] * a.scale_log2 : -INFINITY;
+              mx = fmaxf(mx, sv[q][p][t][ii]);
+            }
+      }
+      mx = xor32_max(xor16_max(mx));
+      // The reference maximum of a query column moves only when a score
+      // exceeds it by more than kAttnSlack (log2 units): probabilities are
+      // then at most 2^kAttnSlack, and l and O, which share the reference,
+      // are rescaled together, so the result is unchanged in exact
+      // arithmetic.  The rescale of O is skipped when no column of the wave
+      // moves (the common case once the first keys have been seen).
+      const bool mv = mx > mrow[q] + kAttnSlack;
+      if (__any(mv)) {
+        const float mnew = mv ? mx : mrow[q];  // finite: every stage holds a valid key
+        const float alpha = __builtin_amdgcn_exp2f(mrow[q] - mnew);
+        lrow[q] *= alpha;
+        mrow[q] = mnew;
+#pragma unroll
+        for (int d = 0; d < DF; ++d) o[q][d] *= alpha;
+      }
+      float ps = 0.f;
 #pragma unroll
       for (int p = 0; p < PVS; ++p)
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int ii = 0; ii < 4; ++ii) {
-            sv[p][t][ii] = cs[p][t][ii] * a.scale_log2;
-            mx = fmaxf(mx, sv[p][t][ii]);
+            // hardware exp2: arguments are <= kAttnSlack; results below 2^-126
+            // flush to zero, far below the weight of any contributing key
+            sv[q][p][t][ii] = __builtin_amdgcn_exp2f(sv[q][p][t][ii] - mrow[q]);
+            ps += sv[q][p][t][ii];
           }
-    } else {
-#pragma unroll
-      for (int p = 0; p < PVS; ++p)
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int key = p * KS + kg * (4 * NT) + 4 * t + ii;
-            sv[p][t][ii] = key < klim ? cs[p][t][ii] * a.scale_log2 : -INFINITY;
-            mx = fmaxf(mx, sv[p][t][ii]);
-          }
+      lrow[q] += xor32_sum(xor16_sum(ps));
     }
-    mx = xor32_max(xor16_max(mx));
-    // The reference maximum of a query column moves only when a score exceeds
-    // it by more than kAttnSlack (log2 units): probabilities are then at most
-    // 2^kAttnSlack, and l and O, which share the reference, are rescaled
-    // together, so the result is unchanged in exact arithmetic.  The rescale
-    // of O is skipped when no column of the wave moves (the common case once
-    // the first keys have been seen).
-    if (__any(mx > mrow + kAttnSlack)) {
-      const float mnew = mx > mrow + kAttnSlack ? mx : mrow;  // finite: every stage holds a valid key
-      const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
-      lrow *= alpha;
-      mrow = mnew;
-#pragma unroll
-      for (int d = 0; d < DF; ++d) o[d] *= alpha;
-    }
-    float ps = 0.f;
-#pragma unroll
-    for (int p = 0; p < PVS; ++p)
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          // hardware exp2: arguments are <= kAttnSlack; results below 2^-126
-          // flush to zero, far below the weight of any contributing key
-          sv[p][t][ii] = __builtin_amdgcn_exp2f(sv[p][t][ii] - mrow);
-          ps += sv[p][t][ii];
-        }
-    lrow += xor32_sum(xor16_sum(ps));
 #pragma unroll
     for (int p = 0; p < PVS; ++p) {
       const int kb0 = p * KS;
       if (kb0 >= klim) break;
-      uint4 pp;
-      if constexpr (NT == 1) {
-        pp = make_uint4(__float_as_uint(sv[p][0][0]), __float_as_uint(sv[p][0][1]), __float_as_uint(sv[p][0][2]),
-                        __float_as_uint(sv[p][0][3]));
-      } else {
-        pp.x = (uint32_t)f2bf(sv[p][0][0]) | ((uint32_t)f2bf(sv[p][0][1]) << 16);
-        pp.y = (uint32_t)f2bf(sv[p][0][2]) | ((uint32_t)f2bf(sv[p][0][3]) << 16);
-        pp.z = (uint32_t)f2bf(sv[p][1][0]) | ((uint32_t)f2bf(sv[p][1][1]) << 16);
-        pp.w = (uint32_t)f2bf(sv[p][1][2]) | ((uint32_t)f2bf(sv[p][1][3]) << 16);
+      uint4 pp[QW];
+#pragma unroll
+      for (int q = 0; q < QW; ++q) {
+        if constexpr (NT == 1) {
+          pp[q] = make_uint4(__float_as_uint(sv[q][p][0][0]), __float_as_uint(sv[q][p][0][1]),
+                             __float_as_uint(sv[q][p][0][2]), __float_as_uint(sv[q][p][0][3]));
+        } else {
+          pp[q].x = (uint32_t)f2bf(sv[q][p][0][0]) | ((uint32_t)f2bf(sv[q][p][0][1]) << 16);
+          pp[q].y = (uint32_t)f2bf(sv[q][p][0][2]) | ((uint32_t)f2bf(sv[q][p][0][3]) << 16);
+          pp[q].z = (uint32_t)f2bf(sv[q][p][1][0]) | ((uint32_t)f2bf(sv[q][p][1][1]) << 16);
+          pp[q].w = (uint32_t)f2bf(sv[q][p][1][2]) | ((uint32_t)f2bf(sv[q][p][1][3]) << 16);
+        }
       }
       const int vkey = kb0 + kg * 4 * NT;  // first of this lane's keys
       const char* vt = vl + (vkey / kVTile) * SG::TILEB;
@@ -306,7 +327,8 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
       for (int d = 0; d < DF; ++d) {
         const int vrow = d * 16 + r16;
         const uint4 vf = *reinterpret_cast<const uint4*>(vt + vrow * SG::VRB + ((vchunk ^ attn_vswz<VCH>(vrow)) << 4));
-        o[d] = MM::step(vf, pp, o[d]);
+#pragma unroll
+        for (int q = 0; q < QW; ++q) o[q][d] = MM::step(vf, pp[q], o[q][d]);
       }
     }
     buf = buf + 1 == NBUF ? 0 : buf + 1;
@@ -320,13 +342,16 @@ __global__ __launch_bounds__(64 * QF, WPE) void attn_kernel(const AttnArgs<T> a)
   }
   float* po = a.part_o + (size_t)w * QR * HD;
   float* pml = a.part_ml + (size_t)w * QR * 2;
-  const int qrow = f * 16 + r16;
 #pragma unroll
-  for (int d = 0; d < DF; ++d)
-    *reinterpret_cast<f32x4_t*>(po + (size_t)qrow * HD + d * 16 + 4 * kg) = o[d];
-  if (kg == 0) {
-    pml[qrow * 2] = mrow;
-    pml[qrow * 2 + 1] = lrow;
+  for (int q = 0; q < QW; ++q) {
+    const int qrow = (f * QW + q) * 16 + r16;
+#pragma unroll
+    for (int d = 0; d < DF; ++d)
+      *reinterpret_cast<f32x4_t*>(po + (size_t)qrow * HD + d * 16 + 4 * kg) = o[q][d];
+    if (kg == 0) {
+      pml[qrow * 2] = mrow[q];
+      pml[qrow * 2 + 1] = lrow[q];
+    }
   }
 }
 

@@ -53,6 +53,7 @@ constexpr int kAttnMinChunk = 128;     // minimum context keys per split
 constexpr int kAttnNbuf = 2;           // attention K/V ring depth
 constexpr int kAttnStg = 32;           // attention keys per stage
 constexpr int kAttnWpe = 4;            // attention waves per SIMD the registers must allow
+constexpr int kAttnQw = 1;             // attention query fragments per wave
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
 constexpr int kNarrowMaxGroups = 64;   // weights of at most 1024 rows also take the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
@@ -521,22 +522,23 @@ void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
     else go(attn_combine_kernel<T, HD, QF * 16, 1>, 1);
     return;
   }
-  // Two work-groups per CU, each with a ring of NBUF stages of K/V (fewer
-  // where a stage takes many copy instructions per wave).
+  // A ring of NBUF stages of K/V per work-group (fewer where a stage takes
+  // many copy instructions per wave); QW query fragments per wave.
   constexpr int STG = kAttnStg;
-  constexpr int NIW = AttnStage<T, HD, QF, 2, STG>::NIW;
+  constexpr int QW = QF % kAttnQw == 0 ? kAttnQw : 1;
+  constexpr int NIW = AttnStage<T, HD, QF / QW, 2, STG>::NIW;
   constexpr int NBUF = std::min(kAttnNbuf, 2 + 63 / NIW);
-  const int lds = AttnStage<T, HD, QF, NBUF, STG>::LDS;
+  const int lds = AttnStage<T, HD, QF / QW, NBUF, STG>::LDS;
   // register cap for four work-groups per CU only where the kernel still fits
   // without spilling much (bf16, head dim 128, four query fragments)
   constexpr int WPE = std::is_same<T, bf16_t>::value && HD == 128 && QF == 4 ? kAttnWpe : 1;
-  auto kern = attn_kernel<T, HD, QF, NBUF, STG, WPE>;
+  auto kern = attn_kernel<T, HD, QF, QW, NBUF, STG, WPE>;
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     attr_set = true;
   }
-  hipLaunchKernelGGL(kern, dim3(work), dim3(64 * QF), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3(work), dim3(64 * (QF / QW)), lds, st, a);
 }
 
 template <typename T>

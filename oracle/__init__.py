@@ -36,6 +36,12 @@ from .dflash2 import (  # noqa: F401
     two_tap_conv,
     walk,
 )
+from .specsample import (  # noqa: F401
+    draft_tokens,
+    philox4x64_10,
+    spec_sample,
+    uniforms,
+)
 from .dflow import (  # noqa: F401
     RelayState,
     block_inputs,

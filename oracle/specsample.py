@@ -1,0 +1,202 @@
+"""Float64 NumPy oracle of lossless speculative sampling at temperature T > 0
+(test infrastructure only).
+
+Sources: "DFlash 投机解码：块扩散草稿与 KV 注入", section 四 (the inference loop
+resamples the rejected position from the target distribution and the last
+position yields the bonus token); "DFlash 2：正确 token 已在候选里，选一条连贯的路就好"
+(the introduction and the selector section: outputs stay lossless through
+rejection sampling, which restores the target distribution; the comparison
+section samples at temperature 1.0).
+
+The pages name the step but do not write it out.  Reading taken: the standard
+rejection rule of speculative sampling.  With drafter distributions q_j over
+the vocabulary for block offsets j = 1..K (K = B-1) and verifier distributions
+p_j for the token after offset j (j = 0..K; p_j is the distribution of the
+token at offset j+1, the same layout as the greedy targets t_j):
+  * the drafted token at offset j is x_j ~ q_j, drawn by the Gumbel-max rule
+    argmax_v (logit_v / T + G_v), G_v standard Gumbel;
+  * walking j = 1..K, x_j is accepted when r_j * q_j(x_j) < p_{j-1}(x_j),
+    r_j ~ U(0, 1), i.e. with probability min(1, p/q);
+  * at the first rejection j the emitted token is drawn from the residual
+    norm(max(0, p_{j-1} - q_j)) and the block stops; when all K are accepted
+    the bonus token is drawn from p_K;
+  * tau = accepted + 1 (the replacement or bonus token counts, as in the
+    greedy scan).
+Distributions are softmax(logits / T) for both models at the same temperature
+(no top-p / top-k truncation).  Ties of a Gumbel argmax go to the lower id.
+
+Random numbers come from one counter-based generator, Philox4x64-10 (Salmon,
+Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011;
+the generator behind numpy.random.Philox), with key (seed, stream) and counter
+(v // 4, row, request, 0); word v % 4 of the output block is the 64-bit draw
+for index v, mapped to the uniform ((x >> 40) + 0.5) * 2^-24 in (0, 1).
+Streams: 0 drafted tokens (row = offset - 1), 1 acceptance draws (row 0,
+index = offset - 1), 2 the replacement / bonus draw (row 0, index = token id).
+"""
+from __future__ import annotations
+
+from typing import Dict
+
+import numpy as np
+
+_M32 = np.uint64(0xFFFFFFFF)
+_S32 = np.uint64(32)
+PHILOX_M = (np.uint64(0xD2E7470EE14C6C93), np.uint64(0xCA5A826395121157))
+PHILOX_W = (np.uint64(0x9E3779B97F4A7C15), np.uint64(0xBB67AE8584CAA73B))
+
+STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL = 0, 1, 2
+
+
+def _mulhilo64(a, b):
+    """(high, low) 64-bit halves of the 128-bit product of uint64 arrays."""
+    al, ah = a & _M32, a >> _S32
+    bl, bh = b & _M32, b >> _S32
+    ll, lh, hl, hh = al * bl, al * bh, ah * bl, ah * bh
+    mid = (ll >> _S32) + (lh & _M32) + (hl & _M32)
+    lo = (ll & _M32) | ((mid & _M32) << _S32)
+    hi = hh + (lh >> _S32) + (hl >> _S32) + (mid >> _S32)
+    return hi, lo
+
+
+def philox4x64_10(ctr: np.ndarray, key: np.ndarray) -> np.ndarray:
+    """Philox4x64 with 10 rounds: ctr [..., 4], key [..., 2] (uint64) -> [..., 4]
+    uint64.  Each round forms the 128-bit products of words 0 and 2 with the two
+    round multipliers, mixes their high halves with words 1 and 3 and the key,
+    and bumps the key by the two Weyl constants."""
+    c = [np.asarray(ctr[..., i], dtype=np.uint64) for i in range(4)]
+    k0 = np.asarray(key[..., 0], dtype=np.uint64)
+    k1 = np.asarray(key[..., 1], dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        for rnd in range(10):
+            hi0, lo0 = _mulhilo64(PHILOX_M[0], c[0])
+            hi1, lo1 = _mulhilo64(PHILOX_M[1], c[2])
+            c = [hi1 ^ c[1] ^ k0, lo1, hi0 ^ c[3] ^ k1, lo0]
+            if rnd < 9:
+                k0 = k0 + PHILOX_W[0]
+                k1 = k1 + PHILOX_W[1]
+    return np.stack(c, axis=-1)
+
+
+def uniforms(seed: int, stream: int, req: int, row: int, n: int) -> np.ndarray:
+    """n uniforms in (0, 1) (float64, 24-bit resolution) for indices 0..n-1 of
+    (seed, stream, request, row)."""
+    blocks = (n + 3) // 4
+    ctr = np.zeros((blocks, 4), dtype=np.uint64)
+    ctr[:, 0] = np.arange(blocks, dtype=np.uint64)
+    ctr[:, 1] = row
+    ctr[:, 2] = req
+    key = np.broadcast_to(np.array([seed, stream], dtype=np.uint64), (blocks, 2))
+    x = philox4x64_10(ctr, key).reshape(-1)[:n]
+    return ((x >> np.uint64(40)).astype(np.float64) + 0.5) * 2.0 ** -24
+
+
+def gumbel(u: np.ndarray) -> np.ndarray:
+    """Standard Gumbel draws from uniforms in (0, 1)."""
+    return -np.log(-np.log(u))
+
+
+def softmax(logits: np.ndarray, temp: float) -> np.ndarray:
+    z = np.asarray(logits, dtype=np.float64) / float(temp)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def argmax_low(v: np.ndarray) -> int:
+    """Index of the maximum, the lowest index among equal maxima."""
+    return int(np.flatnonzero(v == v.max())[0])
+
+
+# The three decisions of the rejection rule (module level, one place each).
+def verifier_row(j: int) -> int:
+    """Row of the verifier logits that scores the token drafted at offset j
+    (1-based): the verifier's distribution after offset j - 1."""
+    return j - 1
+
+
+def accepts(r: float, q_x: float, p_x: float) -> bool:
+    """Keep the drafted token x when r * q(x) < p(x) (probability min(1, p/q))."""
+    return r * q_x < p_x
+
+
+def residual(p_row: np.ndarray, q_row: np.ndarray) -> np.ndarray:
+    """Unnormalised replacement distribution after a rejection: max(0, p - q)."""
+    return np.maximum(p_row - q_row, 0.0)
+
+
+def draft_tokens(draft_logits: np.ndarray, temp: float, seed: int, req: int) -> np.ndarray:
+    """x_j ~ softmax(l_j / T) by the Gumbel-max rule, one row per drafted
+    offset j (row j - 1 of the generator counter)."""
+    K, V = draft_logits.shape
+    out = np.zeros(K, dtype=np.int64)
+    for j in range(K):
+        g = gumbel(uniforms(seed, STREAM_DRAFT, req, j, V))
+        out[j] = argmax_low(np.asarray(draft_logits[j], dtype=np.float64) / temp + g)
+    return out
+
+
+def spec_sample(draft_logits: np.ndarray, target_logits: np.ndarray, cand: np.ndarray, temp: float,
+                seed: int, req: int) -> Dict[str, object]:
+    """One block of speculative sampling for one request.
+
+    draft_logits [K, V] (offsets 1..K), target_logits [K+1, V] (row j = the
+    verifier's logits after offset j), cand [K] the drafted tokens.  Returns the
+    emitted tokens (accepted candidates, then the replacement or bonus token),
+    tau and the number accepted."""
+    q = softmax(draft_logits, temp)
+    p = softmax(target_logits, temp)
+    K, V = q.shape
+    r = uniforms(seed, STREAM_ACCEPT, req, 0, K)
+    n = 0
+    while n < K:
+        x = int(cand[n])
+        if accepts(r[n], q[n, x], p[verifier_row(n + 1), x]):
+            n += 1
+        else:
+            break
+    g = gumbel(uniforms(seed, STREAM_RESIDUAL, req, 0, V))
+    if n < K:
+        w = residual(p[verifier_row(n + 1)], q[n])
+        with np.errstate(divide="ignore"):
+            last = argmax_low(np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf) + g)
+    else:
+        last = argmax_low(np.asarray(target_logits[K], dtype=np.float64) / temp + g)
+    return {"tokens": [int(t) for t in cand[:n]] + [last], "tau": n + 1, "accepted": n}
+
+
+def first_token_distribution(q: np.ndarray, p: np.ndarray, grid: int = 1 << 14) -> np.ndarray:
+    """Distribution of the first emitted token for a block with one drafted
+    token (q over the vocabulary for offset 1, p the verifier's row that
+    scores it), summed over every draft x ~ q and both outcomes of the
+    acceptance draw; the probability of keeping x is the measure of the r in
+    (0, 1) that `accepts` keeps, taken on a midpoint grid of `grid` points
+    (exact up to 1/grid), and a rejected draft is replaced from
+    norm(residual(p, q))."""
+    q = np.asarray(q, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    V = q.shape[0]
+    r = (np.arange(grid) + 0.5) / grid
+    keep = np.array([np.mean(accepts(r, q[x], p[x])) if q[x] > 0 else 0.0 for x in range(V)])
+    w = residual(p, q)
+    resid = w / w.sum() if w.sum() > 0 else np.zeros_like(w)
+    reject = float(np.sum(q * (1.0 - keep)))
+    return q * keep + reject * resid
+
+
+def tau_distribution(q: np.ndarray, p: np.ndarray) -> np.ndarray:
+    """Exact distribution of tau when the drafter's and the verifier's
+    distributions do not depend on the drafted prefix (q [K, V], p [K+1, V]):
+    offset j is accepted with probability beta_j = sum_v min(q_j(v),
+    p_{j-1}(v)), independently, so P(tau = n+1) = prod_{i<=n} beta_i *
+    (1 - beta_{n+1}) and P(tau = K+1) = prod_i beta_i."""
+    q = np.asarray(q, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    K = q.shape[0]
+    beta = np.minimum(q, p[:K]).sum(axis=1)
+    out = np.zeros(K + 1)
+    run = 1.0
+    for n in range(K):
+        out[n] = run * (1.0 - beta[n])
+        run *= beta[n]
+    out[K] = run
+    return out

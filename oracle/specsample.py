@@ -28,10 +28,16 @@ Distributions are softmax(logits / T) for both models at the same temperature
 Random numbers come from one counter-based generator, Philox4x64-10 (Salmon,
 Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011;
 the generator behind numpy.random.Philox), with key (seed, stream) and counter
-(v // 4, row, request, 0); word v % 4 of the output block is the 64-bit draw
-for index v, mapped to the uniform ((x >> 40) + 0.5) * 2^-24 in (0, 1).
-Streams: 0 drafted tokens (row = offset - 1), 1 acceptance draws (row 0,
-index = offset - 1), 2 the replacement / bonus draw (row 0, index = token id).
+(v // 8, row, request, 0).  The output block holds four 64-bit words; index v
+takes word (v % 8) // 2, its high 32-bit half for even v and its low half for
+odd v, and keeps the top 24 bits k of that half: u = (k + 0.5) * 2^-24 in
+(0, 1).  Streams: 0 drafted tokens (row = offset - 1), 1 acceptance draws
+(row 0, index = offset - 1), 2 the replacement / bonus draw (row 0, index =
+token id).
+
+A rejection implies p(x) < q(x) for the drafted x, so the residual has
+positive mass in exact arithmetic; should rounding leave it empty, the
+replacement is drawn from the verifier's row with the same Gumbel draws.
 """
 from __future__ import annotations
 
@@ -79,15 +85,17 @@ def philox4x64_10(ctr: np.ndarray, key: np.ndarray) -> np.ndarray:
 
 def uniforms(seed: int, stream: int, req: int, row: int, n: int) -> np.ndarray:
     """n uniforms in (0, 1) (float64, 24-bit resolution) for indices 0..n-1 of
-    (seed, stream, request, row)."""
-    blocks = (n + 3) // 4
+    (seed, stream, request, row): eight per generator block, one per 32-bit
+    half of its four words (high half first)."""
+    blocks = (n + 7) // 8
     ctr = np.zeros((blocks, 4), dtype=np.uint64)
     ctr[:, 0] = np.arange(blocks, dtype=np.uint64)
     ctr[:, 1] = row
     ctr[:, 2] = req
     key = np.broadcast_to(np.array([seed, stream], dtype=np.uint64), (blocks, 2))
-    x = philox4x64_10(ctr, key).reshape(-1)[:n]
-    return ((x >> np.uint64(40)).astype(np.float64) + 0.5) * 2.0 ** -24
+    x = philox4x64_10(ctr, key)
+    halves = np.stack([x >> _S32, x & _M32], axis=-1).reshape(-1)[:n]
+    return ((halves >> np.uint64(8)).astype(np.float64) + 0.5) * 2.0 ** -24
 
 
 def gumbel(u: np.ndarray) -> np.ndarray:
@@ -155,12 +163,13 @@ def spec_sample(draft_logits: np.ndarray, target_logits: np.ndarray, cand: np.nd
         else:
             break
     g = gumbel(uniforms(seed, STREAM_RESIDUAL, req, 0, V))
-    if n < K:
-        w = residual(p[verifier_row(n + 1)], q[n])
+    row = verifier_row(n + 1) if n < K else K
+    w = residual(p[row], q[n]) if n < K else np.zeros(V)
+    if np.any(w > 0):
         with np.errstate(divide="ignore"):
             last = argmax_low(np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf) + g)
-    else:
-        last = argmax_low(np.asarray(target_logits[K], dtype=np.float64) / temp + g)
+    else:  # the bonus token, or an empty residual (rounding only)
+        last = argmax_low(np.asarray(target_logits[row], dtype=np.float64) / temp + g)
     return {"tokens": [int(t) for t in cand[:n]] + [last], "tau": n + 1, "accepted": n}
 
 

@@ -43,6 +43,22 @@ def test_philox_matches_numpy_philox():
         assert [int(x) for x in got] == want
 
 
+def test_uniform_layout_against_numpy_philox():
+    # indices 8..15 of (seed, stream, req, row) come from counter block
+    # (1, row, req, 0): numpy started at (0, row, req, 0) produces it first;
+    # index 8 + 2w + h takes the top 24 bits of half h (0 = high) of word w
+    seed, stream, req, row = 99, 2, 5, 3
+    bg = np.random.Philox(counter=np.array([0, row, req, 0], dtype=np.uint64),
+                          key=np.array([seed, stream], dtype=np.uint64))
+    words = [int(x) for x in bg.random_raw(4)]
+    want = []
+    for w in words:
+        for half in (w >> 32, w & 0xFFFFFFFF):
+            want.append(((half >> 8) + 0.5) / 2 ** 24)
+    got = ss.uniforms(seed, stream, req, row, 16)[8:]
+    assert list(got) == want
+
+
 def test_uniforms_open_interval_24_bit():
     u = ss.uniforms(7, 1, 3, 2, 10001)
     assert u.shape == (10001,)

@@ -22,12 +22,12 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",
 EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fuse_ctx",
             "dflash_draft_block", "dflash_accept", "dflash_slot_reset", "dflash_slot_len",
             "dflash_read_cache", "dflow_relay", "dflow_read_relay", "dflash2_select", "dflash2_conv_attach",
-            "dflash_profile_enable",
+            "dflash_spec_draft", "dflash_spec_verify", "dflash_profile_enable",
             "dflash_profile_read", "dflash_strerror", "dflash_last_error")
 
 KERNEL_KINDS = ("fuse_gemm", "fuse_norm", "ctx_kv_gemm", "embed", "norm", "qkv_gemm", "attention",
                 "attn_combine", "o_gemm", "gateup_gemm", "down_gemm", "lm_head", "topk_merge", "relay", "select", "conv",
-                "accept")
+                "spec_draft", "spec_stats", "spec_resample", "accept")
 
 
 class DflashError(RuntimeError):
@@ -103,6 +103,9 @@ def lib() -> ctypes.CDLL:
     L.dflow_read_relay.argtypes = [vp, vp, i32, vp, P(i32)]
     L.dflash2_select.argtypes = [vp, vp, i32, vp, vp, vp, i32, P(dflash2_selector_weights), vp, vp]
     L.dflash2_conv_attach.argtypes = [vp, P(dflash2_conv_layer)]
+    u64, f32 = ctypes.c_uint64, ctypes.c_float
+    L.dflash_spec_draft.argtypes = [vp, vp, i32, vp, f32, u64, vp, vp]
+    L.dflash_spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, f32, u64, vp, vp, vp]
     L.dflash_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
     L.dflash_profile_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.dflash_strerror.argtypes = [ctypes.c_int]
@@ -267,6 +270,20 @@ class Drafter:
                 setattr(arr[l], s, dflash2_conv_site(_ptr(layers[l][s]["w"]), _ptr(layers[l][s]["kbase"])))
         _check(lib().dflash2_conv_attach(self.h, arr), "dflash2_conv_attach")
         self._conv = (layers, arr)
+
+    def spec_draft(self, n_req: int, draft_logits, temperature: float, seed: int, req_id, cand, stream=None):
+        """dflash_spec_draft: Gumbel-max drafting from draft_logits [n_req, B-1, V]
+        float (device) into cand [n_req, B-1] int32."""
+        _check(lib().dflash_spec_draft(self.h, _stream(stream), int(n_req), _ptr(draft_logits), float(temperature),
+                                       int(seed), _ptr(req_id), _ptr(cand)), "dflash_spec_draft")
+
+    def spec_verify(self, n_req: int, draft_logits, target_logits, cand, temperature: float, seed: int, req_id,
+                    tokens, tau, stream=None):
+        """dflash_spec_verify: rejection-rule verification of one block per
+        request; tokens [n_req, B] and tau [n_req] int32 (device) out."""
+        _check(lib().dflash_spec_verify(self.h, _stream(stream), int(n_req), _ptr(draft_logits), _ptr(target_logits),
+                                        _ptr(cand), float(temperature), int(seed), _ptr(req_id), _ptr(tokens),
+                                        _ptr(tau)), "dflash_spec_verify")
 
     def read_relay(self, slot: int, out, stream=None) -> int:
         n = ctypes.c_int32()

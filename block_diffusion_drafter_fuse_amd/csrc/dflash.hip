@@ -33,6 +33,7 @@
 #include "gemv_stream.h"
 #include "lmhead.h"
 #include "misc.h"
+#include "specsample.h"
 
 using namespace dfl;
 
@@ -81,7 +82,9 @@ struct Plan {
   // workspace
   size_t x_off, u_off, ssq_off, q_off, kb_off, vbt_off, o_off, h_off;
   size_t po_off, pml_off, lmv_off, lmi_off, hc_off, hclo_off, fssq_off, part_off, ctr_off;
-  size_t rin_off, rlnh_off, rs_off, sel_off, cv_off, ob_off, zc_off, ws_bytes;
+  size_t rin_off, rlnh_off, rs_off, sel_off, cv_off, ob_off, zc_off;
+  size_t ss_part_off, ss_lse_off, ss_nacc_off, ss_rctr_off, ss_qctr_off, ws_bytes;
+  int ss_nchunk;  // vocabulary chunks of the sampling kernels
   int relay_rows;  // relay rows one call can hold: max_batch * (B - 2)
   int BP;
   size_t lm_entries;
@@ -206,6 +209,15 @@ void make_plan(const dflash_dims* d, Plan* p) {
   p->cv_off = off;   off = align_up(off + (size_t)M * d->D * e);
   p->ob_off = off;   off = align_up(off + (size_t)M * d->D * e);
   p->zc_off = off;   off = align_up(off + (size_t)M * (d->D / 8) * 4);
+  // speculative sampling: per-chunk partials of up to 2B-1 rows per request,
+  // row log-sum-exps, accepted counts, row and request tickets
+  const int ss_rows = d->max_batch * (2 * d->B - 1);
+  p->ss_nchunk = ceil_div(d->V, kSsChunk);
+  p->ss_part_off = off; off = align_up(off + (size_t)ss_rows * p->ss_nchunk * 16);
+  p->ss_lse_off = off;  off = align_up(off + (size_t)ss_rows * 4);
+  p->ss_nacc_off = off; off = align_up(off + (size_t)d->max_batch * 4);
+  p->ss_rctr_off = off; off = align_up(off + (size_t)ss_rows * 4);
+  p->ss_qctr_off = off; off = align_up(off + (size_t)d->max_batch * 4);
   p->ws_bytes = off;
 }
 
@@ -1194,6 +1206,96 @@ int dflash2_conv_attach(dflash_ctx* ctx, const dflash2_conv_layer* layers) {
       if (!x->w || !x->kbase) return fail(DFLASH_EINVAL, "convolution tensors must not be NULL");
   }
   ctx->conv.assign(layers, layers + ctx->d.N);
+  return DFLASH_OK;
+}
+
+namespace {
+
+// Shared checks of the two sampling calls; fills the workspace view and the
+// scale factors.
+int spec_prep(dflash_ctx* ctx, int32_t n_req, float temperature, const int32_t* req_id, SsWork* w, float* invT,
+              float* s2) {
+  if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
+  if (n_req < 0) return fail(DFLASH_EINVAL, "n_req must be >= 0");
+  if (n_req > ctx->d.max_batch) return fail(DFLASH_ECAPACITY, "n_req exceeds max_batch");
+  if (!(temperature >= 1e-4f && temperature <= 1e4f))
+    return fail(DFLASH_EINVAL, "temperature must be in [1e-4, 1e4]");
+  if (n_req > 0 && !req_id) return fail(DFLASH_EINVAL, "req_id is NULL");
+  const Plan& p = ctx->p;
+  w->part = ctx->wsp<float4>(p.ss_part_off);
+  w->lse = ctx->wsp<float>(p.ss_lse_off);
+  w->nacc = ctx->wsp<int>(p.ss_nacc_off);
+  w->row_ctr = ctx->wsp<int>(p.ss_rctr_off);
+  w->req_ctr = ctx->wsp<int>(p.ss_qctr_off);
+  *invT = (float)(1.0 / (double)temperature);
+  *s2 = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
+  return DFLASH_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits, float temperature,
+                      uint64_t seed, const int32_t* req_id, int32_t* cand) {
+  g_last_error.clear();
+  SsWork w;
+  float invT, s2;
+  int rc = spec_prep(ctx, n_req, temperature, req_id, &w, &invT, &s2);
+  if (rc) return rc;
+  if (n_req == 0) return DFLASH_OK;
+  if (!draft_logits || !cand) return fail(DFLASH_EINVAL, "NULL argument");
+  const int V = ctx->d.V, K = ctx->d.B - 1, nch = ctx->p.ss_nchunk;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  {
+    ProfScope ps(ctx, DFLASH_K_SPEC_DRAFT, st);
+    const dim3 grid(nch, n_req * K);
+    if (V % 4 == 0 && aligned16(draft_logits))
+      hipLaunchKernelGGL(ss_draft_kernel<true>, grid, dim3(kSsThreads), 0, st, draft_logits, V, K, nch, invT, seed,
+                         req_id, w, cand);
+    else
+      hipLaunchKernelGGL(ss_draft_kernel<false>, grid, dim3(kSsThreads), 0, st, draft_logits, V, K, nch, invT, seed,
+                         req_id, w, cand);
+  }
+  if (!hip_ok(hipGetLastError(), "spec_draft launch", &rc)) return rc;
+  return DFLASH_OK;
+}
+
+int dflash_spec_verify(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits,
+                       const float* target_logits, const int32_t* cand, float temperature, uint64_t seed,
+                       const int32_t* req_id, int32_t* tokens, int32_t* tau) {
+  g_last_error.clear();
+  SsWork w;
+  float invT, s2;
+  int rc = spec_prep(ctx, n_req, temperature, req_id, &w, &invT, &s2);
+  if (rc) return rc;
+  if (n_req == 0) return DFLASH_OK;
+  if (!draft_logits || !target_logits || !cand || !tokens || !tau) return fail(DFLASH_EINVAL, "NULL argument");
+  const int V = ctx->d.V, K = ctx->d.B - 1, nch = ctx->p.ss_nchunk;
+  const bool vec = V % 4 == 0 && aligned16(draft_logits) && aligned16(target_logits);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  {
+    ProfScope ps(ctx, DFLASH_K_SPEC_STATS, st);
+    const dim3 grid(nch, n_req * (2 * K + 1));
+    if (vec)
+      hipLaunchKernelGGL(ss_stats_kernel<true>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, cand, V, K,
+                         nch, s2, seed, req_id, w, tokens);
+    else
+      hipLaunchKernelGGL(ss_stats_kernel<false>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, cand, V,
+                         K, nch, s2, seed, req_id, w, tokens);
+  }
+  if (!hip_ok(hipGetLastError(), "spec_verify stats launch", &rc)) return rc;
+  {
+    ProfScope ps(ctx, DFLASH_K_SPEC_RESAMPLE, st);
+    const dim3 grid(nch, n_req);
+    if (vec)
+      hipLaunchKernelGGL(ss_resample_kernel<true>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, V, K,
+                         nch, invT, s2, seed, req_id, w, tokens, tau);
+    else
+      hipLaunchKernelGGL(ss_resample_kernel<false>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, V, K,
+                         nch, invT, s2, seed, req_id, w, tokens, tau);
+  }
+  if (!hip_ok(hipGetLastError(), "spec_verify resample launch", &rc)) return rc;
   return DFLASH_OK;
 }
 

@@ -300,6 +300,54 @@ typedef struct dflash2_conv_layer {
  * device work, takes effect from the next draft. */
 int dflash2_conv_attach(dflash_ctx* ctx, const dflash2_conv_layer* layers);
 
+/* Speculative sampling at temperature T > 0 (lossless rejection sampling:
+ * "DFlash 2：正确 token 已在候选里", introduction and selector section, where
+ * outputs stay lossless because rejection sampling restores the verifier's
+ * distribution; "DFlash 投机解码：块扩散草稿与 KV 注入", section 四, where the
+ * rejected position is redrawn and the last position yields the bonus token).
+ * Both models' distributions are softmax(logits / T), untruncated.  K = B - 1.
+ *
+ * Random numbers come from Philox4x64-10 (Salmon et al., SC 2011) with key
+ * (seed, stream) and counter (v / 8, row, req_id[r], 0); entry v takes the top
+ * 24 bits k of the high (v even) or low (v odd) 32-bit half of output word
+ * (v % 8) / 2, as u = (k + 0.5) 2^-24.  Streams: 0 drafting (row = offset - 1,
+ * v = token id), 1 acceptance (row 0, v = offset - 1), 2 replacement / bonus
+ * (row 0, v = token id).  A caller advances `seed` per block so that blocks
+ * draw afresh; req_id tells requests of one call apart.
+ *
+ * Both calls use the ctx workspace (calls sharing a ctx must be ordered on one
+ * stream) and leave slot state untouched.  temperature must lie in
+ * [1e-4, 1e4] (EINVAL); n_req <= max_batch (ECAPACITY).  Logit rows must hold
+ * at least one finite value.  All pointers are device pointers. */
+
+/* Draft by Gumbel-max: cand[r][j-1] = argmax_v (draft_logits[r][j-1][v] / T
+ * + G_v), G_v = -log(-log u_v) from stream 0, ties to the lower id, so that
+ * cand[r][j-1] ~ softmax(draft_logits[r][j-1] / T).
+ *   draft_logits [n_req, B-1, V] float (e.g. out_logits of dflash_draft_block)
+ *   req_id [n_req] int32 >= 0
+ *   cand [n_req, B-1] int32 out */
+int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits, float temperature,
+                      uint64_t seed, const int32_t* req_id, int32_t* cand);
+
+/* Verify one block per request by the rejection rule of speculative sampling.
+ * q_j = softmax(draft_logits[r][j-1] / T) drafted offset j = 1..K;
+ * p_j = softmax(target_logits[r][j] / T) is the verifier's distribution of the
+ * token after offset j (j = 0: after the anchor).  Walking j = 1..K, x_j =
+ * cand[r][j-1] is kept when u_j q_j(x_j) < p_{j-1}(x_j) (u_j from stream 1,
+ * the test taken in double from fp32 probabilities); an id outside 0..V-1 is
+ * rejected.  At the first rejection j the emitted token is argmax_v
+ * (log max(0, p_{j-1}(v) - q_j(v)) + G_v); when all K are kept it is argmax_v
+ * (target_logits[r][K][v] / T + G_v) (G from stream 2; a residual that
+ * rounding leaves empty falls back to the verifier row's l / T + G).
+ *   draft_logits [n_req, B-1, V] float, target_logits [n_req, B, V] float
+ *   cand [n_req, B-1] int32, req_id [n_req] int32 >= 0
+ *   tokens [n_req, B] int32 out: the n kept candidates, then the emitted
+ *          token at index n, then -1
+ *   tau [n_req] int32 out: n + 1 */
+int dflash_spec_verify(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits,
+                       const float* target_logits, const int32_t* cand, float temperature, uint64_t seed,
+                       const int32_t* req_id, int32_t* tokens, int32_t* tau);
+
 /* Kernel kinds, for per-kernel timing. */
 enum dflash_kernel_kind {
   DFLASH_K_FUSE_GEMM = 0,   /* context fusion GEMM W_c [H^(l1);...] */
@@ -318,6 +366,9 @@ enum dflash_kernel_kind {
   DFLASH_K_RELAY,           /* DFlow relay: assembly and the relay MLP GEMMs */
   DFLASH_K_SELECT,          /* DFlash 2 selector: gate GEMM, pair scores and walk */
   DFLASH_K_CONV,            /* DFlash 2 two-tap convolution: tap-correction GEMM and the tap mix */
+  DFLASH_K_SPEC_DRAFT,      /* speculative sampling: Gumbel-max drafting */
+  DFLASH_K_SPEC_STATS,      /* speculative sampling: row log-sum-exps and the acceptance scan */
+  DFLASH_K_SPEC_RESAMPLE,   /* speculative sampling: replacement / bonus draw */
   DFLASH_K_ACCEPT,          /* acceptance scan (stateless call: never timed) */
   DFLASH_K_COUNT
 };

@@ -1,9 +1,9 @@
 """Seeded synthetic inputs for the DFlash draft step.
 
-This package draws weights, verifier hidden states, anchors and target tokens
-from fixed seeds, and converts them to the storage dtype.  It holds none of the
-method's arithmetic: both the CPU oracle (tests only) and the HIP path receive
-exactly the arrays produced here.
+This package draws weights, verifier hidden states, anchors, target tokens and
+the logit rows of the sampling stage from fixed seeds, and converts them to the
+storage dtype.  It holds none of the method's arithmetic: both the CPU oracle
+(tests only) and the HIP path receive exactly the arrays produced here.
 """
 from .configs import CONFIGS, Dims, Workload, get_config  # noqa: F401
 from .gen import (  # noqa: F401
@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     make_conv_weights,
     make_hidden,
     make_relay_weights,
+    make_sampling_logits,
     make_selector_weights,
     make_suffix_hidden,
     make_targets,

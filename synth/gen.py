@@ -270,3 +270,34 @@ def make_targets(cand: np.ndarray, m: np.ndarray, V: int, seed: int) -> np.ndarr
         if mr < B - 1:
             t[r, mr] = (int(cand[r, mr]) + 1 + int(shift[r])) % V
     return t.astype(np.int32)
+
+
+def make_sampling_logits(bs: int, B: int, V: int, seed: int, peaks: int = 4):
+    """Drafter and verifier logit rows for speculative sampling at T > 0.
+
+    Verifier row j (0..B-1) of request r is peaked: 2 N(0, 1) over the whole
+    vocabulary plus U(6, 12) on `peaks` random ids.  Drafter row j (offset j,
+    1..B-1) scores the same position as verifier row j-1: that row plus
+    sigma_r N(0, 1) on every entry, sigma_r ~ U(0.3, 1.5) per request, and with
+    probability 0.2 its peaks moved to other random ids (a wrong draft), so
+    acceptance varies across offsets and requests.  Returns float32 arrays
+    draft [bs, B-1, V] and target [bs, B, V]."""
+    K = B - 1
+    draft = np.empty((bs, K, V), dtype=np.float32)
+    target = np.empty((bs, B, V), dtype=np.float32)
+    for r in range(bs):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([4000 + seed, r])))
+        sigma = rng.uniform(0.3, 1.5)
+        for j in range(B):
+            row = 2.0 * rng.standard_normal(V)
+            ids = rng.choice(V, size=min(peaks, V), replace=False)
+            row[ids] += rng.uniform(6.0, 12.0, size=ids.size)
+            target[r, j] = row
+            if j < K:
+                d = row + sigma * rng.standard_normal(V)
+                if rng.random() < 0.2:
+                    moved = rng.choice(V, size=ids.size, replace=False)
+                    d[moved] += rng.uniform(6.0, 12.0, size=ids.size)
+                    d[ids] -= row[ids] - 2.0 * rng.standard_normal(ids.size)
+                draft[r, j] = d
+    return draft, target

@@ -442,6 +442,84 @@ def measure_select(wl, w_dev, torch, steps, warmup):
                     "the draft's top-16 LM head is not included"}
 
 
+def measure_spec(wl, w_dev, torch, steps, warmup, temperature=1.0):
+    """Speculative sampling at T > 0 on the workload's batch and vocabulary:
+    dflash_spec_draft over the drafter's B-1 rows and dflash_spec_verify over
+    those rows and the verifier's B rows per request.  The logit rows are
+    seeded synthetic inputs (synth.make_sampling_logits), resident in HBM.  The
+    draft call hands the drafter rows' log-sum-exps to the verify call, which
+    then reads only the verifier rows in full.  The calls are timed with events
+    over `steps` calls each, and each kernel kind with the library's events on
+    a second pass."""
+    import block_diffusion_drafter_fuse_amd as dfa
+    import synth
+    d, bs, B = wl.dims, wl.bs, wl.dims.B
+    K, V = B - 1, d.V
+    dl, tl = synth.make_sampling_logits(bs, B, V, wl.seed)
+    dlg = torch.from_numpy(dl).cuda()
+    tlg = torch.from_numpy(tl).cuda()
+    del dl, tl
+    dr = dfa.Drafter(d, w_dev, 64, bs, bs)
+    req = torch.arange(bs, dtype=torch.int32, device="cuda")
+    cand = torch.zeros((bs, K), dtype=torch.int32, device="cuda")
+    dlse = torch.zeros((bs, K), dtype=torch.float32, device="cuda")
+    tokens = torch.zeros((bs, B), dtype=torch.int32, device="cuda")
+    tau = torch.zeros(bs, dtype=torch.int32, device="cuda")
+
+    def draft(i):
+        dr.spec_draft(bs, dlg, temperature, 1000 + i, req, cand, dlse)
+
+    def verify(i):
+        dr.spec_verify(bs, dlg, tlg, cand, temperature, 2000 + i, req, tokens, tau, dlse)
+
+    def clock(fn):
+        for i in range(warmup):
+            fn(i)
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        for i in range(steps):
+            fn(i)
+        stop.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / steps
+
+    draft(0)
+    ms_draft = clock(draft)
+    ms_verify = clock(verify)
+    dr.profile_enable(["spec_draft", "spec_stats", "spec_resample"], 8 * (steps + 1))
+    for i in range(steps):
+        draft(i)
+        verify(i)
+    torch.cuda.synchronize()
+    res = dr.profile_read()
+    dr.profile_enable([], 0)
+    taus = tau.cpu().numpy()
+    rej = int((taus <= K).sum())
+    row = V * 4
+    byts = {"spec_draft": bs * K * row + bs * (K * 8 + 4),
+            "spec_stats": bs * (K + 1) * row + bs * K * (4 + 4 + 8),
+            "spec_resample": (bs + rej) * row + bs * (B * 4 + 4)}
+    kernels = {}
+    for k, b in byts.items():
+        tot, cnt = res.get(k, (0.0, 0))
+        us = tot / max(cnt, 1) * 1e3
+        gbs = b / (us * 1e-6) / 1e9 if us > 0 else None
+        kernels[k] = {"us_per_launch": round(us, 2), "algorithmic_bytes": b,
+                      "achieved_GBs": None if gbs is None else round(gbs, 1),
+                      "hbm_roof_frac": None if gbs is None else round(gbs / HBM_PEAK_GBS, 4)}
+    dr.close()
+    del dr, dlg, tlg
+    torch.cuda.synchronize()
+    return {"workload": f"{d.name} speculative sampling, bs {bs}, V {V}, B {B}, T {temperature}",
+            "draft_ms_per_call": round(ms_draft, 4), "verify_ms_per_call": round(ms_verify, 4),
+            "mean_tau": round(float(taus.mean()), 3), "kernels": kernels,
+            "note": "fp32 logit rows resident in HBM; bytes count each logit row read once "
+                    "(draft: the drafter rows; stats: the verifier rows; resample: the verifier row, "
+                    "plus the drafter row where a draft was rejected)"}
+
+
 def cpu_baseline(wl, w_np, budget_s=20.0):
     """The float64 oracle, as it stands, on one request of the workload (the
     one with the shortest context): fuse its new rows, draft its block, accept.
@@ -488,7 +566,8 @@ def main():
     ap.add_argument("--companion", default="qwen3_8b_bs1", help="second workload reported under 'bs1' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-relay", action="store_true",
-                    help="skip the DFlow relay and the DFlash 2 selector and convolution measurements")
+                    help="skip the DFlow relay, DFlash 2 selector and convolution, and speculative sampling "
+                         "measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy one buffer of this many MiB (reference dispatch for byte counters)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -541,12 +620,14 @@ def main():
         assert wc.dims == wl.dims, "companion must share the model shape"
         print(f"[bench] measuring {args.companion}", file=sys.stderr, flush=True)
         comp = measure(wc, w_dev, torch, args.steps, args.warmup, args.companion)
-    relay = select = None
+    relay = select = spec = None
     if not args.no_relay:
         print(f"[bench] measuring the DFlow relay at {args.workload}", file=sys.stderr, flush=True)
         relay = measure_relay(wl, w_dev, torch, args.steps, args.warmup)
         print(f"[bench] measuring the DFlash 2 selector at {args.workload}", file=sys.stderr, flush=True)
         select = measure_select(wl, w_dev, torch, args.steps, args.warmup)
+        print(f"[bench] measuring speculative sampling at {args.workload}", file=sys.stderr, flush=True)
+        spec = measure_spec(wl, w_dev, torch, args.steps, args.warmup)
     if args.copy_probe_mib:
         n = args.copy_probe_mib << 20
         src = torch.full((n,), 7, dtype=torch.uint8, device="cuda")
@@ -591,6 +672,8 @@ def main():
         line["conv"] = main_res["conv"]
     if select:
         line["select"] = select
+    if spec:
+        line["spec_sampling"] = spec
     print(json.dumps(line), flush=True)
 
 

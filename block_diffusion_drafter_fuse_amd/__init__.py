@@ -104,8 +104,8 @@ def lib() -> ctypes.CDLL:
     L.dflash2_select.argtypes = [vp, vp, i32, vp, vp, vp, i32, P(dflash2_selector_weights), vp, vp]
     L.dflash2_conv_attach.argtypes = [vp, P(dflash2_conv_layer)]
     u64, f32 = ctypes.c_uint64, ctypes.c_float
-    L.dflash_spec_draft.argtypes = [vp, vp, i32, vp, f32, u64, vp, vp]
-    L.dflash_spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, f32, u64, vp, vp, vp]
+    L.dflash_spec_draft.argtypes = [vp, vp, i32, vp, f32, u64, vp, vp, vp]
+    L.dflash_spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, f32, u64, vp, vp, vp]
     L.dflash_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
     L.dflash_profile_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.dflash_strerror.argtypes = [ctypes.c_int]
@@ -271,19 +271,21 @@ class Drafter:
         _check(lib().dflash2_conv_attach(self.h, arr), "dflash2_conv_attach")
         self._conv = (layers, arr)
 
-    def spec_draft(self, n_req: int, draft_logits, temperature: float, seed: int, req_id, cand, stream=None):
+    def spec_draft(self, n_req: int, draft_logits, temperature: float, seed: int, req_id, cand, draft_lse=None,
+                   stream=None):
         """dflash_spec_draft: Gumbel-max drafting from draft_logits [n_req, B-1, V]
-        float (device) into cand [n_req, B-1] int32."""
+        float (device) into cand [n_req, B-1] int32; optionally the rows'
+        base-2 log-sum-exps into draft_lse [n_req, B-1] float."""
         _check(lib().dflash_spec_draft(self.h, _stream(stream), int(n_req), _ptr(draft_logits), float(temperature),
-                                       int(seed), _ptr(req_id), _ptr(cand)), "dflash_spec_draft")
+                                       int(seed), _ptr(req_id), _ptr(cand), _ptr(draft_lse)), "dflash_spec_draft")
 
     def spec_verify(self, n_req: int, draft_logits, target_logits, cand, temperature: float, seed: int, req_id,
-                    tokens, tau, stream=None):
+                    tokens, tau, draft_lse=None, stream=None):
         """dflash_spec_verify: rejection-rule verification of one block per
         request; tokens [n_req, B] and tau [n_req] int32 (device) out."""
         _check(lib().dflash_spec_verify(self.h, _stream(stream), int(n_req), _ptr(draft_logits), _ptr(target_logits),
-                                        _ptr(cand), float(temperature), int(seed), _ptr(req_id), _ptr(tokens),
-                                        _ptr(tau)), "dflash_spec_verify")
+                                        _ptr(cand), _ptr(draft_lse), float(temperature), int(seed), _ptr(req_id),
+                                        _ptr(tokens), _ptr(tau)), "dflash_spec_verify")
 
     def read_relay(self, slot: int, out, stream=None) -> int:
         n = ctypes.c_int32()

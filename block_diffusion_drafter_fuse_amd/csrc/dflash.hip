@@ -212,7 +212,7 @@ void make_plan(const dflash_dims* d, Plan* p) {
   // speculative sampling: per-chunk partials of up to 2B-1 rows per request,
   // row log-sum-exps, accepted counts, row and request tickets
   const int ss_rows = d->max_batch * (2 * d->B - 1);
-  p->ss_nchunk = ceil_div(d->V, kSsChunk);
+  p->ss_nchunk = ceil_div(d->V, kSsThreads * kSsPerResampleFew);  // the most chunks a launch uses
   p->ss_part_off = off; off = align_up(off + (size_t)ss_rows * p->ss_nchunk * 16);
   p->ss_lse_off = off;  off = align_up(off + (size_t)ss_rows * 4);
   p->ss_nacc_off = off; off = align_up(off + (size_t)d->max_batch * 4);
@@ -1213,8 +1213,7 @@ namespace {
 
 // Shared checks of the two sampling calls; fills the workspace view and the
 // scale factors.
-int spec_prep(dflash_ctx* ctx, int32_t n_req, float temperature, const int32_t* req_id, SsWork* w, float* invT,
-              float* s2) {
+int spec_prep(dflash_ctx* ctx, int32_t n_req, float temperature, const int32_t* req_id, SsWork* w, float* s2) {
   if (!ctx) return fail(DFLASH_EINVAL, "ctx is NULL");
   if (n_req < 0) return fail(DFLASH_EINVAL, "n_req must be >= 0");
   if (n_req > ctx->d.max_batch) return fail(DFLASH_ECAPACITY, "n_req exceeds max_batch");
@@ -1227,73 +1226,79 @@ int spec_prep(dflash_ctx* ctx, int32_t n_req, float temperature, const int32_t* 
   w->nacc = ctx->wsp<int>(p.ss_nacc_off);
   w->row_ctr = ctx->wsp<int>(p.ss_rctr_off);
   w->req_ctr = ctx->wsp<int>(p.ss_qctr_off);
-  *invT = (float)(1.0 / (double)temperature);
   *s2 = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
   return DFLASH_OK;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
+int ss_nchunk(int V, int per) { return ceil_div(V, kSsThreads * per); }
+
+// Element loads where a row is not 16-byte aligned.
+#define SS_LAUNCH(KERNEL, PER, VEC, GRID, ST, ...)                                             \
+  do {                                                                                       \
+    if (VEC)                                                                                 \
+      hipLaunchKernelGGL((KERNEL<true, PER>), GRID, dim3(kSsThreads), 0, ST, __VA_ARGS__);   \
+    else                                                                                     \
+      hipLaunchKernelGGL((KERNEL<false, PER>), GRID, dim3(kSsThreads), 0, ST, __VA_ARGS__);  \
+  } while (0)
+
 }  // namespace
 
 int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits, float temperature,
-                      uint64_t seed, const int32_t* req_id, int32_t* cand) {
+                      uint64_t seed, const int32_t* req_id, int32_t* cand, float* draft_lse) {
   g_last_error.clear();
   SsWork w;
-  float invT, s2;
-  int rc = spec_prep(ctx, n_req, temperature, req_id, &w, &invT, &s2);
+  float s2;
+  int rc = spec_prep(ctx, n_req, temperature, req_id, &w, &s2);
   if (rc) return rc;
   if (n_req == 0) return DFLASH_OK;
   if (!draft_logits || !cand) return fail(DFLASH_EINVAL, "NULL argument");
-  const int V = ctx->d.V, K = ctx->d.B - 1, nch = ctx->p.ss_nchunk;
+  const int V = ctx->d.V, K = ctx->d.B - 1;
+  const bool vec = V % 4 == 0 && aligned16(draft_logits);
+  const int nch = ss_nchunk(V, kSsPerDraft);
   hipStream_t st = static_cast<hipStream_t>(stream);
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_DRAFT, st);
-    const dim3 grid(nch, n_req * K);
-    if (V % 4 == 0 && aligned16(draft_logits))
-      hipLaunchKernelGGL(ss_draft_kernel<true>, grid, dim3(kSsThreads), 0, st, draft_logits, V, K, nch, invT, seed,
-                         req_id, w, cand);
-    else
-      hipLaunchKernelGGL(ss_draft_kernel<false>, grid, dim3(kSsThreads), 0, st, draft_logits, V, K, nch, invT, seed,
-                         req_id, w, cand);
+    SS_LAUNCH(ss_draft_kernel, kSsPerDraft, vec, dim3(nch, n_req * K), st, draft_logits, V, K, nch, s2, seed, req_id,
+              w, cand, draft_lse);
   }
   if (!hip_ok(hipGetLastError(), "spec_draft launch", &rc)) return rc;
   return DFLASH_OK;
 }
 
 int dflash_spec_verify(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits,
-                       const float* target_logits, const int32_t* cand, float temperature, uint64_t seed,
-                       const int32_t* req_id, int32_t* tokens, int32_t* tau) {
+                       const float* target_logits, const int32_t* cand, const float* draft_lse, float temperature,
+                       uint64_t seed, const int32_t* req_id, int32_t* tokens, int32_t* tau) {
   g_last_error.clear();
   SsWork w;
-  float invT, s2;
-  int rc = spec_prep(ctx, n_req, temperature, req_id, &w, &invT, &s2);
+  float s2;
+  int rc = spec_prep(ctx, n_req, temperature, req_id, &w, &s2);
   if (rc) return rc;
   if (n_req == 0) return DFLASH_OK;
   if (!draft_logits || !target_logits || !cand || !tokens || !tau) return fail(DFLASH_EINVAL, "NULL argument");
-  const int V = ctx->d.V, K = ctx->d.B - 1, nch = ctx->p.ss_nchunk;
+  const int V = ctx->d.V, K = ctx->d.B - 1;
   const bool vec = V % 4 == 0 && aligned16(draft_logits) && aligned16(target_logits);
+  const int rows = n_req * (draft_lse ? K + 1 : 2 * K + 1);
   hipStream_t st = static_cast<hipStream_t>(stream);
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_STATS, st);
-    const dim3 grid(nch, n_req * (2 * K + 1));
-    if (vec)
-      hipLaunchKernelGGL(ss_stats_kernel<true>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, cand, V, K,
-                         nch, s2, seed, req_id, w, tokens);
-    else
-      hipLaunchKernelGGL(ss_stats_kernel<false>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, cand, V,
-                         K, nch, s2, seed, req_id, w, tokens);
+    const int nch = ss_nchunk(V, kSsPerStats);
+    SS_LAUNCH(ss_stats_kernel, kSsPerStats, vec, dim3(nch, rows), st, draft_logits, target_logits, cand, draft_lse, V,
+              K, nch, s2, seed, req_id, w, tokens);
   }
   if (!hip_ok(hipGetLastError(), "spec_verify stats launch", &rc)) return rc;
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_RESAMPLE, st);
-    const dim3 grid(nch, n_req);
-    if (vec)
-      hipLaunchKernelGGL(ss_resample_kernel<true>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, V, K,
-                         nch, invT, s2, seed, req_id, w, tokens, tau);
-    else
-      hipLaunchKernelGGL(ss_resample_kernel<false>, grid, dim3(kSsThreads), 0, st, draft_logits, target_logits, V, K,
-                         nch, invT, s2, seed, req_id, w, tokens, tau);
+    if (n_req <= 4) {
+      const int nch = ss_nchunk(V, kSsPerResampleFew);
+      SS_LAUNCH(ss_resample_kernel, kSsPerResampleFew, vec, dim3(nch, n_req), st, draft_logits, target_logits,
+                draft_lse, V, K, nch, s2, seed, req_id, w, tokens, tau);
+    } else {
+      const int nch = ss_nchunk(V, kSsPerResample);
+      SS_LAUNCH(ss_resample_kernel, kSsPerResample, vec, dim3(nch, n_req), st, draft_logits, target_logits,
+                draft_lse, V, K, nch, s2, seed, req_id, w, tokens, tau);
+    }
   }
   if (!hip_ok(hipGetLastError(), "spec_verify resample launch", &rc)) return rc;
   return DFLASH_OK;

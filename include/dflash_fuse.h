@@ -325,9 +325,11 @@ int dflash2_conv_attach(dflash_ctx* ctx, const dflash2_conv_layer* layers);
  * cand[r][j-1] ~ softmax(draft_logits[r][j-1] / T).
  *   draft_logits [n_req, B-1, V] float (e.g. out_logits of dflash_draft_block)
  *   req_id [n_req] int32 >= 0
- *   cand [n_req, B-1] int32 out */
+ *   cand [n_req, B-1] int32 out
+ *   draft_lse nullable [n_req, B-1] float out: log2 sum_v 2^(l_v log2(e) / T)
+ *             of each row, for dflash_spec_verify at the same temperature */
 int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits, float temperature,
-                      uint64_t seed, const int32_t* req_id, int32_t* cand);
+                      uint64_t seed, const int32_t* req_id, int32_t* cand, float* draft_lse);
 
 /* Verify one block per request by the rejection rule of speculative sampling.
  * q_j = softmax(draft_logits[r][j-1] / T) drafted offset j = 1..K;
@@ -341,12 +343,15 @@ int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float*
  * rounding leaves empty falls back to the verifier row's l / T + G).
  *   draft_logits [n_req, B-1, V] float, target_logits [n_req, B, V] float
  *   cand [n_req, B-1] int32, req_id [n_req] int32 >= 0
+ *   draft_lse nullable [n_req, B-1] float: the draft_lse of the
+ *             dflash_spec_draft call on these drafter rows at this
+ *             temperature; saves reading every drafter row once more
  *   tokens [n_req, B] int32 out: the n kept candidates, then the emitted
  *          token at index n, then -1
  *   tau [n_req] int32 out: n + 1 */
 int dflash_spec_verify(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits,
-                       const float* target_logits, const int32_t* cand, float temperature, uint64_t seed,
-                       const int32_t* req_id, int32_t* tokens, int32_t* tau);
+                       const float* target_logits, const int32_t* cand, const float* draft_lse, float temperature,
+                       uint64_t seed, const int32_t* req_id, int32_t* tokens, int32_t* tau);
 
 /* Kernel kinds, for per-kernel timing. */
 enum dflash_kernel_kind {

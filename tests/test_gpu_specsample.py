@@ -54,16 +54,19 @@ class Sampler:
         buf[1:] = torch.from_numpy(a.reshape(-1)).cuda()
         return buf[1:].view(a.shape)
 
-    def draft(self, dl, temp, seed, req):
+    def draft(self, dl, temp, seed, req, lse=False):
+        """Drafted ids [n, K]; with lse=True also the rows' log-sum-exps as a
+        device tensor (verify input)."""
         n, K = dl.shape[0], dl.shape[1]
         dlg = self.dev(dl)
         rq = torch.tensor(np.asarray(req, dtype=np.int32), device="cuda")
         cand = torch.full((n, K), -7, dtype=torch.int32, device="cuda")
-        self.dr.spec_draft(n, dlg, temp, seed, rq, cand)
+        dlse = torch.full((n, K), float("nan"), dtype=torch.float32, device="cuda") if lse else None
+        self.dr.spec_draft(n, dlg, temp, seed, rq, cand, dlse)
         torch.cuda.synchronize()
-        return cand.cpu().numpy()
+        return (cand.cpu().numpy(), dlse) if lse else cand.cpu().numpy()
 
-    def verify(self, dl, tl, cand, temp, seed, req):
+    def verify(self, dl, tl, cand, temp, seed, req, dlse=None):
         n, K = dl.shape[0], dl.shape[1]
         dlg = self.dev(dl)
         tlg = self.dev(tl)
@@ -71,7 +74,7 @@ class Sampler:
         rq = torch.tensor(np.asarray(req, dtype=np.int32), device="cuda")
         tokens = torch.full((n, K + 1), -7, dtype=torch.int32, device="cuda")
         tau = torch.full((n,), -7, dtype=torch.int32, device="cuda")
-        self.dr.spec_verify(n, dlg, tlg, cd, temp, seed, rq, tokens, tau)
+        self.dr.spec_verify(n, dlg, tlg, cd, temp, seed, rq, tokens, tau, dlse)
         torch.cuda.synchronize()
         return tokens.cpu().numpy(), tau.cpu().numpy()
 
@@ -109,21 +112,29 @@ def draft_keys(dl_row, temp, seed, req, off):
 
 
 def check_draft(sp, dl, temp, seed, req, rows=None, tally=None):
-    cand = sp.draft(dl, temp, seed, req)
+    """Drafted ids against the oracle's Gumbel keys; also checks the rows'
+    log-sum-exps (base 2, of l log2(e) / T) that the call returns, and hands
+    them back for the verifier."""
+    cand, dlse = sp.draft(dl, temp, seed, req, lse=True)
     n, K, V = dl.shape
+    z = dl.astype(np.float64) / temp
+    zm = z.max(axis=-1, keepdims=True)
+    want = (zm[..., 0] + np.log(np.exp(z - zm).sum(-1))) / np.log(2.0)
+    got = dlse.cpu().numpy()
+    assert np.all(np.abs(got - want) <= 1e-5 * np.maximum(1.0, np.abs(want))), np.abs(got - want).max()
     t = tally or Tally()
     for r in range(n):
         for j in range(K):
             if rows is not None and (r, j) not in rows:
                 continue
             t.choice(int(cand[r, j]), draft_keys(dl[r, j], temp, seed, req[r], j), what=f"draft r{r} j{j + 1}")
-    return cand, t
+    return cand, dlse, t
 
 
-def check_verify(sp, dl, tl, cand, temp, seed, req, reqs=None, tally=None):
+def check_verify(sp, dl, tl, cand, temp, seed, req, reqs=None, tally=None, dlse=None):
     """Compare one verify call with the oracle request by request; returns the
     GPU outputs and the tally."""
-    tokens, tau = sp.verify(dl, tl, cand, temp, seed, req)
+    tokens, tau = sp.verify(dl, tl, cand, temp, seed, req, dlse)
     n, K, V = dl.shape
     t = tally or Tally()
     for r in range(n):
@@ -186,10 +197,12 @@ def test_spec_sampling_parity(name, V, B, bs, temp, mis):
     try:
         dl, tl = synth.make_sampling_logits(bs, B, V, seed=11)
         req = [3 * r + 1 for r in range(bs)]
-        cand_gpu, t = check_draft(sp, dl, temp, 1234, req)
+        _, dlse, t = check_draft(sp, dl, temp, 1234, req)
         cand = np.stack([ss.draft_tokens(dl[r], temp, 1234, req[r]) for r in range(bs)])
         _, tau, t = check_verify(sp, dl, tl, cand, temp, 5678, req, tally=t)
-        log(f"[spec] {name}: tau {list(tau)}, exact {t.exact}/{t.total}")
+        # the same with the drafter rows' log-sum-exps handed over by the draft call
+        _, tau2, t = check_verify(sp, dl, tl, cand, temp, 5678, req, tally=t, dlse=dlse)
+        log(f"[spec] {name}: tau {list(tau)} / {list(tau2)}, exact {t.exact}/{t.total}")
         assert t.rate() >= 0.97
     finally:
         sp.close()
@@ -207,12 +220,33 @@ def test_spec_sampling_full_vocab_bs32():
         req = list(range(bs))
         rng = np.random.default_rng(0)
         rows = {(int(rng.integers(bs)), int(rng.integers(B - 1))) for _ in range(24)}
-        _, t = check_draft(sp, dl, temp, 77, req, rows=rows)
+        _, dlse, t = check_draft(sp, dl, temp, 77, req, rows=rows)
         cand = np.stack([ss.draft_tokens(dl[r], temp, 77, req[r]) for r in range(bs)])
         _, tau, t = check_verify(sp, dl, tl, cand, temp, 78, req, reqs=set(range(0, bs, 4)), tally=t)
+        _, tau2, t = check_verify(sp, dl, tl, cand, temp, 78, req, reqs=set(range(2, bs, 4)), tally=t, dlse=dlse)
         log(f"[spec] full vocabulary: mean tau {tau.mean():.2f}, exact {t.exact}/{t.total}")
         assert t.rate() >= 0.97
         assert tau.min() >= 1 and tau.max() <= B
+    finally:
+        sp.close()
+
+
+def test_spec_sampling_full_vocab_misaligned():
+    """Element loads at the full vocabulary with enough rows for the
+    16384-entry work-groups (16 requests, B 16): sampled rows and requests
+    against the oracle."""
+    V, B, bs, temp = 151936, 16, 16, 0.8
+    log(f"[spec] full vocabulary, misaligned rows: V {V} B {B} bs {bs}")
+    sp = Sampler(V, B, bs, misalign=True)
+    try:
+        dl, tl = synth.make_sampling_logits(bs, B, V, seed=6)
+        req = [100 + r for r in range(bs)]
+        rng = np.random.default_rng(1)
+        rows = {(int(rng.integers(bs)), int(rng.integers(B - 1))) for _ in range(12)}
+        _, dlse, t = check_draft(sp, dl, temp, 31, req, rows=rows)
+        cand = np.stack([ss.draft_tokens(dl[r], temp, 31, req[r]) for r in range(bs)])
+        _, tau, t = check_verify(sp, dl, tl, cand, temp, 32, req, reqs={1, 6, 11}, tally=t, dlse=dlse)
+        assert t.rate() >= 0.97
     finally:
         sp.close()
 
@@ -267,7 +301,7 @@ def test_spec_repeat_and_streams():
         v1 = sp.verify(dl, tl, a, temp, 6, [0, 1, 2, 3])
         v2 = sp.verify(dl, tl, a, temp, 6, [0, 1, 2, 3])
         assert np.array_equal(v1[0], v2[0]) and np.array_equal(v1[1], v2[1])
-        sp.dr.spec_draft(0, None, temp, 1, None, None)
+        sp.dr.spec_draft(0, None, temp, 1, None, None, None)
         with pytest.raises(dfa.DflashError):
             sp.draft(dl, 0.0, 5, [0, 1, 2, 3])
         big = np.zeros((bs + 1, B - 1, V), dtype=np.float32)

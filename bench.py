@@ -10,8 +10,11 @@ host so every step has the same shape.
 Headline workload: Qwen3-8B-shaped drafter, bs 32 ragged (context ~ U{512..8192},
 previous-round tau ~ clamped geometric with mean 6.5), bf16 weights and inputs,
 seeded synthetic data.  The same line carries the bs 1 Qwen3-8B-shaped step
-(context 4096, 7 new tokens) under "bs1".  Metric: drafted tokens/s =
-blocks/s x B.
+(context 4096, 7 new tokens) under "bs1", the bs 1 Qwen3-4B-shaped step
+(context 2048) under "bs1_4b", and context prefill (one fuse call of 2048
+tokens at the 4B shape and of 8192 tokens at the 8B shape) under "prefill".
+Metric: drafted tokens/s = blocks/s x B; the per-step spread (p10/p50/p90)
+comes from an event after every timed step.
 
 `roofline` reports the kernel with the largest time share, timed live with HIP
 events recorded by the library on the launch stream over a second pass of the
@@ -262,17 +265,19 @@ class Workbench:
         torch = self.torch
         for _ in range(warmup):
             self.step()
-        start = torch.cuda.Event(enable_timing=True)
-        stop = torch.cuda.Event(enable_timing=True)
+        # one event after every step (recording an event does not wait), for
+        # the per-step spread as well as the mean
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        start.record()
-        for _ in range(steps):
+        evs[0].record()
+        for i in range(steps):
             self.step()
-        stop.record()
+            evs[i + 1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ms = start.elapsed_time(stop) / steps
+        ms = evs[0].elapsed_time(evs[-1]) / steps
+        self.step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
         kern = None
         if kind:
             self.dr.profile_enable([kind], 64 * (steps + 1))
@@ -328,6 +333,7 @@ def measure(wl, w_dev, torch, steps, warmup, label, conv=False):
         "step_algorithmic_flops": flops,
         "step_hbm_roof_frac": round(byts / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
         "step_mfma_roof_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4),
+        "step_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(wb.step_ms, [10, 50, 90])],
         "breakdown_ms": {k: round(v[0], 4) for k, v in sorted(bd.items(), key=lambda kv: -kv[1][0])},
         "roofline": roof_entry(dom, d, wl, kern[0], traffic_for(dom, label)),
     }
@@ -339,6 +345,41 @@ def measure(wl, w_dev, torch, steps, warmup, label, conv=False):
     del wb
     torch.cuda.synchronize()
     return out
+
+
+def measure_prefill(d, w_dev, torch, n_tok, seed, reps=3):
+    """Context prefill: one dflash_fuse_ctx call that fuses `n_tok` verifier
+    rows of one request (fusion GEMM, RMSNorm and the per-layer context K/V
+    projection into the cache), timed with events over `reps` calls (the slot
+    is rewound between calls).  Above the ridge: reported against the MFMA
+    peak."""
+    import block_diffusion_drafter_fuse_amd as dfa
+    import synth
+    dr = dfa.Drafter(d, w_dev, n_tok + d.B, 1, 1)
+    hid = [dfa.to_device(h) for h in synth.make_hidden(d, seed, 0, 0, n_tok)]
+    dr.fuse_ctx([0], [n_tok], hid)
+    dr.slot_reset(0, 0)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    ms = 0.0
+    for _ in range(reps):
+        start.record()
+        dr.fuse_ctx([0], [n_tok], hid)
+        stop.record()
+        torch.cuda.synchronize()
+        ms += start.elapsed_time(stop)
+        dr.slot_reset(0, 0)
+    ms /= reps
+    e = elt(d)
+    flops = 2.0 * n_tok * (d.D * d.L * d.Dt + d.N * 2 * d.D * d.Hkv * d.hd)
+    byts = e * (d.D * d.L * d.Dt + d.N * 2 * d.D * d.Hkv * d.hd) + n_tok * (d.L * d.Dt + d.N * 2 * d.Hkv * d.hd) * e
+    dr.close()
+    del dr, hid
+    torch.cuda.synchronize()
+    return {"workload": f"{d.name} prefill fuse of {n_tok} tokens", "ms_per_call": round(ms, 4),
+            "tokens_per_s": round(n_tok / (ms * 1e-3), 1), "algorithmic_flops": flops, "algorithmic_bytes": byts,
+            "mfma_roof_frac": round(flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12), 4)}
 
 
 def measure_relay(wl, w_dev, torch, steps, warmup):
@@ -565,6 +606,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_bs32")
     ap.add_argument("--companion", default="qwen3_8b_bs1", help="second workload reported under 'bs1' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-4b", action="store_true",
+                    help="skip the Qwen3-4B-shaped bs1 step and its 2048-token prefill")
     ap.add_argument("--no-relay", action="store_true",
                     help="skip the DFlow relay, DFlash 2 selector and convolution, and speculative sampling "
                          "measurements")
@@ -620,6 +663,18 @@ def main():
         assert wc.dims == wl.dims, "companion must share the model shape"
         print(f"[bench] measuring {args.companion}", file=sys.stderr, flush=True)
         comp = measure(wc, w_dev, torch, args.steps, args.warmup, args.companion)
+    prefill = [measure_prefill(wl.dims, w_dev, torch, 8192, wl.seed)]
+    bs1_4b = None
+    if not args.no_4b:
+        w4 = synth.get_config("qwen3_4b_bs1")
+        print("[bench] measuring qwen3_4b_bs1", file=sys.stderr, flush=True)
+        w4_dev = dfa.Drafter.upload_weights(synth.make_weights(w4.dims, w4.seed))
+        r4 = measure(w4, w4_dev, torch, args.steps, args.warmup, "qwen3_4b_bs1")
+        bs1_4b = {k: r4[k] for k in ("workload", "drafted_tokens_per_s", "blocks_per_s", "ms_per_step",
+                                     "step_ms_p10_p50_p90", "step_hbm_roof_frac", "roofline", "breakdown_ms")}
+        prefill.insert(0, measure_prefill(w4.dims, w4_dev, torch, 2048, w4.seed))
+        del w4_dev
+        torch.cuda.synchronize()
     relay = select = spec = None
     if not args.no_relay:
         print(f"[bench] measuring the DFlow relay at {args.workload}", file=sys.stderr, flush=True)
@@ -660,12 +715,16 @@ def main():
         "roofline": main_res["roofline"],
         "step_hbm_roof_frac": main_res["step_hbm_roof_frac"],
         "step_mfma_roof_frac": main_res["step_mfma_roof_frac"],
+        "step_ms_p10_p50_p90": main_res["step_ms_p10_p50_p90"],
         "breakdown_ms": main_res["breakdown_ms"],
         "cpu_baseline": cpu,
     }
     if comp:
         line["bs1"] = {k: comp[k] for k in ("workload", "drafted_tokens_per_s", "blocks_per_s", "ms_per_step",
-                                            "step_hbm_roof_frac", "roofline", "breakdown_ms")}
+                                            "step_ms_p10_p50_p90", "step_hbm_roof_frac", "roofline", "breakdown_ms")}
+    if bs1_4b:
+        line["bs1_4b"] = bs1_4b
+    line["prefill"] = prefill
     if relay:
         line["relay"] = relay
     if "conv" in main_res:

@@ -304,7 +304,10 @@ void launch_tiled(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, con
 }
 
 // Row-streaming GEMV plan: K ranges and tiles per work-group for about one
-// work-group per CU, fewest stages per work-group (ties: fewer K ranges).
+// work-group per CU, least time per work-group (ties: fewer K ranges).  A
+// tile costs its stages plus a fixed two-stage equivalent (ring fill and
+// drain, the split-K ticket): without it, rows of five 1 KB stages (K = 2560)
+// were split five ways into one-stage tiles, 1.7x slower than whole rows.
 // Returns false where the kernel does not apply (rows not whole 1 KB stages,
 // too many stages for the held activations of a row epilogue, tile sums
 // beyond LDS, or partials beyond the workspace).
@@ -328,7 +331,7 @@ bool plan_rs(const WOperand<T>& w, const AOperand<T>& a, int mt, RsPlan* out) {
     const int lds = gemv_rs_lds(kRsNbuf, red2, tpw);
     if (lds > kRsLdsMax) continue;
     if (ks > 1 && ((long)mt * w.ngroups > kCounters - 64 || (size_t)mt * w.ngroups * ks * 256 > kPartFloats)) continue;
-    const long cost = (long)tpw * nst;
+    const long cost = (long)tpw * (nst + 2);
     if (best < 0 || cost < best) {
       best = cost;
       *out = RsPlan{ceil_div(nst_all, nst), nst, red2, tpw, ceil_div(w.ngroups, tpw), lds};

@@ -606,6 +606,9 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_bs32")
     ap.add_argument("--companion", default="qwen3_8b_bs1", help="second workload reported under 'bs1' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="the draft-step workloads only (implies --no-4b and --no-relay, skips prefill): "
+                         "for kernel traces and counter runs of the step")
     ap.add_argument("--no-4b", action="store_true",
                     help="skip the Qwen3-4B-shaped bs1 step and its 2048-token prefill")
     ap.add_argument("--no-relay", action="store_true",
@@ -617,6 +620,8 @@ def main():
                     help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE, WRITE_SIZE) of a run with --copy-probe-mib; needs no GPU")
     args = ap.parse_args()
+    if args.no_extras:
+        args.no_4b = args.no_relay = True
     if args.traffic_from:
         if not args.copy_probe_mib:
             ap.error("--traffic-from needs the --copy-probe-mib of the profiled run")
@@ -663,7 +668,7 @@ def main():
         assert wc.dims == wl.dims, "companion must share the model shape"
         print(f"[bench] measuring {args.companion}", file=sys.stderr, flush=True)
         comp = measure(wc, w_dev, torch, args.steps, args.warmup, args.companion)
-    prefill = [measure_prefill(wl.dims, w_dev, torch, 8192, wl.seed)]
+    prefill = [] if args.no_extras else [measure_prefill(wl.dims, w_dev, torch, 8192, wl.seed)]
     bs1_4b = None
     if not args.no_4b:
         w4 = synth.get_config("qwen3_4b_bs1")
@@ -724,7 +729,8 @@ def main():
                                             "step_ms_p10_p50_p90", "step_hbm_roof_frac", "roofline", "breakdown_ms")}
     if bs1_4b:
         line["bs1_4b"] = bs1_4b
-    line["prefill"] = prefill
+    if prefill:
+        line["prefill"] = prefill
     if relay:
         line["relay"] = relay
     if "conv" in main_res:

@@ -23,7 +23,16 @@ token at offset j+1, the same layout as the greedy targets t_j):
   * tau = accepted + 1 (the replacement or bonus token counts, as in the
     greedy scan).
 Distributions are softmax(logits / T) for both models at the same temperature
-(no top-p / top-k truncation).  Ties of a Gumbel argmax go to the lower id.
+(no top-p / top-k truncation).
+
+Every categorical draw (the drafted tokens, the replacement, the bonus) is taken
+in two stages, an exact composition: the vocabulary is cut into blocks of
+BLOCK consecutive ids; a block b is chosen by inverse CDF over the block masses
+with one uniform (cum_{b-1} <= u S < cum_b), then an id within b by Gumbel-max
+(argmax of log-weight + Gumbel noise, ties to the lower id), so
+P(v) = (mass_b / S)(w_v / mass_b) = w_v / S.  The pages fix the distribution,
+not the sampling algorithm; this one needs generator output for one block of
+ids per draw instead of the whole vocabulary.
 
 Random numbers come from one counter-based generator, Philox4x64-10 (Salmon,
 Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011;
@@ -31,13 +40,15 @@ the generator behind numpy.random.Philox), with key (seed, stream) and counter
 (v // 8, row, request, 0).  The output block holds four 64-bit words; index v
 takes word (v % 8) // 2, its high 32-bit half for even v and its low half for
 odd v, and keeps the top 24 bits k of that half: u = (k + 0.5) * 2^-24 in
-(0, 1).  Streams: 0 drafted tokens (row = offset - 1), 1 acceptance draws
-(row 0, index = offset - 1), 2 the replacement / bonus draw (row 0, index =
-token id).
+(0, 1).  Streams: 0 drafted tokens, Gumbel noise (row = offset - 1, index =
+token id); 1 acceptance draws (row 0, index = offset - 1); 2 the replacement /
+bonus draw, Gumbel noise (row 0, index = token id); 3 and 4 the block choice
+of the drafted tokens (row = offset - 1) and of the replacement / bonus (row
+0), index 0.
 
 A rejection implies p(x) < q(x) for the drafted x, so the residual has
 positive mass in exact arithmetic; should rounding leave it empty, the
-replacement is drawn from the verifier's row with the same Gumbel draws.
+replacement is drawn from the verifier's row with the same random numbers.
 """
 from __future__ import annotations
 
@@ -50,7 +61,8 @@ _S32 = np.uint64(32)
 PHILOX_M = (np.uint64(0xD2E7470EE14C6C93), np.uint64(0xCA5A826395121157))
 PHILOX_W = (np.uint64(0x9E3779B97F4A7C15), np.uint64(0xBB67AE8584CAA73B))
 
-STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL = 0, 1, 2
+STREAM_DRAFT, STREAM_ACCEPT, STREAM_RESIDUAL, STREAM_DRAFT_BLOCK, STREAM_RESIDUAL_BLOCK = 0, 1, 2, 3, 4
+BLOCK = 16384  # vocabulary ids per block of the two-stage draw
 
 
 def _mulhilo64(a, b):
@@ -132,14 +144,37 @@ def residual(p_row: np.ndarray, q_row: np.ndarray) -> np.ndarray:
     return np.maximum(p_row - q_row, 0.0)
 
 
+def block_choice(weights: np.ndarray, u: float) -> int:
+    """Inverse CDF over the masses of the BLOCK-id blocks of `weights` (>= 0):
+    the block b with cum_{b-1} <= u * S < cum_b."""
+    w = np.asarray(weights, dtype=np.float64)
+    mass = np.add.reduceat(w, np.arange(0, w.size, BLOCK))
+    cum = np.cumsum(mass)
+    return min(int(np.searchsorted(cum, u * cum[-1], side="right")), mass.size - 1)
+
+
+def two_stage_draw(logw: np.ndarray, seed: int, stream_block: int, stream_entry: int, req: int, row: int) -> int:
+    """Id v with probability exp(logw_v) / sum_v exp(logw_v) (logw may hold
+    -inf): a block by block_choice with uniform 0 of stream_block, then the
+    Gumbel-max over that block's ids with the noise of index v from
+    stream_entry."""
+    logw = np.asarray(logw, dtype=np.float64)
+    with np.errstate(under="ignore"):
+        w = np.exp(logw - logw.max())
+    b = block_choice(w, uniforms(seed, stream_block, req, row, 1)[0])
+    lo, hi = b * BLOCK, min(logw.size, (b + 1) * BLOCK)
+    g = gumbel(uniforms(seed, stream_entry, req, row, hi)[lo:])
+    return lo + argmax_low(logw[lo:hi] + g)
+
+
 def draft_tokens(draft_logits: np.ndarray, temp: float, seed: int, req: int) -> np.ndarray:
-    """x_j ~ softmax(l_j / T) by the Gumbel-max rule, one row per drafted
-    offset j (row j - 1 of the generator counter)."""
+    """x_j ~ softmax(l_j / T), one row per drafted offset j (row j - 1 of the
+    generator counters)."""
     K, V = draft_logits.shape
     out = np.zeros(K, dtype=np.int64)
     for j in range(K):
-        g = gumbel(uniforms(seed, STREAM_DRAFT, req, j, V))
-        out[j] = argmax_low(np.asarray(draft_logits[j], dtype=np.float64) / temp + g)
+        out[j] = two_stage_draw(np.asarray(draft_logits[j], dtype=np.float64) / temp, seed, STREAM_DRAFT_BLOCK,
+                                STREAM_DRAFT, req, j)
     return out
 
 
@@ -162,14 +197,14 @@ def spec_sample(draft_logits: np.ndarray, target_logits: np.ndarray, cand: np.nd
             n += 1
         else:
             break
-    g = gumbel(uniforms(seed, STREAM_RESIDUAL, req, 0, V))
     row = verifier_row(n + 1) if n < K else K
     w = residual(p[row], q[n]) if n < K else np.zeros(V)
     if np.any(w > 0):
         with np.errstate(divide="ignore"):
-            last = argmax_low(np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf) + g)
+            logw = np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf)
     else:  # the bonus token, or an empty residual (rounding only)
-        last = argmax_low(np.asarray(target_logits[row], dtype=np.float64) / temp + g)
+        logw = np.asarray(target_logits[row], dtype=np.float64) / temp
+    last = two_stage_draw(logw, seed, STREAM_RESIDUAL_BLOCK, STREAM_RESIDUAL, req, 0)
     return {"tokens": [int(t) for t in cand[:n]] + [last], "tau": n + 1, "accepted": n}
 
 

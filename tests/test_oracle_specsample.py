@@ -5,7 +5,9 @@ temperature T > 0, oracle/specsample.py) against facts fixed outside it:
 * the defining property of the rejection rule: the emitted token has exactly
   the verifier's distribution, whatever the drafter's (closed form, summed
   over every draft and both outcomes), and the sampler reproduces it;
-* the Gumbel-max draw reproduces softmax(l / T);
+* the Gumbel-max draw reproduces softmax(l / T); the block stage of the
+  two-stage draw is an inverse CDF over the block masses (exact on a grid of
+  uniforms) and the composed draw reproduces the weights across blocks;
 * the accepted length follows the product of per-offset acceptance masses
   sum_v min(q, p) (closed form) when the distributions do not depend on the
   prefix;
@@ -174,3 +176,31 @@ def test_replacement_comes_from_the_residual_and_tau_in_range():
             last = out["tokens"][-1]
             assert p[last] > q[last]
     assert seen > 50
+
+
+def test_block_choice_is_the_inverse_cdf_of_the_block_masses():
+    rng = np.random.default_rng(12)
+    V = 3 * ss.BLOCK + 100
+    w = rng.random(V) ** 8
+    w[ss.BLOCK:2 * ss.BLOCK] = 0.0  # an empty block is never chosen
+    mass = np.array([w[b * ss.BLOCK:(b + 1) * ss.BLOCK].sum() for b in range(4)])
+    grid = 1 << 13
+    counts = np.zeros(4)
+    for u in (np.arange(grid) + 0.5) / grid:
+        counts[ss.block_choice(w, u)] += 1
+    assert counts[1] == 0
+    assert np.all(np.abs(counts / grid - mass / mass.sum()) <= 1.0 / grid + 1e-12)
+
+
+def test_two_stage_draw_across_blocks():
+    V = 2 * ss.BLOCK + 7
+    ids = np.array([5, ss.BLOCK - 1, ss.BLOCK, 2 * ss.BLOCK + 6, 123])
+    logw = np.full(V, -np.inf)
+    logw[ids] = np.log([0.3, 0.1, 0.25, 0.15, 0.2])
+    want = np.exp(logw[ids]) / np.exp(logw[ids]).sum()
+    n = 1500
+    cnt = np.zeros(ids.size)
+    for s_ in range(n):
+        v = ss.two_stage_draw(logw, s_, ss.STREAM_DRAFT_BLOCK, ss.STREAM_DRAFT, 0, 0)
+        cnt[int(np.flatnonzero(ids == v)[0])] += 1
+    assert np.all(np.abs(cnt / n - want) <= _mc_bound(want, n))

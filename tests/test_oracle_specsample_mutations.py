@@ -1,7 +1,8 @@
 """Planted mistakes in the speculative-sampling oracle (CPU, monkeypatch) must
 each fail a pin: the acceptance ratio inverted, the replacement drawn from the
 verifier's row instead of the residual, the verifier row shifted by one
-offset, and the Gumbel draw taken with the wrong sign."""
+offset, the Gumbel draw taken with the wrong sign, and the block of the
+two-stage draw chosen without regard to the block masses."""
 import numpy as np
 
 import oracle.specsample as ss
@@ -40,3 +41,11 @@ def test_wrong_gumbel_sign_caught(monkeypatch):
     orig = ss.gumbel
     monkeypatch.setattr(ss, "gumbel", lambda u: -orig(u))
     assert _fails(pins.test_gumbel_draw_matches_softmax)
+
+
+def test_block_choice_ignoring_masses_caught(monkeypatch):
+    def uniform_block(w, u):
+        nb = -(-len(w) // ss.BLOCK)
+        return min(int(u * nb), nb - 1)
+    monkeypatch.setattr(ss, "block_choice", uniform_block)
+    assert _fails(pins.test_two_stage_draw_across_blocks)

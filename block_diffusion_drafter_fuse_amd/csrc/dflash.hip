@@ -83,7 +83,7 @@ struct Plan {
   size_t x_off, u_off, ssq_off, q_off, kb_off, vbt_off, o_off, h_off;
   size_t po_off, pml_off, lmv_off, lmi_off, hc_off, hclo_off, fssq_off, part_off, ctr_off;
   size_t rin_off, rlnh_off, rs_off, sel_off, cv_off, ob_off, zc_off;
-  size_t ss_part_off, ss_lse_off, ss_nacc_off, ss_rctr_off, ss_qctr_off, ws_bytes;
+  size_t ss_part_off, ss_lse_off, ss_nacc_off, ss_rctr_off, ss_qctr_off, ss_blk_off, ws_bytes;
   int ss_nchunk;  // vocabulary chunks of the sampling kernels
   int relay_rows;  // relay rows one call can hold: max_batch * (B - 2)
   int BP;
@@ -212,12 +212,13 @@ void make_plan(const dflash_dims* d, Plan* p) {
   // speculative sampling: per-chunk partials of up to 2B-1 rows per request,
   // row log-sum-exps, accepted counts, row and request tickets
   const int ss_rows = d->max_batch * (2 * d->B - 1);
-  p->ss_nchunk = ceil_div(d->V, kSsThreads * kSsPerResampleFew);  // the most chunks a launch uses
+  p->ss_nchunk = ceil_div(d->V, kSsThreads * 8);  // the most pieces per row (2048-id pieces)
   p->ss_part_off = off; off = align_up(off + (size_t)ss_rows * p->ss_nchunk * 16);
   p->ss_lse_off = off;  off = align_up(off + (size_t)ss_rows * 4);
   p->ss_nacc_off = off; off = align_up(off + (size_t)d->max_batch * 4);
   p->ss_rctr_off = off; off = align_up(off + (size_t)ss_rows * 4);
   p->ss_qctr_off = off; off = align_up(off + (size_t)d->max_batch * 4);
+  p->ss_blk_off = off;  off = align_up(off + (size_t)ss_rows * 4);
   p->ws_bytes = off;
 }
 
@@ -1223,27 +1224,52 @@ int spec_prep(dflash_ctx* ctx, int32_t n_req, float temperature, const int32_t* 
   if (!(temperature >= 1e-4f && temperature <= 1e4f))
     return fail(DFLASH_EINVAL, "temperature must be in [1e-4, 1e4]");
   if (n_req > 0 && !req_id) return fail(DFLASH_EINVAL, "req_id is NULL");
+  if (ceil_div(ctx->d.V, kSsBlock) > kSsMaxBlocks) return fail(DFLASH_EUNSUPPORTED, "sampling needs V <= 1048576");
   const Plan& p = ctx->p;
   w->part = ctx->wsp<float4>(p.ss_part_off);
   w->lse = ctx->wsp<float>(p.ss_lse_off);
   w->nacc = ctx->wsp<int>(p.ss_nacc_off);
   w->row_ctr = ctx->wsp<int>(p.ss_rctr_off);
   w->req_ctr = ctx->wsp<int>(p.ss_qctr_off);
+  w->blk = ctx->wsp<int>(p.ss_blk_off);
   *s2 = (float)(1.4426950408889634 / (double)temperature);  // log2(e) / T
   return DFLASH_OK;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-int ss_nchunk(int V, int per) { return ceil_div(V, kSsThreads * per); }
-
 // Element loads where a row is not 16-byte aligned.
-#define SS_LAUNCH(KERNEL, PER, VEC, GRID, ST, ...)                                             \
-  do {                                                                                       \
-    if (VEC)                                                                                 \
-      hipLaunchKernelGGL((KERNEL<true, PER>), GRID, dim3(kSsThreads), 0, ST, __VA_ARGS__);   \
-    else                                                                                     \
-      hipLaunchKernelGGL((KERNEL<false, PER>), GRID, dim3(kSsThreads), 0, ST, __VA_ARGS__);  \
+#define SS_LAUNCH(KERNEL, VEC, GRID, ST, ...)                                             \
+  do {                                                                                  \
+    if (VEC)                                                                            \
+      hipLaunchKernelGGL((KERNEL<true>), GRID, dim3(kSsThreads), 0, ST, __VA_ARGS__);   \
+    else                                                                                \
+      hipLaunchKernelGGL((KERNEL<false>), GRID, dim3(kSsThreads), 0, ST, __VA_ARGS__);  \
+  } while (0)
+
+// Piece size of a block-mass pass (entries per thread): the largest piece that
+// still gives one work-group per CU over `rows` rows (each work-group holds
+// its slot until its ticket returns: fewer, larger pieces waste less).
+int ss_mass_per(int V, int rows) {
+  for (int per : {64, 16})
+    if ((long long)rows * ceil_div(V, kSsThreads * per) >= 256) return per;
+  return 8;
+}
+
+#define SS_MASS(KERNEL, VEC, PER, ROWS, ST, ...)                                                              \
+  do {                                                                                                       \
+    const int np_ = ceil_div(V, kSsThreads * (PER));                                                         \
+    const dim3 g_(np_, ROWS), b_(kSsThreads);                                                                \
+    if ((PER) == 64) {                                                                                       \
+      if (VEC) hipLaunchKernelGGL((KERNEL<true, 64>), g_, b_, 0, ST, __VA_ARGS__);                           \
+      else hipLaunchKernelGGL((KERNEL<false, 64>), g_, b_, 0, ST, __VA_ARGS__);                              \
+    } else if ((PER) == 16) {                                                                                \
+      if (VEC) hipLaunchKernelGGL((KERNEL<true, 16>), g_, b_, 0, ST, __VA_ARGS__);                           \
+      else hipLaunchKernelGGL((KERNEL<false, 16>), g_, b_, 0, ST, __VA_ARGS__);                              \
+    } else {                                                                                                 \
+      if (VEC) hipLaunchKernelGGL((KERNEL<true, 8>), g_, b_, 0, ST, __VA_ARGS__);                            \
+      else hipLaunchKernelGGL((KERNEL<false, 8>), g_, b_, 0, ST, __VA_ARGS__);                               \
+    }                                                                                                        \
   } while (0)
 
 }  // namespace
@@ -1259,12 +1285,19 @@ int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float*
   if (!draft_logits || !cand) return fail(DFLASH_EINVAL, "NULL argument");
   const int V = ctx->d.V, K = ctx->d.B - 1;
   const bool vec = V % 4 == 0 && aligned16(draft_logits);
-  const int nch = ss_nchunk(V, kSsPerDraft);
+  const int per = ss_mass_per(V, n_req * K);
+  const int np = ceil_div(V, kSsThreads * per);
   hipStream_t st = static_cast<hipStream_t>(stream);
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_DRAFT, st);
-    SS_LAUNCH(ss_draft_kernel, kSsPerDraft, vec, dim3(nch, n_req * K), st, draft_logits, V, K, nch, s2, seed, req_id,
-              w, cand, draft_lse);
+    SS_MASS(ss_draft_mass_kernel, vec, per, n_req * K, st, draft_logits, V, K, np, s2, seed, req_id, w, draft_lse);
+    const dim3 g(n_req * K), b(kSsPickThreads);
+    if (vec)
+      hipLaunchKernelGGL((ss_pick_kernel<true, false>), g, b, 0, st, draft_logits, nullptr, nullptr, V, K, s2, seed,
+                         req_id, w, cand, nullptr);
+    else
+      hipLaunchKernelGGL((ss_pick_kernel<false, false>), g, b, 0, st, draft_logits, nullptr, nullptr, V, K, s2, seed,
+                         req_id, w, cand, nullptr);
   }
   if (!hip_ok(hipGetLastError(), "spec_draft launch", &rc)) return rc;
   return DFLASH_OK;
@@ -1286,22 +1319,24 @@ int dflash_spec_verify(dflash_ctx* ctx, void* stream, int32_t n_req, const float
   hipStream_t st = static_cast<hipStream_t>(stream);
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_STATS, st);
-    const int nch = ss_nchunk(V, kSsPerStats);
-    SS_LAUNCH(ss_stats_kernel, kSsPerStats, vec, dim3(nch, rows), st, draft_logits, target_logits, cand, draft_lse, V,
-              K, nch, s2, seed, req_id, w, tokens);
+    const int nch = ceil_div(V, kSsBlock);
+    SS_LAUNCH(ss_stats_kernel, vec, dim3(nch, rows), st, draft_logits, target_logits, cand, draft_lse, V, K, nch, s2,
+              seed, req_id, w, tokens);
   }
   if (!hip_ok(hipGetLastError(), "spec_verify stats launch", &rc)) return rc;
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_RESAMPLE, st);
-    if (n_req <= 4) {
-      const int nch = ss_nchunk(V, kSsPerResampleFew);
-      SS_LAUNCH(ss_resample_kernel, kSsPerResampleFew, vec, dim3(nch, n_req), st, draft_logits, target_logits,
-                draft_lse, V, K, nch, s2, seed, req_id, w, tokens, tau);
-    } else {
-      const int nch = ss_nchunk(V, kSsPerResample);
-      SS_LAUNCH(ss_resample_kernel, kSsPerResample, vec, dim3(nch, n_req), st, draft_logits, target_logits,
-                draft_lse, V, K, nch, s2, seed, req_id, w, tokens, tau);
-    }
+    const int per = ss_mass_per(V, n_req);
+    const int np = ceil_div(V, kSsThreads * per);
+    SS_MASS(ss_resample_mass_kernel, vec, per, n_req, st, draft_logits, target_logits, draft_lse, V, K, np, s2, seed,
+            req_id, w);
+    const dim3 g(n_req), b(kSsPickThreads);
+    if (vec)
+      hipLaunchKernelGGL((ss_pick_kernel<true, true>), g, b, 0, st, draft_logits, target_logits, draft_lse, V, K, s2,
+                         seed, req_id, w, tokens, tau);
+    else
+      hipLaunchKernelGGL((ss_pick_kernel<false, true>), g, b, 0, st, draft_logits, target_logits, draft_lse, V, K, s2,
+                         seed, req_id, w, tokens, tau);
   }
   if (!hip_ok(hipGetLastError(), "spec_verify resample launch", &rc)) return rc;
   return DFLASH_OK;

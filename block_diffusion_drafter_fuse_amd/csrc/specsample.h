@@ -2,16 +2,29 @@
 // ("DFlash 2：正确 token 已在候选里", introduction and selector section:
 // outputs stay lossless through rejection sampling; "DFlash 投机解码", section
 // 四: the rejected position is redrawn and the last position gives the bonus
-// token).  Three HBM-streaming kernels, each a grid of (vocabulary chunk, row)
-// work-groups of 256 threads over 4096 entries:
+// token).  Draws use blocks of kSsBlock = 16384 ids.  Kernels (grids of
+// (vocabulary piece, row) work-groups of 256 threads unless noted):
 //
-//   ss_draft_kernel     x_j = argmax_v (l_j[v] / T + G_v): Gumbel-max drafting
-//   ss_stats_kernel     base-2 log-sum-exp of every drafter and verifier row,
-//                       then, in the last work-group of a request, the
-//                       acceptance scan r_j q_j(x_j) < p_{j-1}(x_j)
-//   ss_resample_kernel  the emitted token after the scan: Gumbel-max over
-//                       log max(0, p - q) on the rejected offset, or over the
-//                       verifier's last row when every draft was kept
+//   ss_draft_mass_kernel     per-piece (max, sum) of l log2(e) / T; the last
+//                            work-group of a row merges them into the row's
+//                            log-sum-exp and the block masses and picks a
+//                            block by inverse CDF
+//   ss_stats_kernel          base-2 log-sum-exp of the verifier rows (and of
+//                            the drafter rows when the draft call did not hand
+//                            them over), then, in the last work-group of a
+//                            request, the acceptance scan
+//                            r_j q_j(x_j) < p_{j-1}(x_j)
+//   ss_resample_mass_kernel  per-piece masses of max(0, p - q) on the rejected
+//                            offset and of the verifier row; the last
+//                            work-group of a request picks the weights and a
+//                            block
+//   ss_pick_kernel           one 1024-thread work-group per draw: Gumbel-max
+//                            over the chosen block's ids (the drafted token, or
+//                            the replacement / bonus token)
+//
+// The two-stage draw is exact: P(block b) = mass_b / S and P(v | b) =
+// w_v / mass_b.  Only the chosen block needs generator output (one Philox
+// block per 8 ids), so the draws stream the logits at HBM speed.
 //
 // Per-chunk partials go to the workspace with agent-scope stores (coherent
 // across XCDs); the last work-group of a row (ticket) combines them in chunk
@@ -22,8 +35,10 @@
 // "Parallel random numbers: as easy as 1, 2, 3", SC 2011), key (seed, stream),
 // counter (v / 8, row, request, 0); entry v uses the top 24 bits k of 32-bit
 // half (v % 2 == 0: high) of word (v % 8) / 2, as the uniform (k + 0.5) 2^-24.
-// Streams: 0 drafting (row = offset - 1), 1 acceptance (index offset - 1),
-// 2 replacement / bonus (index = token id).
+// Streams: 0 drafting noise (row = offset - 1, index = token id), 1 acceptance
+// (index offset - 1), 2 replacement / bonus noise (index = token id), 3 and 4
+// the block choice of drafting (row = offset - 1) and of the replacement /
+// bonus (row 0), index 0.
 #pragma once
 #include "common.h"
 #include "gemm_tiled.h"
@@ -31,23 +46,20 @@
 namespace dfl {
 
 constexpr int kSsThreads = 256;
-// Vocabulary entries per thread (work-group: 256 times that), measured best
-// at 1 and 32 requests of a 151,936-entry vocabulary: drafting (bound by the
-// generator's integer arithmetic) 32, row statistics (bound by HBM) 64, the
-// replacement draw (one or two rows per request) 8 up to four requests and 16
-// beyond.
-constexpr int kSsPerDraft = 32;
-constexpr int kSsPerStats = 64;
-constexpr int kSsPerResampleFew = 8;
-constexpr int kSsPerResample = 16;
+constexpr int kSsPer = 64;                    // entries per thread of the statistics pass
+constexpr int kSsBlock = kSsThreads * kSsPer;  // ids per sampling block (and per statistics work-group)
+constexpr int kSsPickThreads = 1024;          // threads of a block draw: 16 ids each
+constexpr int kSsMaxBlocks = 64;              // block masses are scanned by one wave
 constexpr int kSsStreamDraft = 0, kSsStreamAccept = 1, kSsStreamResample = 2;
+constexpr int kSsStreamDraftBlock = 3, kSsStreamResampleBlock = 4;
 
 struct SsWork {
-  float4* part;  // [rows][nchunk] per-chunk partials
+  float4* part;  // [rows][npiece] per-piece partials
   float* lse;    // [n_req][2K+1] base-2 log-sum-exp of l log2(e) / T: K drafter rows, then K+1 verifier rows
   int* nacc;     // [n_req] accepted drafts
   int* row_ctr;  // [rows] tickets
   int* req_ctr;  // [n_req] tickets
+  int* blk;      // [rows] chosen block of a draw; the replacement draw adds 64 when it samples the residual
 };
 
 // hi/lo 64-bit halves of the 128-bit product m * c, from four 32 x 32 -> 64
@@ -180,58 +192,6 @@ __device__ __forceinline__ float4 ss_load_part(const SsWork& w, int row, int chu
                      __hip_atomic_load(p + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Work-group argmax of (v, i) pairs (x and y of the float4: value, id bits)
-// and optionally a second pair (z, w); result valid in thread 0.
-template <int NPAIR>
-__device__ __forceinline__ void ss_block_argmax(float v[NPAIR], int i[NPAIR]) {
-  __shared__ float sv[NPAIR][kSsThreads / 64];
-  __shared__ int si[NPAIR][kSsThreads / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int p = 0; p < NPAIR; ++p) {
-    ss_wave_argmax(v[p], i[p]);
-    if (lane == 0) {
-      sv[p][wave] = v[p];
-      si[p][wave] = i[p];
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-#pragma unroll
-    for (int p = 0; p < NPAIR; ++p)
-      for (int x = 1; x < kSsThreads / 64; ++x)
-        if (ss_better(sv[p][x], si[p][x], v[p], i[p])) {
-          v[p] = sv[p][x];
-          i[p] = si[p][x];
-        }
-  }
-}
-
-// Wave 0 merges the nchunk argmax partials of `row` in chunk order; the
-// result is valid in lane 0 of wave 0.  NPAIR pairs per partial.
-template <int NPAIR>
-__device__ __forceinline__ void ss_merge_argmax(const SsWork& w, int row, int nchunk, float v[NPAIR], int i[NPAIR]) {
-#pragma unroll
-  for (int p = 0; p < NPAIR; ++p) {
-    v[p] = -INFINITY;
-    i[p] = 0x7fffffff;
-  }
-  if (threadIdx.x >= 64) return;
-  for (int x = threadIdx.x; x < nchunk; x += 64) {
-    const float4 q = ss_load_part(w, row, x, nchunk);
-    const float qv[2] = {q.x, q.z};
-    const int qi[2] = {__float_as_int(q.y), __float_as_int(q.w)};
-#pragma unroll
-    for (int p = 0; p < NPAIR; ++p)
-      if (ss_better(qv[p], qi[p], v[p], i[p])) {
-        v[p] = qv[p];
-        i[p] = qi[p];
-      }
-  }
-#pragma unroll
-  for (int p = 0; p < NPAIR; ++p) ss_wave_argmax(v[p], i[p]);
-}
-
 // Work-group (max, sum) merge of the lse pairs; result valid in thread 0.
 __device__ __forceinline__ void ss_block_lse(float& m, float& s) {
   __shared__ float sm[kSsThreads / 64], ss[kSsThreads / 64];
@@ -246,7 +206,7 @@ __device__ __forceinline__ void ss_block_lse(float& m, float& s) {
     for (int x = 1; x < kSsThreads / 64; ++x) ss_lse_merge(m, s, sm[x], ss[x]);
 }
 
-// Loads the PER entries of this thread (in 8-entry groups, ids
+// Loads the PER entries of this thread (PER a multiple of 8; 8-entry groups, ids
 // chunk * 256 * PER + (it * 256 + thread) * 8 + e) scaled by s2 = log2(e) / T,
 // and their maximum.  Entries at or past V are -inf.
 template <bool VEC, int PER>
@@ -282,62 +242,81 @@ __device__ __forceinline__ float ss_sum_exp2(const float z[PER], float m) {
   return s;
 }
 
-// Gumbel-max drafting.  Grid (nchunk, n_req * K); row = r * K + (offset - 1)
-// of logits [n_req][K][V]; cand[row] = the drafted token.  The pass also
-// yields the row's base-2 log-sum-exp, written to dlse[row] when dlse is
-// given (the verifier then need not read the drafter rows again for it).
+// Inverse CDF over block masses held one per lane of a wave (lanes past the
+// last block hold 0): the first block whose inclusive prefix exceeds u times
+// the total, never an empty block (should rounding leave no prefix above the
+// target, the last block with mass).  All 64 lanes call it; the result is the
+// same in every lane.
+__device__ __forceinline__ int ss_choose_block(float mass, double u) {
+  const int lane = threadIdx.x & 63;
+  float cum = mass;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_up(cum, o);
+    if (lane >= o) cum += t;
+  }
+  const float target = (float)(u * (double)__shfl(cum, 63));
+  const unsigned long long over = __ballot(cum > target && mass > 0.f);
+  if (over) return __ffsll(over) - 1;
+  const unsigned long long pos = __ballot(mass > 0.f);
+  return pos ? 63 - __clzll(pos) : 0;
+}
+
+// Work-group sums of two values; result valid in thread 0.
+__device__ __forceinline__ void ss_block_sum2(float& a, float& b) {
+  __shared__ float sa[kSsThreads / 64], sb[kSsThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  a = wave_sum(a);
+  b = wave_sum(b);
+  if (lane == 0) {
+    sa[wave] = a;
+    sb[wave] = b;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    for (int x = 1; x < kSsThreads / 64; ++x) {
+      a += sa[x];
+      b += sb[x];
+    }
+}
+
+// Drafting, first pass.  Grid (npiece, n_req * K), pieces of 256 * PER ids;
+// row = r * K + (offset - 1) of logits [n_req][K][V].  The last work-group of
+// a row stores the chosen block in blk[row] and, when dlse is given, the
+// row's base-2 log-sum-exp of l log2(e) / T (for the verifier).
 template <bool VEC, int PER>
 __global__ void __launch_bounds__(kSsThreads)
-    ss_draft_kernel(const float* __restrict__ logits, int V, int K, int nchunk, float s2, uint64_t seed,
-                    const int* __restrict__ req_id, SsWork w, int* __restrict__ cand, float* __restrict__ dlse) {
+    ss_draft_mass_kernel(const float* __restrict__ logits, int V, int K, int npiece, float s2, uint64_t seed,
+                         const int* __restrict__ req_id, SsWork w, float* __restrict__ dlse) {
+  static_assert(PER % 8 == 0 && kSsBlock % (kSsThreads * PER) == 0, "whole 8-entry groups, whole pieces per block");
+  constexpr int PPB = kSsBlock / (kSsThreads * PER);  // pieces per block
   const int chunk = blockIdx.x, row = blockIdx.y;
   const int r = row / K, off = row - r * K;
-  const uint64_t req = (uint64_t)(uint32_t)req_id[r];
-  float z[PER];
-  float m = ss_load_row<VEC, PER>(logits + (size_t)row * V, chunk, V, s2, z);
-  float bv[1] = {-INFINITY};
-  int bi[1] = {0x7fffffff};
-  // ids rise within a thread, so a strict > keeps the lowest id of a tie;
-  // entries past V hold -inf and never win
-#pragma unroll
-  for (int it = 0; it < PER / 8; ++it) {
-    const int v0 = chunk * (kSsThreads * PER) + (it * kSsThreads + (int)threadIdx.x) * 8;
-    if (v0 < V) {
-      uint64_t c[4] = {(uint64_t)(v0 >> 3), (uint64_t)off, req, 0};
-      philox4x64_10(c, seed, kSsStreamDraft);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float key = z[it * 8 + e] - ss_log2_exp(ss_bits(c, e));
-        if (key > bv[0]) {
-          bv[0] = key;
-          bi[0] = v0 + e;
-        }
-      }
-    }
+  {
+    float z[PER];
+    float m = ss_load_row<VEC, PER>(logits + (size_t)row * V, chunk, V, s2, z);
+    float s = ss_sum_exp2<PER>(z, m);
+    ss_block_lse(m, s);
+    if (!ss_publish(w, row, chunk, npiece, make_float4(m, s, 0.f, 0.f), w.row_ctr)) return;
   }
-  float s = ss_sum_exp2<PER>(z, m);
-  ss_block_argmax<1>(bv, bi);
-  ss_block_lse(m, s);
-  if (!ss_publish(w, row, chunk, nchunk, make_float4(bv[0], __int_as_float(bi[0]), m, s), w.row_ctr)) return;
   if (threadIdx.x >= 64) return;
-  // wave 0: merge the row's partials in chunk order
-  bv[0] = -INFINITY;
-  bi[0] = 0x7fffffff;
-  m = -INFINITY;
-  s = 0.f;
-  for (int x = threadIdx.x; x < nchunk; x += 64) {
-    const float4 q = ss_load_part(w, row, x, nchunk);
-    if (ss_better(q.x, __float_as_int(q.y), bv[0], bi[0])) {
-      bv[0] = q.x;
-      bi[0] = __float_as_int(q.y);
-    }
-    ss_lse_merge(m, s, q.z, q.w);
+  // wave 0 of the last work-group: lane b merges the pieces of block b in
+  // piece order, then the block by inverse CDF over the masses
+  const int lane = threadIdx.x;
+  float bm = -INFINITY, bs = 0.f;
+  for (int x = lane * PPB; x < min(npiece, (lane + 1) * PPB); ++x) {
+    const float4 q = ss_load_part(w, row, x, npiece);
+    ss_lse_merge(bm, bs, q.x, q.y);
   }
-  ss_wave_argmax(bv[0], bi[0]);
-  ss_wave_lse(m, s);
-  if (threadIdx.x == 0) {
-    cand[row] = bv[0] > -INFINITY ? bi[0] : 0;  // a row without a finite logit: id 0
-    if (dlse) dlse[row] = m + log2f(s);
+  float M = bm, S = bs;
+  ss_wave_lse(M, S);  // the same totals in every lane
+  const float mass = bs > 0.f ? bs * exp2f(bm - M) : 0.f;
+  uint64_t c[4] = {0, (uint64_t)off, (uint64_t)(uint32_t)req_id[r], 0};
+  philox4x64_10(c, seed, kSsStreamDraftBlock);
+  const int b = ss_choose_block(mass, ss_uniform(ss_bits(c, 0)));
+  if (lane == 0) {
+    w.blk[row] = b;
+    if (dlse) dlse[row] = M + log2f(S);
     __hip_atomic_store(w.row_ctr + row, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -347,7 +326,7 @@ __global__ void __launch_bounds__(kSsThreads)
 // k (offset k + 1) for k < K, verifier row k - K otherwise; with dlse (the
 // drafter rows' values from ss_draft_kernel) the grid is (nchunk,
 // n_req * (K + 1)) over the verifier rows alone.  s2 = log2(e) / T.
-template <bool VEC, int PER>
+template <bool VEC>
 __global__ void __launch_bounds__(kSsThreads)
     ss_stats_kernel(const float* __restrict__ draft, const float* __restrict__ target, const int* __restrict__ cand,
                     const float* __restrict__ dlse, int V, int K, int nchunk, float s2, uint64_t seed,
@@ -357,9 +336,9 @@ __global__ void __launch_bounds__(kSsThreads)
   const int RA = dlse ? K + 1 : R;  // rows of a request in this grid
   const int r = y / RA, k = (dlse ? K : 0) + (y - r * RA);  // k: row of the request in 0..2K
   const float* lr = k < K ? draft + ((size_t)r * K + k) * V : target + ((size_t)r * (K + 1) + (k - K)) * V;
-  float z[PER];
-  float m = ss_load_row<VEC, PER>(lr, chunk, V, s2, z);
-  float s = ss_sum_exp2<PER>(z, m);
+  float z[kSsPer];
+  float m = ss_load_row<VEC, kSsPer>(lr, chunk, V, s2, z);
+  float s = ss_sum_exp2<kSsPer>(z, m);
   ss_block_lse(m, s);
   if (!ss_publish(w, y, chunk, nchunk, make_float4(m, s, 0.f, 0.f), w.row_ctr)) return;
   if (threadIdx.x >= 64) return;
@@ -410,65 +389,168 @@ __global__ void __launch_bounds__(kSsThreads)
   }
 }
 
-// The emitted token after the scan.  Grid (nchunk, n_req).  With n = nacc[r]
-// < K: Gumbel-max over log max(0, p_n - q_{n+1}) (verifier row n, drafter row
-// n); with n = K, or a residual that rounding left empty: Gumbel-max over the
-// verifier row's l / T.  tokens[r][n] = that token, tau[r] = n + 1.
+// The emitted token after the scan, first pass.  Grid (npiece, n_req),
+// pieces of 256 * PER ids.  With n = nacc[r] < K the weights are
+// max(0, p_n - q_{n+1}) (verifier row n, drafter row n); with n = K, or a
+// residual that rounding left empty, the verifier row's softmax(l / T).  The
+// last work-group of a request stores the chosen block in blk[r] (+ 64 when
+// the residual is sampled).
 template <bool VEC, int PER>
 __global__ void __launch_bounds__(kSsThreads)
-    ss_resample_kernel(const float* __restrict__ draft, const float* __restrict__ target,
-                       const float* __restrict__ dlse, int V, int K, int nchunk, float s2, uint64_t seed,
-                       const int* __restrict__ req_id, SsWork w, int* __restrict__ tokens, int* __restrict__ tau) {
+    ss_resample_mass_kernel(const float* __restrict__ draft, const float* __restrict__ target,
+                            const float* __restrict__ dlse, int V, int K, int npiece, float s2, uint64_t seed,
+                            const int* __restrict__ req_id, SsWork w) {
+  static_assert(PER % 8 == 0 && kSsBlock % (kSsThreads * PER) == 0, "whole 8-entry groups, whole pieces per block");
+  constexpr int PPB = kSsBlock / (kSsThreads * PER);
   const int chunk = blockIdx.x, r = blockIdx.y;
   const int R = 2 * K + 1;
   const int n = min(max(w.nacc[r], 0), K);  // written by ss_stats_kernel, in 0..K
   const bool rej = n < K;
+  {
+    const float lse_t = w.lse[(size_t)r * R + K + n];
+    const float lse_d = rej ? (dlse ? dlse[(size_t)r * K + n] : w.lse[(size_t)r * R + n]) : 0.f;
+    float zt[PER], zd[PER];  // all loads issued before the arithmetic
+    ss_load_row<VEC, PER>(target + ((size_t)r * (K + 1) + n) * V, chunk, V, s2, zt);
+    if (rej) ss_load_row<VEC, PER>(draft + ((size_t)r * K + n) * V, chunk, V, s2, zd);
+    float ws = 0.f, ps = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float p = exp2f(zt[e] - lse_t);
+      ps += p;
+      if (rej) ws += fmaxf(p - exp2f(zd[e] - lse_d), 0.f);
+    }
+    ss_block_sum2(ws, ps);
+    if (!ss_publish(w, r, chunk, npiece, make_float4(ws, ps, 0.f, 0.f), w.req_ctr)) return;
+  }
+  if (threadIdx.x >= 64) return;
+  // wave 0 of the last work-group: lane b sums the pieces of block b in piece order
+  const int lane = threadIdx.x;
+  float qx = 0.f, qy = 0.f;
+  for (int x = lane * PPB; x < min(npiece, (lane + 1) * PPB); ++x) {
+    const float4 q = ss_load_part(w, r, x, npiece);
+    qx += q.x;
+    qy += q.y;
+  }
+  const bool res = rej && wave_sum(qx) > 0.f;
+  uint64_t c[4] = {0, 0, (uint64_t)(uint32_t)req_id[r], 0};
+  philox4x64_10(c, seed, kSsStreamResampleBlock);
+  const int b = ss_choose_block(res ? qx : qy, ss_uniform(ss_bits(c, 0)));
+  if (lane == 0) {
+    w.blk[r] = b + (res ? kSsMaxBlocks : 0);
+    __hip_atomic_store(w.req_ctr + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Gumbel-max over the chosen block of one draw; one work-group of 1024
+// threads per draw, 16 ids per thread (two Philox blocks).
+//   RESAMPLE = false: draw d = row of the drafter logits; cand[d] = the token.
+//   RESAMPLE = true:  draw d = request; the weights of blk[d] (see
+//   ss_resample_mass_kernel); tokens[d][n] = the token, tau[d] = n + 1.
+template <bool VEC, bool RESAMPLE>
+__global__ void __launch_bounds__(kSsPickThreads)
+    ss_pick_kernel(const float* __restrict__ draft, const float* __restrict__ target,
+                   const float* __restrict__ dlse, int V, int K, float s2, uint64_t seed,
+                   const int* __restrict__ req_id, SsWork w, int* __restrict__ out, int* __restrict__ tau) {
+  constexpr int PER = kSsBlock / kSsPickThreads;  // 16
+  const int d = blockIdx.x, tid = threadIdx.x;
+  const int R = 2 * K + 1;
+  const int code = w.blk[d];
+  const int b = code % kSsMaxBlocks;
+  const bool res = RESAMPLE && code >= kSsMaxBlocks;
+  int n = 0, r = d, off = 0;
+  const float* la;  // weights' logits: the drafter row, or the verifier row
+  const float* lb = nullptr;
+  float lse_t = 0.f, lse_d = 0.f;
+  if constexpr (RESAMPLE) {
+    n = min(max(w.nacc[d], 0), K);
+    la = target + ((size_t)d * (K + 1) + n) * V;
+    if (res) {
+      lb = draft + ((size_t)d * K + n) * V;
+      lse_t = w.lse[(size_t)d * R + K + n];
+      lse_d = dlse ? dlse[(size_t)d * K + n] : w.lse[(size_t)d * R + n];
+    }
+  } else {
+    r = d / K;
+    off = d - r * K;
+    la = draft + (size_t)d * V;
+  }
   const uint64_t req = (uint64_t)(uint32_t)req_id[r];
-  const float* lt = target + ((size_t)r * (K + 1) + n) * V;
-  const float* ld = draft + ((size_t)r * K + (rej ? n : 0)) * V;
-  const float lse_t = w.lse[(size_t)r * R + K + n];
-  const float lse_d = rej ? (dlse ? dlse[(size_t)r * K + n] : w.lse[(size_t)r * R + n]) : 0.f;
-  // pair 0: residual, pair 1: verifier row
-  float bv[2] = {-INFINITY, -INFINITY};
-  int bi[2] = {0x7fffffff, 0x7fffffff};
+  float za[PER], zb[PER];
+  {
+    // ids b * kSsBlock + (it * 1024 + tid) * 8 + e: consecutive lanes read
+    // consecutive 32-byte runs
 #pragma unroll
-  for (int it = 0; it < PER / 8; ++it) {
-    const int v0 = chunk * (kSsThreads * PER) + (it * kSsThreads + (int)threadIdx.x) * 8;
-    if (v0 >= V) break;
-    float a[8], b[8];
-    ss_load8<VEC>(lt, v0, V, a);
-    if (rej) ss_load8<VEC>(ld, v0, V, b);
-    uint64_t c[4] = {(uint64_t)(v0 >> 3), 0, req, 0};
-    philox4x64_10(c, seed, kSsStreamResample);
-    // base-2 keys (see ss_log2_exp); ids rise within a thread, so strict >
-    // keeps the lowest id of a tie; entries past V hold -inf and never win
+    for (int it = 0; it < PER / 8; ++it) {
+      const int v0 = b * kSsBlock + (it * kSsPickThreads + tid) * 8;
+      float l[8];
+      if (v0 < V) {
+        ss_load8<VEC>(la, v0, V, l);
+      } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float g = ss_log2_exp(ss_bits(c, e));
-      const float tk = fmaf(a[e], s2, -g);
-      if (tk > bv[1]) {
-        bv[1] = tk;
-        bi[1] = v0 + e;
+        for (int e = 0; e < 8; ++e) l[e] = -INFINITY;
       }
-      if (rej) {
-        const float d = exp2f(fmaf(a[e], s2, -lse_t)) - exp2f(fmaf(b[e], s2, -lse_d));
-        const float rk = d > 0.f ? __builtin_amdgcn_logf(d) - g : -INFINITY;
-        if (rk > bv[0]) {
-          bv[0] = rk;
-          bi[0] = v0 + e;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) za[it * 8 + e] = l[e] * s2;
+      if (res) {
+        if (v0 < V) {
+          ss_load8<VEC>(lb, v0, V, l);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) l[e] = -INFINITY;
         }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zb[it * 8 + e] = l[e] * s2;
       }
     }
   }
-  ss_block_argmax<2>(bv, bi);
-  if (!ss_publish(w, r, chunk, nchunk,
-                  make_float4(bv[0], __int_as_float(bi[0]), bv[1], __int_as_float(bi[1])), w.req_ctr))
-    return;
-  ss_merge_argmax<2>(w, r, nchunk, bv, bi);
-  if (threadIdx.x == 0) {
-    tokens[(size_t)r * (K + 1) + n] = (rej && bv[0] > -INFINITY) ? bi[0] : (bv[1] > -INFINITY ? bi[1] : 0);
-    tau[r] = n + 1;
-    __hip_atomic_store(w.req_ctr + r, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  // ids rise within a thread, so a strict > keeps the lowest id of a tie;
+  // entries past V hold -inf and never win
+#pragma unroll
+  for (int it = 0; it < PER / 8; ++it) {
+    const int v0 = b * kSsBlock + (it * kSsPickThreads + tid) * 8;
+    if (v0 >= V) break;
+    uint64_t c[4] = {(uint64_t)(v0 >> 3), (uint64_t)off, req, 0};
+    philox4x64_10(c, seed, RESAMPLE ? kSsStreamResample : kSsStreamDraft);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float g = ss_log2_exp(ss_bits(c, e));
+      float key;
+      if (res) {
+        const float dd = exp2f(za[it * 8 + e] - lse_t) - exp2f(zb[it * 8 + e] - lse_d);
+        key = dd > 0.f ? __builtin_amdgcn_logf(dd) - g : -INFINITY;
+      } else {
+        key = za[it * 8 + e] - g;
+      }
+      if (key > bv) {
+        bv = key;
+        bi = v0 + e;
+      }
+    }
+  }
+  // work-group argmax (16 waves)
+  __shared__ float sv[kSsPickThreads / 64];
+  __shared__ int si[kSsPickThreads / 64];
+  ss_wave_argmax(bv, bi);
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = bv;
+    si[tid >> 6] = bi;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int x = 1; x < kSsPickThreads / 64; ++x)
+      if (ss_better(sv[x], si[x], bv, bi)) {
+        bv = sv[x];
+        bi = si[x];
+      }
+    const int tok = bv > -INFINITY ? bi : b * kSsBlock;  // no finite key: the block's first id
+    if constexpr (RESAMPLE) {
+      out[(size_t)d * (K + 1) + n] = tok;
+      tau[d] = n + 1;
+    } else {
+      out[d] = tok;
+    }
   }
 }
 

@@ -6,11 +6,13 @@ verifier rows, drafter rows = the matching verifier row plus per-request noise,
 one in five with its peaks moved), the same arrays on both sides; the
 candidates passed to the verifier are the oracle's own drafts.
 
-Bars.  Every choice the kernels make by an argmax of fp32 keys must be valid:
-its float64 key lies within the key's rounding bound of the oracle's maximum
-(1e-3 absolute, plus the cancellation bound of log max(0, p - q) on residual
-draws); where the oracle's winner leads by more than that bound the token is
-the oracle's.  Every acceptance decision equals the oracle's where
+Bars.  Every draw is two-stage (a vocabulary block by inverse CDF over the
+block masses, then a Gumbel-max within it).  The block must be the oracle's
+unless u S lies within 1e-4 S of the boundary between the two blocks (fp32
+masses).  Within the block the choice must be valid: its float64 key lies
+within the key's rounding bound of the oracle's maximum (1e-3 absolute, plus
+the cancellation bound of log max(0, p - q) on residual draws); where the
+oracle's winner leads by more than that bound the token is the oracle's.  Every acceptance decision equals the oracle's where
 |u q - p| > 1e-4 max(u q, p); a request whose walk reaches a closer decision is
 compared up to it.  Integer outputs (tau, the kept prefix, the -1 tail) are
 exact.  At least 97% of all choices must equal the oracle's outright."""
@@ -106,9 +108,33 @@ class Tally:
         return self.exact / max(1, self.total)
 
 
-def draft_keys(dl_row, temp, seed, req, off):
-    g = ss.gumbel(ss.uniforms(seed, ss.STREAM_DRAFT, req, off, dl_row.size))
-    return dl_row.astype(np.float64) / temp + g
+BLOCK_TOL = 1e-4
+
+
+def check_two_stage(t, got, logw, seed, stream_block, stream_entry, req, row, err=None, what=""):
+    """One GPU draw against the oracle's two-stage draw over log-weights logw."""
+    logw = np.asarray(logw, dtype=np.float64)
+    V = logw.size
+    assert 0 <= got < V, f"{what}: id {got} outside the vocabulary"
+    with np.errstate(under="ignore"):
+        w = np.exp(logw - logw.max())
+    mass = np.add.reduceat(w, np.arange(0, V, ss.BLOCK))
+    cum = np.cumsum(mass)
+    u = ss.uniforms(seed, stream_block, req, row, 1)[0]
+    b = ss.block_choice(w, u)
+    bg = got // ss.BLOCK
+    assert mass[bg] > 0, f"{what}: chose an empty block"
+    if bg != b:
+        # blocks may differ only where u S sits on the boundary between them
+        edge = cum[min(b, bg)]
+        assert abs(u * cum[-1] - edge) <= BLOCK_TOL * cum[-1], f"{what}: block {bg}, oracle {b}"
+        t.total += 1
+        log(f"{what}: block differs at a boundary")
+        return
+    lo, hi = b * ss.BLOCK, min(V, (b + 1) * ss.BLOCK)
+    keys = np.full(V, -np.inf)
+    keys[lo:hi] = logw[lo:hi] + ss.gumbel(ss.uniforms(seed, stream_entry, req, row, hi)[lo:])
+    t.choice(got, keys, err, what)
 
 
 def check_draft(sp, dl, temp, seed, req, rows=None, tally=None):
@@ -127,7 +153,8 @@ def check_draft(sp, dl, temp, seed, req, rows=None, tally=None):
         for j in range(K):
             if rows is not None and (r, j) not in rows:
                 continue
-            t.choice(int(cand[r, j]), draft_keys(dl[r, j], temp, seed, req[r], j), what=f"draft r{r} j{j + 1}")
+            check_two_stage(t, int(cand[r, j]), dl[r, j].astype(np.float64) / temp, seed, ss.STREAM_DRAFT_BLOCK,
+                            ss.STREAM_DRAFT, req[r], j, what=f"draft r{r} j{j + 1}")
     return cand, dlse, t
 
 
@@ -160,22 +187,20 @@ def check_verify(sp, dl, tl, cand, temp, seed, req, reqs=None, tally=None, dlse=
             log(f"r{r}: walks part at a close acceptance decision (offset {j + 1})")
             continue
         # the emitted token
-        g = ss.gumbel(ss.uniforms(seed, ss.STREAM_RESIDUAL, req[r], 0, V))
         err = None
+        logw = tl[r, ss.verifier_row(no + 1) if no < K else K].astype(np.float64) / temp
         if no < K:
             q = ss.softmax(dl[r, no], temp)
             p = ss.softmax(tl[r, ss.verifier_row(no + 1)], temp)
             w = ss.residual(p, q)
-            with np.errstate(divide="ignore"):
-                keys = np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf) + g
-            # fp32 probabilities carry ~1e-6 relative error; the difference
-            # magnifies it by (p + q) / w in the log
-            err = np.where(w > 0, 4e-6 * (p + q) / np.where(w > 0, w, 1.0), 0.0)
-            if not np.any(w > 0):
-                keys, err = tl[r, no].astype(np.float64) / temp + g, None
-        else:
-            keys = tl[r, K].astype(np.float64) / temp + g
-        t.choice(int(tokens[r, ng]), keys, err, what=f"emitted r{r} (n={no})")
+            if np.any(w > 0):
+                with np.errstate(divide="ignore"):
+                    logw = np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), -np.inf)
+                # fp32 probabilities carry ~1e-6 relative error; the difference
+                # magnifies it by (p + q) / w in the log
+                err = np.where(w > 0, 4e-6 * (p + q) / np.where(w > 0, w, 1.0), 0.0)
+        check_two_stage(t, int(tokens[r, ng]), logw, seed, ss.STREAM_RESIDUAL_BLOCK, ss.STREAM_RESIDUAL, req[r], 0,
+                        err, what=f"emitted r{r} (n={no})")
     return tokens, tau, t
 
 
@@ -187,6 +212,7 @@ CASES = [
     ("one_offset", 1024, 2, 5, 1.0, False),      # B = 2: a single drafted token
     ("cold", 2048, 16, 4, 0.05, False),          # near-greedy
     ("misaligned", 4160, 6, 3, 1.0, True),       # element loads
+    ("two_blocks", 20480, 6, 3, 1.0, False),     # two sampling blocks, the second a quarter full
 ]
 
 

@@ -556,9 +556,10 @@ def measure_spec(wl, w_dev, torch, steps, warmup, temperature=1.0):
     return {"workload": f"{d.name} speculative sampling, bs {bs}, V {V}, B {B}, T {temperature}",
             "draft_ms_per_call": round(ms_draft, 4), "verify_ms_per_call": round(ms_verify, 4),
             "mean_tau": round(float(taus.mean()), 3), "kernels": kernels,
-            "note": "fp32 logit rows resident in HBM; bytes count each logit row read once "
-                    "(draft: the drafter rows; stats: the verifier rows; resample: the verifier row, "
-                    "plus the drafter row where a draft was rejected)"}
+            "note": "fp32 logit rows resident in HBM; spec_draft times both drafting kernels (block masses, "
+                    "block draw) and spec_resample both replacement kernels; bytes count each logit row read "
+                    "once (draft: the drafter rows; stats: the verifier rows; resample: the verifier row, plus "
+                    "the drafter row where a draft was rejected)"}
 
 
 def cpu_baseline(wl, w_np, budget_s=20.0):

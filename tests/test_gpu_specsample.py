@@ -257,6 +257,23 @@ def test_spec_sampling_full_vocab_bs32():
         sp.close()
 
 
+def test_spec_sampling_full_vocab_bs1():
+    """One request at the full vocabulary: 4096-id pieces for drafting, 2048-id
+    pieces for the replacement draw (the other piece sizes run above)."""
+    V, B, bs, temp = 151936, 16, 1, 1.0
+    log(f"[spec] full vocabulary, one request: V {V} B {B}")
+    sp = Sampler(V, B, bs)
+    try:
+        dl, tl = synth.make_sampling_logits(bs, B, V, seed=9)
+        _, dlse, t = check_draft(sp, dl, temp, 55, [7])
+        cand = np.stack([ss.draft_tokens(dl[0], temp, 55, 7)])
+        _, _, t = check_verify(sp, dl, tl, cand, temp, 56, [7], tally=t, dlse=dlse)
+        _, _, t = check_verify(sp, dl, tl, cand, temp, 57, [7], tally=t)
+        assert t.rate() >= 0.9
+    finally:
+        sp.close()
+
+
 def test_spec_sampling_full_vocab_misaligned():
     """Element loads at the full vocabulary with enough rows for the
     16384-entry work-groups (16 requests, B 16): sampled rows and requests

@@ -212,7 +212,7 @@ void make_plan(const dflash_dims* d, Plan* p) {
   // speculative sampling: per-chunk partials of up to 2B-1 rows per request,
   // row log-sum-exps, accepted counts, row and request tickets
   const int ss_rows = d->max_batch * (2 * d->B - 1);
-  p->ss_nchunk = ceil_div(d->V, kSsThreads * 8);  // the most pieces per row (2048-id pieces)
+  p->ss_nchunk = std::max(ceil_div(d->V, kSsThreads * 8), kSsPickParts);  // partial slots per row: 2048-id pieces, block-draw parts
   p->ss_part_off = off; off = align_up(off + (size_t)ss_rows * p->ss_nchunk * 16);
   p->ss_lse_off = off;  off = align_up(off + (size_t)ss_rows * 4);
   p->ss_nacc_off = off; off = align_up(off + (size_t)d->max_batch * 4);
@@ -1291,7 +1291,7 @@ int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float*
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_DRAFT, st);
     SS_MASS(ss_draft_mass_kernel, vec, per, n_req * K, st, draft_logits, V, K, np, s2, seed, req_id, w, draft_lse);
-    const dim3 g(n_req * K), b(kSsPickThreads);
+    const dim3 g(kSsPickParts, n_req * K), b(kSsThreads);
     if (vec)
       hipLaunchKernelGGL((ss_pick_kernel<true, false>), g, b, 0, st, draft_logits, nullptr, nullptr, V, K, s2, seed,
                          req_id, w, cand, nullptr);
@@ -1330,7 +1330,7 @@ int dflash_spec_verify(dflash_ctx* ctx, void* stream, int32_t n_req, const float
     const int np = ceil_div(V, kSsThreads * per);
     SS_MASS(ss_resample_mass_kernel, vec, per, n_req, st, draft_logits, target_logits, draft_lse, V, K, np, s2, seed,
             req_id, w);
-    const dim3 g(n_req), b(kSsPickThreads);
+    const dim3 g(kSsPickParts, n_req), b(kSsThreads);
     if (vec)
       hipLaunchKernelGGL((ss_pick_kernel<true, true>), g, b, 0, st, draft_logits, target_logits, draft_lse, V, K, s2,
                          seed, req_id, w, tokens, tau);

@@ -18,9 +18,9 @@
 //                            offset and of the verifier row; the last
 //                            work-group of a request picks the weights and a
 //                            block
-//   ss_pick_kernel           one 1024-thread work-group per draw: Gumbel-max
-//                            over the chosen block's ids (the drafted token, or
-//                            the replacement / bonus token)
+//   ss_pick_kernel           Gumbel-max over the chosen block's ids, eight
+//                            work-groups per draw (the drafted token, or the
+//                            replacement / bonus token)
 //
 // The two-stage draw is exact: P(block b) = mass_b / S and P(v | b) =
 // w_v / mass_b.  Only the chosen block needs generator output (one Philox
@@ -48,7 +48,7 @@ namespace dfl {
 constexpr int kSsThreads = 256;
 constexpr int kSsPer = 64;                    // entries per thread of the statistics pass
 constexpr int kSsBlock = kSsThreads * kSsPer;  // ids per sampling block (and per statistics work-group)
-constexpr int kSsPickThreads = 1024;          // threads of a block draw: 16 ids each
+constexpr int kSsPickParts = kSsBlock / (kSsThreads * 8);  // work-groups of a block draw, 8 ids per thread
 constexpr int kSsMaxBlocks = 64;              // block masses are scanned by one wave
 constexpr int kSsStreamDraft = 0, kSsStreamAccept = 1, kSsStreamResample = 2;
 constexpr int kSsStreamDraftBlock = 3, kSsStreamResampleBlock = 4;
@@ -441,18 +441,19 @@ __global__ void __launch_bounds__(kSsThreads)
   }
 }
 
-// Gumbel-max over the chosen block of one draw; one work-group of 1024
-// threads per draw, 16 ids per thread (two Philox blocks).
+// Gumbel-max over the chosen block of one draw.  Grid (kSsPickParts, draws):
+// work-group x of draw d covers ids 2048 x .. 2048 x + 2047 of the block, 8
+// per thread (one Philox block); the last of the draw's work-groups (ticket)
+// merges their winners in part order.
 //   RESAMPLE = false: draw d = row of the drafter logits; cand[d] = the token.
 //   RESAMPLE = true:  draw d = request; the weights of blk[d] (see
 //   ss_resample_mass_kernel); tokens[d][n] = the token, tau[d] = n + 1.
 template <bool VEC, bool RESAMPLE>
-__global__ void __launch_bounds__(kSsPickThreads)
+__global__ void __launch_bounds__(kSsThreads)
     ss_pick_kernel(const float* __restrict__ draft, const float* __restrict__ target,
                    const float* __restrict__ dlse, int V, int K, float s2, uint64_t seed,
                    const int* __restrict__ req_id, SsWork w, int* __restrict__ out, int* __restrict__ tau) {
-  constexpr int PER = kSsBlock / kSsPickThreads;  // 16
-  const int d = blockIdx.x, tid = threadIdx.x;
+  const int part = blockIdx.x, d = blockIdx.y, tid = threadIdx.x;
   const int R = 2 * K + 1;
   const int code = w.blk[d];
   const int b = code % kSsMaxBlocks;
@@ -474,54 +475,26 @@ __global__ void __launch_bounds__(kSsPickThreads)
     off = d - r * K;
     la = draft + (size_t)d * V;
   }
-  const uint64_t req = (uint64_t)(uint32_t)req_id[r];
-  float za[PER], zb[PER];
-  {
-    // ids b * kSsBlock + (it * 1024 + tid) * 8 + e: consecutive lanes read
-    // consecutive 32-byte runs
-#pragma unroll
-    for (int it = 0; it < PER / 8; ++it) {
-      const int v0 = b * kSsBlock + (it * kSsPickThreads + tid) * 8;
-      float l[8];
-      if (v0 < V) {
-        ss_load8<VEC>(la, v0, V, l);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) l[e] = -INFINITY;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) za[it * 8 + e] = l[e] * s2;
-      if (res) {
-        if (v0 < V) {
-          ss_load8<VEC>(lb, v0, V, l);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) l[e] = -INFINITY;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zb[it * 8 + e] = l[e] * s2;
-      }
-    }
-  }
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  // ids rise within a thread, so a strict > keeps the lowest id of a tie;
-  // entries past V hold -inf and never win
-#pragma unroll
-  for (int it = 0; it < PER / 8; ++it) {
-    const int v0 = b * kSsBlock + (it * kSsPickThreads + tid) * 8;
-    if (v0 >= V) break;
-    uint64_t c[4] = {(uint64_t)(v0 >> 3), (uint64_t)off, req, 0};
+  const int v0 = b * kSsBlock + part * (kSsThreads * 8) + tid * 8;
+  if (v0 < V) {
+    float za[8], zb[8];
+    ss_load8<VEC>(la, v0, V, za);
+    if (res) ss_load8<VEC>(lb, v0, V, zb);
+    uint64_t c[4] = {(uint64_t)(v0 >> 3), (uint64_t)off, (uint64_t)(uint32_t)req_id[r], 0};
     philox4x64_10(c, seed, RESAMPLE ? kSsStreamResample : kSsStreamDraft);
+    // ids rise within a thread, so a strict > keeps the lowest id of a tie;
+    // entries past V hold -inf and never win
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float g = ss_log2_exp(ss_bits(c, e));
       float key;
       if (res) {
-        const float dd = exp2f(za[it * 8 + e] - lse_t) - exp2f(zb[it * 8 + e] - lse_d);
+        const float dd = exp2f(fmaf(za[e], s2, -lse_t)) - exp2f(fmaf(zb[e], s2, -lse_d));
         key = dd > 0.f ? __builtin_amdgcn_logf(dd) - g : -INFINITY;
       } else {
-        key = za[it * 8 + e] - g;
+        key = fmaf(za[e], s2, -g);
       }
       if (key > bv) {
         bv = key;
@@ -529,21 +502,33 @@ __global__ void __launch_bounds__(kSsPickThreads)
       }
     }
   }
-  // work-group argmax (16 waves)
-  __shared__ float sv[kSsPickThreads / 64];
-  __shared__ int si[kSsPickThreads / 64];
+  __shared__ float sv[kSsThreads / 64];
+  __shared__ int si[kSsThreads / 64];
   ss_wave_argmax(bv, bi);
   if ((tid & 63) == 0) {
     sv[tid >> 6] = bv;
     si[tid >> 6] = bi;
   }
   __syncthreads();
-  if (tid == 0) {
-    for (int x = 1; x < kSsPickThreads / 64; ++x)
+  if (tid == 0)
+    for (int x = 1; x < kSsThreads / 64; ++x)
       if (ss_better(sv[x], si[x], bv, bi)) {
         bv = sv[x];
         bi = si[x];
       }
+  int* ctr = RESAMPLE ? w.req_ctr : w.row_ctr;
+  if (!ss_publish(w, d, part, kSsPickParts, make_float4(bv, __int_as_float(bi), 0.f, 0.f), ctr)) return;
+  if (tid >= 64) return;
+  // wave 0 of the last work-group: merge the parts in part order
+  bv = -INFINITY;
+  bi = 0x7fffffff;
+  if (tid < kSsPickParts) {
+    const float4 q = ss_load_part(w, d, tid, kSsPickParts);
+    bv = q.x;
+    bi = __float_as_int(q.y);
+  }
+  ss_wave_argmax(bv, bi);
+  if (tid == 0) {
     const int tok = bv > -INFINITY ? bi : b * kSsBlock;  // no finite key: the block's first id
     if constexpr (RESAMPLE) {
       out[(size_t)d * (K + 1) + n] = tok;
@@ -551,6 +536,7 @@ __global__ void __launch_bounds__(kSsPickThreads)
     } else {
       out[d] = tok;
     }
+    __hip_atomic_store(ctr + d, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 

@@ -307,22 +307,31 @@ int dflash2_conv_attach(dflash_ctx* ctx, const dflash2_conv_layer* layers);
  * rejected position is redrawn and the last position yields the bonus token).
  * Both models' distributions are softmax(logits / T), untruncated.  K = B - 1.
  *
+ * Every categorical draw below ("draw v ~ w") is exact and taken in two
+ * stages: the vocabulary is cut into blocks of 16384 consecutive ids; a block
+ * b is chosen by inverse CDF over the block masses with one uniform u
+ * (cum_{b-1} <= u S < cum_b), then the id within b that maximises
+ * log w_v + G_v, G_v = -log(-log u_v) (ties to the lower id).  So
+ * P(v) = w_v / S, with generator output for one block per draw.  V is at
+ * most 1048576 (EUNSUPPORTED otherwise).
+ *
  * Random numbers come from Philox4x64-10 (Salmon et al., SC 2011) with key
  * (seed, stream) and counter (v / 8, row, req_id[r], 0); entry v takes the top
  * 24 bits k of the high (v even) or low (v odd) 32-bit half of output word
- * (v % 8) / 2, as u = (k + 0.5) 2^-24.  Streams: 0 drafting (row = offset - 1,
- * v = token id), 1 acceptance (row 0, v = offset - 1), 2 replacement / bonus
- * (row 0, v = token id).  A caller advances `seed` per block so that blocks
- * draw afresh; req_id tells requests of one call apart.
+ * (v % 8) / 2, as u = (k + 0.5) 2^-24.  Streams: 0 drafting noise G (row =
+ * offset - 1, v = token id), 1 acceptance (row 0, v = offset - 1),
+ * 2 replacement / bonus noise G (row 0, v = token id), 3 and 4 the block
+ * choice of drafting (row = offset - 1) and of the replacement / bonus (row
+ * 0), v = 0.  A caller advances `seed` per block so that blocks draw afresh;
+ * req_id tells requests of one call apart.
  *
  * Both calls use the ctx workspace (calls sharing a ctx must be ordered on one
  * stream) and leave slot state untouched.  temperature must lie in
  * [1e-4, 1e4] (EINVAL); n_req <= max_batch (ECAPACITY).  Logit rows must hold
  * at least one finite value.  All pointers are device pointers. */
 
-/* Draft by Gumbel-max: cand[r][j-1] = argmax_v (draft_logits[r][j-1][v] / T
- * + G_v), G_v = -log(-log u_v) from stream 0, ties to the lower id, so that
- * cand[r][j-1] ~ softmax(draft_logits[r][j-1] / T).
+/* Draft: cand[r][j-1] ~ softmax(draft_logits[r][j-1] / T), drawn as above
+ * (block from stream 3, noise from stream 0).
  *   draft_logits [n_req, B-1, V] float (e.g. out_logits of dflash_draft_block)
  *   req_id [n_req] int32 >= 0
  *   cand [n_req, B-1] int32 out
@@ -337,10 +346,10 @@ int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float*
  * token after offset j (j = 0: after the anchor).  Walking j = 1..K, x_j =
  * cand[r][j-1] is kept when u_j q_j(x_j) < p_{j-1}(x_j) (u_j from stream 1,
  * the test taken in double from fp32 probabilities); an id outside 0..V-1 is
- * rejected.  At the first rejection j the emitted token is argmax_v
- * (log max(0, p_{j-1}(v) - q_j(v)) + G_v); when all K are kept it is argmax_v
- * (target_logits[r][K][v] / T + G_v) (G from stream 2; a residual that
- * rounding leaves empty falls back to the verifier row's l / T + G).
+ * rejected.  At the first rejection j the emitted token is drawn from
+ * w = max(0, p_{j-1} - q_j); when all K are kept, from p_K (block from
+ * stream 4, noise from stream 2; a residual that rounding leaves empty falls
+ * back to the verifier row p_{j-1}).
  *   draft_logits [n_req, B-1, V] float, target_logits [n_req, B, V] float
  *   cand [n_req, B-1] int32, req_id [n_req] int32 >= 0
  *   draft_lse nullable [n_req, B-1] float: the draft_lse of the

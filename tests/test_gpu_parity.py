@@ -159,6 +159,38 @@ def test_gpu_block_size_two_and_empty_context(tiny):
     g.close()
 
 
+def test_gpu_tiny_max_batch_and_full_slots(tiny):
+    """The largest call the library takes: 64 requests (the per-call limit) in
+    one fusion and one draft, slots permuted against request order, contexts
+    ragged from empty to exactly max_ctx."""
+    import block_diffusion_drafter_fuse_amd as dfa
+    wl, d, w_np = tiny
+    n, max_ctx = 64, 96
+    log("case tiny max batch 64, ctx 0..96")
+    ctxs = [(r * 29) % (max_ctx + 1) for r in range(n)]
+    ctxs[0], ctxs[n - 1] = 0, max_ctx
+    slots = [n - 1 - r for r in range(n)]
+    g = GpuDraft(d, w_np, max_ctx=max_ctx, max_slots=n, max_batch=n)
+    g.fuse(slots, ctxs, hidden_rows(d, wl.seed, [(r, 0, ctxs[r]) for r in range(n)]))
+    for r in range(n):
+        assert g.dr.slot_len(slots[r]) == ctxs[r]
+    o = _oracle_for(d, w_np, wl.seed, list(enumerate(ctxs)))
+    anchors = synth.make_anchors(d, wl.seed, n)
+    ids, _, lg = g.draft(slots, anchors, top_k=4, logits=True)
+    for r in range(n):
+        ref = o.draft(r, int(anchors[r]))["logits"]
+        _compare_request(lg[r], ids[r], ref, d, 0, f"max batch r{r} ctx {ctxs[r]}")
+        _, bad = check_topk(ids[r], ref)
+        assert len(bad) == 0, f"max batch r{r}: top-k mismatch at rows {bad}"
+    # a full slot takes no further row, and the failed call changes nothing
+    with pytest.raises(dfa.DflashError) as e:
+        g.fuse([slots[n - 1]], [1], hidden_rows(d, wl.seed, [(n - 1, max_ctx, 1)]))
+    assert e.value.code == -3 and g.dr.slot_len(slots[n - 1]) == max_ctx
+    ids2, _, _ = g.draft(slots, anchors, top_k=4)
+    assert np.array_equal(ids2, ids)
+    g.close()
+
+
 def test_gpu_capacity_errors_leave_state(tiny):
     import block_diffusion_drafter_fuse_amd as dfa
     wl, d, w_np = tiny

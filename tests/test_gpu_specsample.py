@@ -213,6 +213,7 @@ CASES = [
     ("cold", 2048, 16, 4, 0.05, False),          # near-greedy
     ("misaligned", 4160, 6, 3, 1.0, True),       # element loads
     ("two_blocks", 20480, 6, 3, 1.0, False),     # two sampling blocks, the second a quarter full
+    ("max_batch", 20480, 16, 64, 1.0, False),    # the per-call request limit
 ]
 
 

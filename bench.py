@@ -715,8 +715,9 @@ def main():
         "vs_baseline": None,
         "dtype": d.dtype,
         "data": "synthetic (seeded random-init weights and verifier features)",
-        "config": {"workload": args.workload, "model": d.name, "batch": wl.bs, "block": d.B,
-                   "ctx_sum": sum(wl.ctx), "new_rows": sum(wl.n_new), "top_k": 1},
+        "config": {"workload": args.workload, "batch": wl.bs, "block": d.B, "hidden": d.D,
+                   "draft_layers": d.N, "vocab": d.V, "ctx_sum": sum(wl.ctx), "new_rows": sum(wl.n_new),
+                   "top_k": 1},
         "blocks_per_s": main_res["blocks_per_s"],
         "roofline": main_res["roofline"],
         "step_hbm_roof_frac": main_res["step_hbm_roof_frac"],

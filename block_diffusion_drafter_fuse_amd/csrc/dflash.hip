@@ -405,7 +405,9 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
   }
   if constexpr (ALO)
     launch_tiled<TileLo, T, true>(c, w, a, nrm, epi, st);
-  else if (Epi::kRow || (a.M >= 256 && w.ngroups * 16 >= kWideMinFeatures)) {
+  else if (Epi::kRow || (a.M >= 256 && (w.ngroups * 16 >= kWideMinFeatures ||
+                                         (long)ceil_div(a.M, 256) * ceil_div(w.ngroups, 16) >= kTiledSlots))) {
+    // wide weights, or enough 256 x 256 tiles to fill every CU (many tokens):
     // whole waves of one work-group per CU, times the per-tile cost
     const int mt = ceil_div(a.M, 256);
     const double w256 = ceil_div(mt * ceil_div(w.ngroups, 16), kTiledSlots);

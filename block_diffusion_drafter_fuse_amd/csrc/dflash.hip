@@ -105,6 +105,7 @@ using TileW192 = TileCfg<256, 192, 4, 2, 2>;  // same, 64 x 96 per wave, where i
 // bf16 GEMM with one tile per CU): 256 x 192 takes 0.86 of a 256 x 256 tile.
 constexpr double kW192TileCost = 0.86;
 using TileLo = TileCfg<64, 128, 2, 4, 3>;     // activations as hi + lo planes
+using TileLoWide = TileCfg<128, 256, 2, 4, 2>;  // same, many tokens (every CU filled)
 constexpr int kWideMinFeatures = 16384;
 
 int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
@@ -403,8 +404,12 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
       return;
     }
   }
-  if constexpr (ALO)
-    launch_tiled<TileLo, T, true>(c, w, a, nrm, epi, st);
+  if constexpr (ALO) {
+    if ((long)ceil_div(a.M, TileLoWide::BM) * ceil_div(w.ngroups, TileLoWide::BN / 16) >= kTiledSlots)
+      launch_tiled<TileLoWide, T, true>(c, w, a, nrm, epi, st);
+    else
+      launch_tiled<TileLo, T, true>(c, w, a, nrm, epi, st);
+  }
   else if (Epi::kRow || (a.M >= 256 && (w.ngroups * 16 >= kWideMinFeatures ||
                                          (long)ceil_div(a.M, 256) * ceil_div(w.ngroups, 16) >= kTiledSlots))) {
     // wide weights, or enough 256 x 256 tiles to fill every CU (many tokens):

@@ -261,12 +261,16 @@ def _full_size_case(wl, sample_reqs, label, repeat=False):
     cover = []
     for r in sample_reqs:
         o.fuse(r, synth.as_f32(synth.make_hidden(d, wl.seed, r, 0, wl.ctx[r])))
+        # cache windows: the context's start and, past 4096 rows, the second
+        # fusion chunk (both written by the prefill fusion), and its end (the
+        # step's own rows)
+        n_chk = min(wl.ctx[r], 64)
+        starts = {0, wl.ctx[r] - n_chk} | ({4096} if wl.ctx[r] >= 4096 + n_chk else set())
         for l in (0, d.N - 1):
-            n_chk = min(wl.ctx[r], 64)
-            pos0 = wl.ctx[r] - n_chk
-            k, v = g.read_cache(r, l, pos0, n_chk)
-            assert rel_inf(k, o.cache(r).K[l][:, pos0:]) <= 2e-2
-            assert rel_inf(v, o.cache(r).V[l][:, pos0:]) <= 2e-2
+            for pos0 in sorted(starts):
+                k, v = g.read_cache(r, l, pos0, n_chk)
+                assert rel_inf(k, o.cache(r).K[l][:, pos0:pos0 + n_chk]) <= 2e-2, f"r{r} layer {l} K at {pos0}"
+                assert rel_inf(v, o.cache(r).V[l][:, pos0:pos0 + n_chk]) <= 2e-2, f"r{r} layer {l} V at {pos0}"
         ref = o.draft(r, int(anchors[r]))["logits"]
         err, mask = _compare_request(lg[r], ids[r], ref, d, 2e-2, f"{label} r{r}")
         worst = max(worst, err)

@@ -21,8 +21,10 @@ events recorded by the library on the launch stream over a second pass of the
 timed steps (the step time itself comes from an uninstrumented pass);
 its achieved rate is the kernel's algorithmic bytes (HBM-bound kernels) or
 flops (MFMA-bound) per launch divided by its mean launch time.
-`cpu_baseline` times the float64 CPU oracle on one request of the same
-workload.
+`cpu_baseline` times the float64 CPU oracle on a sample of the same workload's
+requests (evenly spaced context quantiles) and scales it to the whole batch
+step; it records the host CPU count, the BLAS vendor and threads, and one
+single-thread figure.
 """
 from __future__ import annotations
 
@@ -562,41 +564,67 @@ def measure_spec(wl, w_dev, torch, steps, warmup, temperature=1.0):
                     "the drafter row where a draft was rejected)"}
 
 
-def cpu_baseline(wl, w_np, budget_s=20.0):
-    """The float64 oracle, as it stands, on one request of the workload (the
-    one with the shortest context): fuse its new rows, draft its block, accept.
-    Returns blocks/s x B for that single-request stream."""
-    import oracle
-    import synth
+def _blas_info():
+    """(vendor string, thread count) of the BLAS numpy calls."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        infos = [i for i in threadpool_info() if i.get("user_api") == "blas"] or threadpool_info()
+        vendor = ",".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in infos})) or "unknown"
+        threads = max([i.get("num_threads", 1) for i in infos] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        vendor, threads = "unknown", os.cpu_count() or 1
+    return vendor, int(threads)
+
+
+def cpu_baseline(wl, w_np, n_sample=6):
+    """The float64 oracle, as it stands, on a sample of the workload's
+    requests.  The oracle drafts one request at a time, so a step of the whole
+    batch costs the sum of its requests' costs: each sampled request (evenly
+    spaced context quantiles) is timed once over fuse(its new rows) + draft +
+    accept, and the batch step is estimated as bs / n_sample times their sum.
+    One more request (the median context) is timed with BLAS limited to one
+    thread.  Returns drafted tokens/s of the batch (blocks/s x B)."""
+    import oracle
+    import synth
+    vendor, threads = _blas_info()
     d = wl.dims
-    r = int(np.argmin(wl.ctx))
+    order = np.argsort(wl.ctx, kind="stable")
+    k = min(n_sample, wl.bs)
+    pick = sorted({int(order[int(round(i * (wl.bs - 1) / max(k - 1, 1)))]) for i in range(k)})
     w32 = synth.weights_as_f32(w_np)
-    pre = wl.ctx[r] - wl.n_new[r]
-    new = synth.as_f32(synth.make_hidden(d, wl.seed, r, pre, wl.n_new[r]))
-    anchor = int(synth.make_anchors(d, wl.seed, wl.bs)[r])
-    o = oracle.OracleDrafter(w32, d)
-    if pre:
-        o.fuse(r, synth.as_f32(synth.make_hidden(d, wl.seed, r, 0, pre)))
-    times = []
-    t_start = time.perf_counter()
-    while not times or (time.perf_counter() - t_start < budget_s and len(times) < 5):
+    anchors = synth.make_anchors(d, wl.seed, wl.bs)
+
+    def one(r):
+        pre = wl.ctx[r] - wl.n_new[r]
+        o = oracle.OracleDrafter(w32, d)
+        if pre:
+            o.fuse(r, synth.as_f32(synth.make_hidden(d, wl.seed, r, 0, pre)))
+        new = synth.as_f32(synth.make_hidden(d, wl.seed, r, pre, wl.n_new[r]))
         t0 = time.perf_counter()
         o.fuse(r, new)
-        res = o.draft(r, anchor)
+        res = o.draft(r, int(anchors[r]))
         cand, _ = oracle.topk(res["logits"], 1)
         oracle.accept(cand[:, 0], np.zeros(d.B, np.int64))
-        times.append(time.perf_counter() - t0)
-        o.reset(r, pre)
-    t = float(np.median(times))
-    return {"value": round(d.B / t, 3), "unit": "drafted tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"1 request of the workload (ctx {wl.ctx[r]}, {wl.n_new[r]} new rows), "
-                      f"median of {len(times)} float64 steps, {t:.2f} s/step"}
+        return time.perf_counter() - t0
+
+    per = {r: one(r) for r in pick}
+    step_s = sum(per.values()) * wl.bs / len(pick)
+    single = None
+    try:
+        from threadpoolctl import threadpool_limits
+        r1 = int(order[len(order) // 2])
+        with threadpool_limits(limits=1, user_api="blas"):
+            t1 = one(r1)
+        single = {"value": round(d.B / t1, 3), "unit": "drafted tokens/s (one request stream)", "threads": 1,
+                  "sample": f"request with ctx {wl.ctx[r1]}, {t1:.2f} s"}
+    except Exception as e:  # pragma: no cover
+        single = {"error": str(e)}
+    return {"value": round(wl.bs * d.B / step_s, 3), "unit": "drafted tokens/s", "cores": threads,
+            "kind": "oracle", "host_cpus": os.cpu_count(), "blas": vendor, "blas_threads": threads,
+            "sample": f"{len(pick)} of the {wl.bs} requests (contexts {[wl.ctx[r] for r in pick]}), each timed "
+                      f"once over fuse + draft + accept in float64 ({', '.join(f'{per[r]:.2f}' for r in pick)} s); "
+                      f"batch step = {wl.bs}/{len(pick)} x their sum = {step_s:.1f} s",
+            "single_thread": single}
 
 
 def main():

@@ -112,6 +112,11 @@ int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
 
 // Few-token LM head: one 16-wave work-group per CU and 16-row block.
 int lm_chunks_small(int rowblocks) { return std::max(1, 256 / rowblocks); }
+constexpr int kLdsMax = 160 * 1024;  // LDS of one CU
+// LDS of the top-k LM head: 16 staged rows, reused for the 16 x 64 x 16 list merge.
+int lm_small_lds(const dflash_dims& d) {
+  return std::max(16 * (d.D * elt_size(d.dtype) + 16), 16 * 64 * 16 * 8);
+}
 
 // Which GEMM engine serves M rows against a weight of ngroups 16-row groups:
 // few rows, or a narrow weight (it stays in L2 across the 16-row blocks),
@@ -619,7 +624,7 @@ void plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPla
 template <typename T, int KTOP>
 void launch_lm_small(const LmArgs<T>& la, int nchunk, int rowblocks, int* tile_ctr, hipStream_t st) {
   // staged rows, reused afterwards for the 16 x 64 x KTOP list merge
-  const int lds = std::max(16 * (la.a.kseg * (int)sizeof(T) + 16), 16 * 64 * KTOP * 8);
+  const int lds = std::max(16 * (la.a.kseg * (int)sizeof(T) + 16), 16 * 64 * KTOP * 8);  // <= kLdsMax (checked)
   auto kern = lmhead_lds_kernel<T, KTOP, kLmFN, kLmU>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -1077,6 +1082,8 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32
   if (top_k < 1 || top_k > 16) return fail(DFLASH_EUNSUPPORTED, "top_k must be in 1..16");
   if (n_req == 0) return DFLASH_OK;
   if (!anchor || !out_ids) return fail(DFLASH_EINVAL, "anchor and out_ids must not be NULL");
+  if (top_k > 1 && lm_small_lds(ctx->d) > kLdsMax)
+    return fail(DFLASH_EUNSUPPORTED, "top_k > 1 needs 16 rows of D in LDS: D too large for this dtype");
   AttnPlan apl;
   plan_attention(ctx, n_req, slot, &apl);
   const int Mlm = n_req * (ctx->d.B - 1);

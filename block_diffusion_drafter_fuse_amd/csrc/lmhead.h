@@ -45,8 +45,11 @@ struct LmArgs {
 };
 
 // Few-token LM head with the activations staged in LDS: one work-group of
-// 16 waves per CU holds the 16 normed rows [16][D] (rows padded by 16 bytes),
-// so the vector-memory path carries only the weight stream.  Waves take
+// 16 waves per CU holds the 16 normed rows [16][D] (rows padded by 16 bytes,
+// so 16 * (D * sizeof(T) + 16) bytes of LDS, which the host checks against
+// the 160 KB of a CU), so the vector-memory path carries only the weight
+// stream.  Any D that is a multiple of the MFMA k-step is handled (the k-loop
+// is unrolled by U with a remainder loop).  Waves take
 // 16*FN-row vocabulary tiles from a per-launch atomic counter (reset by the
 // merge kernel) and keep a running top-KTOP per lane; the lists are merged
 // per work-group in LDS.  The partial lists depend on which wave took which
@@ -96,7 +99,8 @@ __global__ __launch_bounds__(1024) void lmhead_lds_kernel(const LmArgs<T> p, int
     f32x4_t acc[FN];
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) acc[fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int ks = 0; ks < nks; ks += U) {
+    const int nks_u = nks - nks % U;  // whole unrolled batches, then the k-steps left over
+    for (int ks = 0; ks < nks_u; ks += U) {
       uint4 wf[U][FN], af[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
@@ -108,6 +112,11 @@ __global__ __launch_bounds__(1024) void lmhead_lds_kernel(const LmArgs<T> p, int
       for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fn] = MM::step(wf[u][fn], af[u], acc[fn]);
+    }
+    for (int ks = nks_u; ks < nks; ++ks) {
+      const uint4 af = *reinterpret_cast<const uint4*>(abase + ks * 64);
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fn] = MM::step(ld16_stream(wp[fn] + ks * KS), af, acc[fn]);
     }
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn) {

@@ -119,8 +119,11 @@ typedef struct dflash_weights {
 typedef struct dflash_ctx dflash_ctx;
 
 /* Byte sizes of the two caller-allocated device buffers for `dims`: the KV
- * pool (projected context K/V of every slot and the RoPE table; persistent) and the workspace (per-call scratch).  Pure host
- * computation.  Returns DFLASH_OK or DFLASH_EINVAL / DFLASH_EUNSUPPORTED. */
+ * pool (projected context K/V of every slot and the RoPE table; persistent)
+ * and the workspace (per-call scratch, sized for dims->max_batch requests per
+ * call: the batch capacity is part of the dims, so that dflash_create checks
+ * the buffers against the same figure).  Pure host computation.  Returns
+ * DFLASH_OK or DFLASH_EINVAL / DFLASH_EUNSUPPORTED. */
 int dflash_query_sizes(const dflash_dims* dims, size_t* kv_pool_bytes, size_t* workspace_bytes);
 
 /* Create a context over caller-owned buffers.  kv_pool and workspace must be
@@ -148,8 +151,14 @@ int dflash_fuse_ctx(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t*
 /* Draft one block per request.
  *   slot [host, n_req]     slot ids (distinct); the block of request r sits at
  *                          absolute positions len(slot[r]) .. + B-1
- *   anchor [n_req] int32   anchor token per request (device)
- *   top_k                  1..16
+ *   anchor [n_req] int32   anchor token per request (device); the anchors are
+ *                          read by a kernel, so an id outside 0..V-1 cannot be
+ *                          reported as an error: it is clamped into 0..V-1
+ *                          (the caller is responsible for valid ids)
+ *   top_k                  1..16; top_k > 1 stages 16 rows of D in one CU's
+ *                          LDS (16 * (D * elt + 16) bytes <= 160 KB, so D <= 5056
+ *                          for bf16 and D <= 2496 for fp32; EUNSUPPORTED
+ *                          beyond)
  *   out_ids [n_req, B-1, top_k] int32: per block offset 1..B-1, ids ordered by
  *                          (logit descending, id ascending)
  *   out_vals  nullable [n_req, B-1, top_k] float: the matching logits
@@ -173,9 +182,12 @@ int dflash_draft_block(dflash_ctx* ctx, void* stream, int32_t n_req, const int32
 int dflash_accept(void* stream, int32_t n_req, int32_t B, const int32_t* cand,
                   int32_t cand_stride, const int32_t* target, int32_t* tau, int32_t* bonus);
 
-/* Rewind (or confirm) a slot: set its length to keep_len <= current length.
- * Host-side bookkeeping only; cached entries past keep_len are ignored and
- * overwritten by later appends. */
+/* Rewind (or confirm) a slot: set its length to keep_len <= current length
+ * ("DFlash 投机解码：块扩散草稿与 KV 注入", section 四: after verification the
+ * draft cache is rolled back to the committed prefix, rewind_kv in the
+ * dflash_cycle pseudocode).  Host-side bookkeeping only; cached entries past
+ * keep_len are ignored and overwritten by later appends; a stored DFlow relay
+ * of the slot is dropped. */
 int dflash_slot_reset(dflash_ctx* ctx, int32_t slot, int32_t keep_len);
 
 /* Current fused length of a slot. */

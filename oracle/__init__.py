@@ -56,8 +56,10 @@ from .dflash import (  # noqa: F401
     block_attention,
     draft_block,
     fuse_context,
+    normed_stored,
     project_context_kv,
     rms_norm,
+    round_bf16,
     rope,
     swiglu_ffn,
     topk,

@@ -102,6 +102,29 @@ def block_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, G: int) -> np.n
     return out.reshape(B, Hq * hd)
 
 
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Round to the nearest bfloat16 value (ties to even), through float32,
+    returned as float64: the storage precision of a bf16 drafter's activations
+    (weights already hold bf16 values).  bfloat16 keeps the top 16 bits of the
+    float32 pattern; adding 0x7FFF plus the lowest kept bit before truncation
+    rounds to nearest, ties to even.  Finite inputs only."""
+    b = np.ascontiguousarray(np.asarray(a, dtype=np.float32)).view(np.uint32).astype(np.uint64)
+    b = (b + np.uint64(0x7FFF) + ((b >> np.uint64(16)) & np.uint64(1))) & np.uint64(0xFFFF0000)
+    return b.astype(np.uint32).view(np.float32).astype(F)
+
+
+def normed_stored(x: np.ndarray, g: np.ndarray, eps: float, store) -> np.ndarray:
+    """RMSNorm with the normed operand held in storage precision: the gained
+    row x * g is what is stored (rounded by `store`), and the per-row factor
+    1 / sqrt(mean(x^2) + eps) applies to the stored values (a per-row scalar
+    commutes with the projection that reads them).  store=None gives rms_norm."""
+    if store is None:
+        return rms_norm(x, g, eps)
+    x = _f64(x)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return store(x * _f64(g)) / np.sqrt(ms + eps)
+
+
 def silu(x: np.ndarray) -> np.ndarray:
     return x / (1.0 + np.exp(-x))
 
@@ -160,7 +183,7 @@ class ContextCache:
 # --------------------------------------------------------------------------
 
 def draft_block(w: dict, d, cache: ContextCache, anchor: int,
-                block_inputs: Optional[np.ndarray] = None, conv=None) -> dict:
+                block_inputs: Optional[np.ndarray] = None, conv=None, store=None) -> dict:
     """One-pass block draft over the cached context.
 
     DFlash page, section 二 (block [anchor, mask x (B-1)]; one forward pass, no
@@ -179,8 +202,18 @@ def draft_block(w: dict, d, cache: ContextCache, anchor: int,
     before the residual add, normed FFN input, FFN output before the residual
     add); see oracle.dflash2.draft_block_conv.
 
+    store: None (every activation in float64), or a rounding function for
+    the activations a bf16 drafter stores between its projections (the pages
+    fix no precision; a bf16 drafter keeps its activations in bf16 with fp32
+    sums): the context K/V, the rotated Q / K_b / V_b, the attention output,
+    the gained normed operands (normed_stored), the SwiGLU product and the
+    final normed state.  Token-id decisions on a bf16 drafter are compared in
+    that precision; the residual stream and every sum stay float64.
+
     Returns dict with "logits" [B-1, V], "hidden" [B, D] (final residual
     stream) and "x0" [B, D] (block input)."""
+    assert store is None or conv is None, "storage rounding is defined for the plain drafter"
+    st = (lambda v: v) if store is None else store
     B = d.B
     if block_inputs is None:
         x = np.stack([_f64(w["embed"][anchor])] + [_f64(w["e_mask"])] * (B - 1))
@@ -192,20 +225,24 @@ def draft_block(w: dict, d, cache: ContextCache, anchor: int,
     ident = (lambda v: v,) * 4
     for l, layer in enumerate(w["layers"]):
         c_attn_in, c_attn_out, c_ffn_in, c_ffn_out = ident if conv is None else conv[l]
-        u = c_attn_in(rms_norm(x, layer["g_attn"], d.rms_eps))
+        u = c_attn_in(normed_stored(x, layer["g_attn"], d.rms_eps, store))
         q = (u @ _f64(layer["w_q"]).T).reshape(B, d.Hq, d.hd).transpose(1, 0, 2)
         kb = (u @ _f64(layer["w_kb"]).T).reshape(B, d.Hkv, d.hd).transpose(1, 0, 2)
         vb = (u @ _f64(layer["w_vb"]).T).reshape(B, d.Hkv, d.hd).transpose(1, 0, 2)
         if d.use_rope:
             q = rope(q, pos, d.rope_base)
             kb = rope(kb, pos, d.rope_base)
-        K = np.concatenate([cache.K[l], kb], axis=1)
-        V = np.concatenate([cache.V[l], vb], axis=1)
-        o = block_attention(q, K, V, d.G)
+        K = np.concatenate([st(cache.K[l]), st(kb)], axis=1)
+        V = np.concatenate([st(cache.V[l]), st(vb)], axis=1)
+        o = st(block_attention(st(q), K, V, d.G))
         x = x + c_attn_out(o @ _f64(layer["w_o"]).T)
-        u = c_ffn_in(rms_norm(x, layer["g_ffn"], d.rms_eps))
-        x = x + c_ffn_out(swiglu_ffn(u, layer))
-    h = rms_norm(x[1:], w["g_final"], d.rms_eps)
+        u = c_ffn_in(normed_stored(x, layer["g_ffn"], d.rms_eps, store))
+        if store is None:
+            x = x + c_ffn_out(swiglu_ffn(u, layer))
+        else:
+            hh = st(silu(u @ _f64(layer["w_gate"]).T) * (u @ _f64(layer["w_up"]).T))
+            x = x + hh @ _f64(layer["w_down"]).T
+    h = normed_stored(x[1:], w["g_final"], d.rms_eps, store)
     logits = h @ _f64(w["w_lm"]).T
     return {"logits": logits, "hidden": x, "x0": x0}
 
@@ -261,8 +298,8 @@ class OracleDrafter:
     def fuse(self, r: int, hidden: Sequence[np.ndarray]) -> np.ndarray:
         return self.cache(r).append(self.w, self.d, hidden)
 
-    def draft(self, r: int, anchor: int) -> dict:
-        return draft_block(self.w, self.d, self.cache(r), anchor)
+    def draft(self, r: int, anchor: int, store=None) -> dict:
+        return draft_block(self.w, self.d, self.cache(r), anchor, store=store)
 
     def reset(self, r: int, keep: int) -> None:
         self.cache(r).truncate(keep)

@@ -244,3 +244,52 @@ def tau_distribution(q: np.ndarray, p: np.ndarray) -> np.ndarray:
         run *= beta[n]
     out[K] = run
     return out
+
+
+# --------------------------------------------------------------------------
+# Plain definitions (no two-stage draw, no generator): the distributions the
+# sampling step must produce, written out from the rejection rule itself.
+# --------------------------------------------------------------------------
+
+def draft_distribution(draft_row: np.ndarray, temp: float) -> np.ndarray:
+    """Distribution of a drafted token: softmax(l / T) over the whole
+    vocabulary (the drafter's temperature-T distribution)."""
+    return softmax(draft_row, temp)
+
+
+def emitted_first_token_plain(q: np.ndarray, p: np.ndarray) -> np.ndarray:
+    """Distribution of the first token the rejection rule emits, from its
+    definition: the draft x ~ q is kept with probability min(1, p(x) / q(x));
+    otherwise the token is drawn from norm(max(0, p - q)).  So
+      P(v) = q(v) min(1, p(v) / q(v)) + P(reject) max(0, p(v) - q(v)) / Z,
+      P(reject) = 1 - sum_x q(x) min(1, p(x) / q(x)),  Z = sum max(0, p - q).
+    (Its value is p itself, the losslessness of the rule.)"""
+    q = np.asarray(q, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        keep = np.where(q > 0, np.minimum(1.0, p / np.where(q > 0, q, 1.0)), 0.0)
+    kept = q * keep
+    reject = 1.0 - kept.sum()
+    w = np.maximum(p - q, 0.0)
+    z = w.sum()
+    return kept + (reject * w / z if z > 0 else 0.0)
+
+
+def tau_distribution_plain(q: np.ndarray, p: np.ndarray) -> np.ndarray:
+    """Distribution of tau (kept drafts + 1) from the definition, when every
+    offset j drafts from q_j and is checked against p_{j-1} independently of
+    the prefix: offset j survives with probability
+    a_j = sum_x q_j(x) min(1, p_{j-1}(x) / q_j(x)), and the walk stops at the
+    first offset that does not survive (tau = K + 1 when all K survive)."""
+    q = np.asarray(q, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    K = q.shape[0]
+    a = np.array([float(np.sum(q[j] * np.minimum(1.0, p[j] / np.where(q[j] > 0, q[j], 1.0))))
+                  for j in range(K)])
+    out = np.zeros(K + 1)
+    alive = 1.0
+    for j in range(K):
+        out[j] = alive * (1.0 - a[j])
+        alive *= a[j]
+    out[K] = alive
+    return out

@@ -8,7 +8,9 @@ each side computes the gates from its own final hidden states.  Bars: every
 pair score rel <= 1e-4 (fp32, max-norm per request), the chosen path equal to
 the oracle's at every position whose walk step wins by more than 1e-3 (the
 comparison of a request stops at the first closer step, where the walks may
-part), and the top-16 lists equal where the oracle's gaps exceed 0.05."""
+part), and the top-16 lists equal where the oracle's gaps exceed 0.05 (for a
+bf16 drafter the oracle takes its candidates in the drafter's storage
+precision, oracle.round_bf16)."""
 import dataclasses
 
 import numpy as np
@@ -47,8 +49,10 @@ def _run(d, seed, bs, ctx, tables_np, zero_a=False, check_top16=True):
     cand = np.zeros((bs, d.B - 1, K), np.int32)
     u = np.zeros((bs, d.B - 1, K), np.float32)
     ref = []
+    # bf16: candidate decisions in the drafter's storage precision
+    store = oracle.round_bf16 if d.dtype == "bf16" else None
     for r in slots:
-        out = o.draft(r, int(anchors[r]))
+        out = o.draft(r, int(anchors[r]), store=store)
         if check_top16:
             _, bad = check_topk(ids[r], out["logits"])
             assert len(bad) == 0, f"req {r}: top-16 mismatch at {bad[:5]}"
@@ -117,5 +121,5 @@ def test_gpu_selector_bf16_qwen3_4b_shape():
     d = QWEN3_4B
     log("case dflash2 selector, Qwen3-4B shape bf16")
     tables = synth.make_selector_weights(d, 8)
-    cand, u, path, scores, ref = _run(d, 8, 2, 96, tables, check_top16=False)
-    _compare(d, 2, path, scores, ref, 2e-2, margin=0.1)
+    cand, u, path, scores, ref = _run(d, 8, 2, 96, tables)
+    _compare(d, 2, path, scores, ref, 2e-2, margin=0.05)

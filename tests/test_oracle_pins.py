@@ -301,3 +301,64 @@ def test_whole_forward_tiny_config_equals_library_form():
     got = o.draft(0, 321)["logits"]
     ref = lf.forward(w, d, hid, 321)
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+
+
+# ---- storage precision (bf16 activations) for token-id decisions
+
+def test_round_bf16_matches_torch_conversion():
+    """oracle.round_bf16 equals torch's float32 -> bfloat16 conversion (round
+    to nearest, ties to even) on random values, exact ties and tiny values."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000) * 10.0 ** rng.integers(-30, 30, 20000),
+                        rng.standard_normal(1000) * 1e-39]).astype(np.float32)
+    # exact ties: the 16 dropped bits are 0x8000, with odd and even kept bits
+    ties = (np.arange(1000, dtype=np.uint32) << np.uint32(16)) | np.uint32(0x8000)
+    x = np.concatenate([x, (ties + np.uint32(0x3F800000)).view(np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy().astype(np.float64)
+    assert np.array_equal(oracle.round_bf16(x), ref)
+
+
+def test_storage_hook_identity_is_the_plain_draft():
+    """With an identity rounding the storage form equals the plain draft (up to
+    float64 rounding of the regrouped RMSNorm)."""
+    d = _tiny_dims()
+    w = synth.weights_as_f32(synth.make_weights(d, 3))
+    c = oracle.ContextCache.empty(d)
+    c.append(w, d, synth.as_f32(synth.make_hidden(d, 3, 0, 0, 20)))
+    a = oracle.draft_block(w, d, c, 9)["logits"]
+    b = oracle.draft_block(w, d, c, 9, store=lambda v: v)["logits"]
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+    assert np.allclose(oracle.normed_stored(a, np.ones(a.shape[1]), 1e-6, None),
+                       oracle.rms_norm(a, np.ones(a.shape[1]), 1e-6))
+
+
+def test_storage_rounding_touches_each_stored_activation():
+    """The rounding applies to what a bf16 drafter stores between its
+    projections, and to nothing else: per layer the context K and V, the
+    rotated Q / K_b / V_b, the attention output, the gained attention and FFN
+    operands and the SwiGLU product, then the final gained state."""
+    d = _tiny_dims()
+    w = synth.weights_as_f32(synth.make_weights(d, 4))
+    c = oracle.ContextCache.empty(d)
+    c.append(w, d, synth.as_f32(synth.make_hidden(d, 4, 0, 0, 12)))
+    seen = []
+
+    def rec(v):
+        seen.append(tuple(np.shape(v)))
+        return oracle.round_bf16(v)
+
+    plain = oracle.draft_block(w, d, c, 2)["logits"]
+    got = oracle.draft_block(w, d, c, 2, store=rec)["logits"]
+    B, ctx = d.B, 12
+    per_layer = [(B, d.D), (d.Hkv, ctx, d.hd), (d.Hkv, B, d.hd), (d.Hkv, ctx, d.hd), (d.Hkv, B, d.hd),
+                 (d.Hq, B, d.hd), (B, d.Hq * d.hd), (B, d.D), (B, d.I)]
+    assert seen == per_layer * d.N + [(B - 1, d.D)]
+    # bf16 storage moves the logits by about the bf16 unit, not more
+    rel = np.abs(got - plain).max() / np.abs(plain).max()
+    assert 1e-5 < rel < 3e-2
+
+
+def _tiny_dims():
+    from synth.configs import _tiny
+    return _tiny()

@@ -204,3 +204,60 @@ def test_two_stage_draw_across_blocks():
         v = ss.two_stage_draw(logw, s_, ss.STREAM_DRAFT_BLOCK, ss.STREAM_DRAFT, 0, 0)
         cnt[int(np.flatnonzero(ids == v)[0])] += 1
     assert np.all(np.abs(cnt / n - want) <= _mc_bound(want, n))
+
+
+# ---- plain definitions (the distributions the GPU's draws are tested against)
+
+@pytest.mark.parametrize("V,seed", [(5, 0), (64, 1), (1024, 2)])
+def test_plain_emitted_token_is_the_verifier_distribution(V, seed):
+    """The rejection rule's first emitted token follows p exactly (the
+    losslessness the pages attribute to rejection sampling), also where q or p
+    has zeros, and the grid form of the same sum agrees."""
+    rng = np.random.default_rng(seed)
+    q = rng.dirichlet(np.full(V, 0.3))
+    p = rng.dirichlet(np.full(V, 0.3))
+    q[rng.integers(0, V, size=max(1, V // 5))] = 0.0
+    q /= q.sum()
+    p[rng.integers(0, V, size=max(1, V // 7))] = 0.0
+    p /= p.sum()
+    got = ss.emitted_first_token_plain(q, p)
+    assert np.allclose(got, p, atol=1e-12, rtol=0)
+    assert np.allclose(got, ss.first_token_distribution(q, p), atol=2e-4)
+    # q = p keeps every draft: the emitted token is the draft itself
+    assert np.allclose(ss.emitted_first_token_plain(p, p), p, atol=1e-15)
+
+
+def test_plain_draft_distribution_is_softmax_at_temperature():
+    l = np.array([0.0, 1.0, 2.0, -1.0])
+    for T in (0.5, 1.0, 3.0):
+        e = np.exp(l / T)
+        assert np.allclose(ss.draft_distribution(l, T), e / e.sum(), rtol=1e-14)
+
+
+@pytest.mark.parametrize("K", [1, 3, 7])
+def test_plain_tau_distribution_matches_product_form_and_enumeration(K):
+    """tau from the definition equals the product form prod beta (1 - beta)
+    with beta_j = sum min(q_j, p_{j-1}), and, for a 3-token vocabulary, the
+    brute-force sum over every drafted sequence of its keep probabilities."""
+    rng = np.random.default_rng(K)
+    V = 3
+    q = rng.dirichlet(np.ones(V), size=K)
+    p = rng.dirichlet(np.ones(V), size=K + 1)
+    plain = ss.tau_distribution_plain(q, p)
+    assert np.isclose(plain.sum(), 1.0)
+    assert np.allclose(plain, ss.tau_distribution(q, p), atol=1e-14)
+    import itertools
+    brute = np.zeros(K + 1)
+    for xs in itertools.product(range(V), repeat=K):
+        # drafted sequence xs: the walk keeps offsets 1..n and stops at n+1
+        # (drafts after the stop only carry their own probability)
+        for n in range(K + 1):
+            prob = 1.0
+            for j in range(n):
+                prob *= q[j][xs[j]] * min(1.0, p[j][xs[j]] / q[j][xs[j]])
+            if n < K:
+                prob *= q[n][xs[n]] * (1.0 - min(1.0, p[n][xs[n]] / q[n][xs[n]]))
+                for j in range(n + 1, K):
+                    prob *= q[j][xs[j]]
+            brute[n] += prob
+    assert np.allclose(brute, plain, atol=1e-12)

@@ -313,27 +313,31 @@ def _full_size_case(wl, sample_reqs, label, tau_kind, repeat=False):
         cand_for_targets[r] = oracle.topk(ref_s, 1)[0][:, 0]
         ref_masks[r] = mask
         o.caches.pop(r)
-    m = synth.draw_first_mismatch(tau_kind, bs, d.B, wl.seed)
-    tgt = synth.make_targets(cand_for_targets, m, d.V, wl.seed)
-    tau, bonus = g.accept(ids, 1, tgt)
-    for r in range(bs):
-        # the scan itself: bit-exact on the GPU's own candidates
-        assert (int(tau[r]), int(bonus[r])) == oracle.accept(ids[r, :, 0], tgt[r]), f"{label} r{r}: scan"
-        assert 1 <= tau[r] <= d.B
-    n_tau = 0
-    for r in sample_reqs:
-        # tau and the bonus against the oracle's step, wherever every candidate
-        # position up to the oracle's tau clears the margin
-        tau_ref, bonus_ref = oracle.accept(cand_for_targets[r], tgt[r])
-        assert tau_ref == m[r] + 1
-        if ref_masks[r][:min(tau_ref, d.B - 1)].all():
-            assert (int(tau[r]), int(bonus[r])) == (tau_ref, bonus_ref), f"{label} r{r}: tau/bonus"
-            n_tau += 1
+    # acceptance rounds: tau drawn with the workload's recipe, sixteen target
+    # sets per step (each a fresh draw of the first mismatch)
+    n_tau, taus = 0, []
+    for k in range(16):
+        m = synth.draw_first_mismatch(tau_kind, bs, d.B, wl.seed + 100 * k)
+        tgt = synth.make_targets(cand_for_targets, m, d.V, wl.seed + 100 * k)
+        tau, bonus = g.accept(ids, 1, tgt)
+        for r in range(bs):
+            # the scan itself: bit-exact on the GPU's own candidates
+            assert (int(tau[r]), int(bonus[r])) == oracle.accept(ids[r, :, 0], tgt[r]), f"{label} r{r}: scan"
+            assert 1 <= tau[r] <= d.B
+        for r in sample_reqs:
+            # tau and the bonus against the oracle's step, wherever every
+            # candidate position up to the oracle's tau clears the margin
+            tau_ref, bonus_ref = oracle.accept(cand_for_targets[r], tgt[r])
+            assert tau_ref == m[r] + 1
+            if ref_masks[r][:min(tau_ref, d.B - 1)].all():
+                assert (int(tau[r]), int(bonus[r])) == (tau_ref, bonus_ref), f"{label} r{r}: tau/bonus"
+                n_tau += 1
+                taus.append(tau_ref)
+    assert n_tau > 0, f"{label}: no acceptance round had every position up to tau above the margin"
     log(f"case {label}: worst logit err {worst:.3e} (plain oracle), max |diff| {worst_s:.4f} against the "
         f"storage-precision oracle; top-1 ids equal to the plain oracle's on {plain_agree} (equal, compared) rows; "
-        f"margin coverage {np.mean(cover):.2f}, "
-        f"tau compared on {n_tau}/{len(sample_reqs)} sampled requests (tau drawn {tau_kind}: "
-        f"{[int(m[r]) + 1 for r in sample_reqs]})")
+        f"margin coverage {np.mean(cover):.2f}; tau and bonus equal to the oracle's in {n_tau} of "
+        f"{16 * len(sample_reqs)} request rounds (tau drawn {tau_kind}; compared values {sorted(taus)})")
     g.close()
 
 

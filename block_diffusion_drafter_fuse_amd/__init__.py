@@ -22,7 +22,7 @@ STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",
 EXPORTED = ("dflash_query_sizes", "dflash_create", "dflash_destroy", "dflash_fuse_ctx",
             "dflash_draft_block", "dflash_accept", "dflash_slot_reset", "dflash_slot_len",
             "dflash_read_cache", "dflow_relay", "dflow_read_relay", "dflash2_select", "dflash2_conv_attach",
-            "dflash_spec_draft", "dflash_spec_verify", "dflash_profile_enable",
+            "dflash_spec_draft", "dflash_spec_draft_static", "dflash_spec_verify", "dflash_profile_enable",
             "dflash_profile_read", "dflash_strerror", "dflash_last_error")
 
 KERNEL_KINDS = ("fuse_gemm", "fuse_norm", "ctx_kv_gemm", "embed", "norm", "qkv_gemm", "attention",
@@ -106,6 +106,7 @@ def lib() -> ctypes.CDLL:
     u64, f32 = ctypes.c_uint64, ctypes.c_float
     L.dflash_spec_draft.argtypes = [vp, vp, i32, vp, f32, u64, vp, vp, vp]
     L.dflash_spec_verify.argtypes = [vp, vp, i32, vp, vp, vp, vp, f32, u64, vp, vp, vp]
+    L.dflash_spec_draft_static.argtypes = [vp, i32, i32, i32, vp, f32, u64, vp, vp, vp]
     L.dflash_profile_enable.argtypes = [vp, ctypes.c_uint32, i32]
     L.dflash_profile_read.argtypes = [vp, P(ctypes.c_double), P(i32)]
     L.dflash_strerror.argtypes = [ctypes.c_int]
@@ -296,6 +297,15 @@ class Drafter:
     def read_cache(self, slot: int, layer: int, pos0: int, n: int, k_out, v_out, stream=None):
         _check(lib().dflash_read_cache(self.h, _stream(stream), int(slot), int(layer), int(pos0), int(n),
                                        _ptr(k_out), _ptr(v_out)), "dflash_read_cache")
+
+
+def spec_draft_static(n_req: int, V: int, B: int, draft_logits, temperature: float, seed: int, req_id, cand,
+                      draft_lse=None, stream=None):
+    """dflash_spec_draft_static: dflash_spec_draft without a ctx or workspace
+    (a fixed per-GPU scratch; allocates nothing)."""
+    _check(lib().dflash_spec_draft_static(_stream(stream), int(n_req), int(V), int(B), _ptr(draft_logits),
+                                          float(temperature), int(seed), _ptr(req_id), _ptr(cand), _ptr(draft_lse)),
+           "dflash_spec_draft_static")
 
 
 def accept(n_req: int, B: int, cand, cand_stride: int, target, tau, bonus, stream=None):

@@ -21,6 +21,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1288,6 +1289,55 @@ int ss_mass_per(int V, int rows) {
 
 }  // namespace
 
+}  // extern "C"
+
+namespace {
+
+// The two drafting kernels (block masses with the block choice, then the
+// Gumbel-max within the chosen block) over n_req * K rows, on scratch `w`
+// (part, row_ctr with zero tickets, blk).
+void launch_spec_draft(const SsWork& w, hipStream_t st, int n_req, int V, int K, const float* draft_logits,
+                       float s2, uint64_t seed, const int32_t* req_id, int32_t* cand, float* draft_lse) {
+  const bool vec = V % 4 == 0 && aligned16(draft_logits);
+  const int per = ss_mass_per(V, n_req * K);
+  const int np = ceil_div(V, kSsThreads * per);
+  SS_MASS(ss_draft_mass_kernel, vec, per, n_req * K, st, draft_logits, V, K, np, s2, seed, req_id, w, draft_lse);
+  const dim3 g(kSsPickParts, n_req * K), b(kSsThreads);
+  if (vec)
+    hipLaunchKernelGGL((ss_pick_kernel<true, false>), g, b, 0, st, draft_logits, nullptr, nullptr, V, K, s2, seed,
+                       req_id, w, cand, nullptr);
+  else
+    hipLaunchKernelGGL((ss_pick_kernel<false, false>), g, b, 0, st, draft_logits, nullptr, nullptr, V, K, s2, seed,
+                       req_id, w, cand, nullptr);
+}
+
+// Scratch of dflash_spec_draft_static, for callers that cannot allocate: the
+// per-piece partials of up to kStaticRows drafted rows (pieces of 2048 ids,
+// up to kStaticMaxV ids), the row tickets and the chosen blocks.  Each GPU
+// holds its own copy until the process ends; host code reaches it only
+// through the address hipGetSymbolAddress returns on that device.
+constexpr int kStaticMaxV = 262144;
+constexpr int kStaticRows = kMaxReq * 15;  // n_req <= 64, B <= 16
+constexpr int kStaticPieces = kStaticMaxV / (kSsThreads * 8);
+constexpr size_t kStaticPartBytes = (size_t)kStaticRows * kStaticPieces * sizeof(float4);
+constexpr size_t kStaticBytes = kStaticPartBytes + 2 * (size_t)kStaticRows * sizeof(int);
+constexpr int kMaxDevices = 64;
+static_assert(kStaticPieces >= kSsPickParts, "block-draw parts fit the per-row partial slots");
+
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kStaticBytes];
+
+extern "C" {
+
 int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits, float temperature,
                       uint64_t seed, const int32_t* req_id, int32_t* cand, float* draft_lse) {
   g_last_error.clear();
@@ -1297,23 +1347,53 @@ int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float*
   if (rc) return rc;
   if (n_req == 0) return DFLASH_OK;
   if (!draft_logits || !cand) return fail(DFLASH_EINVAL, "NULL argument");
-  const int V = ctx->d.V, K = ctx->d.B - 1;
-  const bool vec = V % 4 == 0 && aligned16(draft_logits);
-  const int per = ss_mass_per(V, n_req * K);
-  const int np = ceil_div(V, kSsThreads * per);
   hipStream_t st = static_cast<hipStream_t>(stream);
   {
     ProfScope ps(ctx, DFLASH_K_SPEC_DRAFT, st);
-    SS_MASS(ss_draft_mass_kernel, vec, per, n_req * K, st, draft_logits, V, K, np, s2, seed, req_id, w, draft_lse);
-    const dim3 g(kSsPickParts, n_req * K), b(kSsThreads);
-    if (vec)
-      hipLaunchKernelGGL((ss_pick_kernel<true, false>), g, b, 0, st, draft_logits, nullptr, nullptr, V, K, s2, seed,
-                         req_id, w, cand, nullptr);
-    else
-      hipLaunchKernelGGL((ss_pick_kernel<false, false>), g, b, 0, st, draft_logits, nullptr, nullptr, V, K, s2, seed,
-                         req_id, w, cand, nullptr);
+    launch_spec_draft(w, st, n_req, ctx->d.V, ctx->d.B - 1, draft_logits, s2, seed, req_id, cand, draft_lse);
   }
   if (!hip_ok(hipGetLastError(), "spec_draft launch", &rc)) return rc;
+  return DFLASH_OK;
+}
+
+int dflash_spec_draft_static(void* stream, int32_t n_req, int32_t V, int32_t B, const float* draft_logits,
+                             float temperature, uint64_t seed, const int32_t* req_id, int32_t* cand,
+                             float* draft_lse) {
+  g_last_error.clear();
+  if (n_req < 0) return fail(DFLASH_EINVAL, "n_req must be >= 0");
+  if (n_req > kMaxReq) return fail(DFLASH_ECAPACITY, "n_req exceeds 64 (the static scratch holds 64 x 15 rows)");
+  if (B < 2 || B > 16) return fail(DFLASH_EUNSUPPORTED, "block size must be in 2..16");
+  if (V < 1) return fail(DFLASH_EINVAL, "V must be >= 1");
+  if (V > kStaticMaxV) return fail(DFLASH_ECAPACITY, "V exceeds 262144 (the static scratch limit)");
+  if (!(temperature >= 1e-4f && temperature <= 1e4f))
+    return fail(DFLASH_EINVAL, "temperature must be in [1e-4, 1e4]");
+  if (n_req == 0) return DFLASH_OK;
+  if (!draft_logits || !cand || !req_id) return fail(DFLASH_EINVAL, "NULL argument");
+  int rc = DFLASH_OK;
+  int dev = -1;
+  if (!hip_ok(hipGetDevice(&dev), "hipGetDevice", &rc)) return rc;
+  if (dev < 0 || dev >= kMaxDevices) return fail(DFLASH_EUNSUPPORTED, "device index beyond 63");
+  char* base = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+      void* p = nullptr;
+      if (!hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)", &rc)) return rc;
+      g_scratch_dev[dev] = static_cast<char*>(p);
+    }
+    base = g_scratch_dev[dev];
+  }
+  SsWork w{};
+  w.part = reinterpret_cast<float4*>(base);
+  w.row_ctr = reinterpret_cast<int*>(base + kStaticPartBytes);
+  w.blk = w.row_ctr + kStaticRows;
+  const int K = B - 1, rows = n_req * K;
+  const float s2 = (float)(1.4426950408889634 / (double)temperature);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the array keeps the previous call's contents: the tickets start at zero here
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(ceil_div(rows, 256)), dim3(256), 0, st, w.row_ctr, rows);
+  launch_spec_draft(w, st, n_req, V, K, draft_logits, s2, seed, req_id, cand, draft_lse);
+  if (!hip_ok(hipGetLastError(), "spec_draft_static launch", &rc)) return rc;
   return DFLASH_OK;
 }
 

@@ -352,6 +352,24 @@ int dflash2_conv_attach(dflash_ctx* ctx, const dflash2_conv_layer* layers);
 int dflash_spec_draft(dflash_ctx* ctx, void* stream, int32_t n_req, const float* draft_logits, float temperature,
                       uint64_t seed, const int32_t* req_id, int32_t* cand, float* draft_lse);
 
+/* Drafting as dflash_spec_draft, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): no ctx and no workspace.  The kernels' scratch (per-piece
+ * partials, row tickets, chosen blocks) is a fixed array of about 2 MB that
+ * each GPU holds for the life of the process; the call allocates nothing.
+ * Sizes come as arguments: n_req <= 64 (ECAPACITY beyond), B in 2..16
+ * (EUNSUPPORTED), V in 1..262144 (ECAPACITY beyond).  Same draws, same
+ * outputs as dflash_spec_draft on a ctx of the same V and B.  The scratch
+ * serves the current device, which must be the device of `stream`; every call
+ * on one GPU shares it, so calls on one GPU must not overlap (order them on
+ * one stream): overlapping calls race.  Each call clears the tickets it uses
+ * before its kernels run.
+ *   draft_logits [n_req, B-1, V] float, req_id [n_req] int32 >= 0,
+ *   cand [n_req, B-1] int32 out, draft_lse nullable [n_req, B-1] float out. */
+int dflash_spec_draft_static(void* stream, int32_t n_req, int32_t V, int32_t B, const float* draft_logits,
+                             float temperature, uint64_t seed, const int32_t* req_id, int32_t* cand,
+                             float* draft_lse);
+
 /* Verify one block per request by the rejection rule of speculative sampling.
  * q_j = softmax(draft_logits[r][j-1] / T) drafted offset j = 1..K;
  * p_j = softmax(target_logits[r][j] / T) is the verifier's distribution of the

@@ -135,3 +135,16 @@ def test_relay_rejects_null_ctx_and_arguments():
     assert L.dflow_relay(None, None, 1, slots, nacc, None, 1, None, None, ctypes.byref(rw)) == -1
     n = ctypes.c_int32()
     assert L.dflow_read_relay(None, None, 0, None, ctypes.byref(n)) == -1
+
+
+def test_spec_draft_static_rejects_bad_sizes_before_any_launch():
+    """The allocation-free drafting call validates its sizes on the host (no
+    GPU is touched for a rejected call)."""
+    L = dfa.lib()
+    f = L.dflash_spec_draft_static
+    assert f(None, 65, 1024, 16, None, 1.0, 0, None, None, None) == -3       # n_req beyond 64
+    assert f(None, 1, 262145, 16, None, 1.0, 0, None, None, None) == -3      # V beyond the scratch
+    assert f(None, 1, 1024, 17, None, 1.0, 0, None, None, None) == -2        # B beyond 16
+    assert f(None, 1, 1024, 16, None, 0.0, 0, None, None, None) == -1        # temperature
+    assert f(None, 0, 1024, 16, None, 1.0, 0, None, None, None) == 0         # nothing to do
+    assert f(None, 1, 1024, 16, None, 1.0, 0, None, None, None) == -1        # NULL logits

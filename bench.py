@@ -126,18 +126,64 @@ def kind_of_dispatch(name, prev):
     return None
 
 
-def read_counter_csv(path, counter):
+def read_counter_csv(path, counter, reduce="sum"):
     """[(kernel name, value)] per dispatch, in dispatch order, from a rocprofv3
-    counter_collection.csv."""
+    counter_collection.csv (rows of one dispatch combined by sum or max)."""
     per = {}
     with open(path) as fh:
         for r in csv.DictReader(fh):
             if r["Counter_Name"] != counter:
                 continue
             did = int(r["Dispatch_Id"])
-            name, v = per.get(did, (r["Kernel_Name"], 0.0))
-            per[did] = (name, v + float(r["Counter_Value"]))
+            v = float(r["Counter_Value"])
+            if did in per:
+                name, old = per[did]
+                v = old + v if reduce == "sum" else max(old, v)
+            else:
+                name = r["Kernel_Name"]
+            per[did] = (name, v)
     return [per[k] for k in sorted(per)]
+
+
+SIMDS = 1024       # MI355X: 256 CUs x 4 SIMDs
+GPU_CLOCK_HZ = 2.4e9
+
+
+def counter_summary(paths):
+    """Per kernel kind of the draft step: the median over dispatches of every
+    counter in the given rocprofv3 counter_collection.csv files (SQ counters
+    summed over the instances of a dispatch, GRBM_GUI_ACTIVE its maximum), and
+    where the counters are present the derived MFMA utilisation
+    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and the MFMA rate
+    512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 flops over GRBM_GUI_ACTIVE cycles at the
+    nominal 2.4 GHz clock."""
+    table = {}
+    for path in paths:
+        counters = set()
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                counters.add(r["Counter_Name"])
+        for c in sorted(counters):
+            prev = None
+            for name, v in read_counter_csv(path, c, "max" if c.startswith("GRBM") else "sum"):
+                kind = kind_of_dispatch(name, prev)
+                if kind is None:
+                    continue
+                prev = kind
+                table.setdefault(kind, {}).setdefault(c, []).append(v)
+    out = {}
+    for kind, cs in table.items():
+        row = {c: float(np.median(v)) for c, v in cs.items()}
+        row["dispatches"] = max(len(v) for v in cs.values())
+        gui = row.get("GRBM_GUI_ACTIVE")
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in row:
+            row["mfma_busy_frac"] = round(row["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS), 4)
+        if gui and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row:
+            tf = 512.0 * row["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / (gui / GPU_CLOCK_HZ) / 1e12
+            row["mfma_bf16_tflops"] = round(tf, 1)
+            row["mfma_bf16_frac_of_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
+        out[kind] = row
+    return out
 
 
 def traffic_summary(fetch_csv, write_csv, copy_mib, workload):
@@ -645,12 +691,18 @@ def main():
                          "measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy one buffer of this many MiB (reference dispatch for byte counters)")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="print per-kind medians of the counters in rocprofv3 counter_collection.csv files "
+                         "(and the derived MFMA utilisation); needs no GPU")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE, WRITE_SIZE) of a run with --copy-probe-mib; needs no GPU")
     args = ap.parse_args()
     if args.no_extras:
         args.no_4b = args.no_relay = True
+    if args.counter_summary:
+        print(json.dumps(counter_summary(args.counter_summary), indent=1, sort_keys=True))
+        return
     if args.traffic_from:
         if not args.copy_probe_mib:
             ap.error("--traffic-from needs the --copy-probe-mib of the profiled run")

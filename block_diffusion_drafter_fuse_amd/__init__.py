@@ -13,7 +13,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdflash_fuse.so")
+# DFLASH_FUSE_LIB may name another build of the same library (tuning sweeps).
+LIB_PATH = os.environ.get("DFLASH_FUSE_LIB") or os.path.join(HERE, "libdflash_fuse.so")
 
 DFLASH_F32, DFLASH_BF16 = 0, 1
 STATUS = {0: "DFLASH_OK", -1: "DFLASH_EINVAL", -2: "DFLASH_EUNSUPPORTED",

@@ -21,18 +21,20 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build_library(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, SRC]
+def build_library(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    """Compile the library to `out` (default: in-tree); `defines` are extra
+    -D options (tuning sweeps build variants outside the tree)."""
+    tmp = out + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, *[f"-D{x}" for x in defines], "-o", tmp, SRC]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
+    msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + out)
-    if verbose and out.strip():
-        print(out, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + msg)
+    if verbose and msg.strip():
+        print(msg, file=sys.stderr)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

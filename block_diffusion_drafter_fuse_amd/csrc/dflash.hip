@@ -49,13 +49,33 @@ int fail(int code, const std::string& msg) {
 
 constexpr size_t kAlign = 256;
 constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
+// Tuning constants of the attention launch (overridable at build time for
+// sweeps: -DDFL_ATTN_TARGET_WG=... etc.).
+#ifndef DFL_ATTN_TARGET_WG
+#define DFL_ATTN_TARGET_WG 512
+#endif
+#ifndef DFL_ATTN_MIN_CHUNK
+#define DFL_ATTN_MIN_CHUNK 128
+#endif
+#ifndef DFL_ATTN_NBUF
+#define DFL_ATTN_NBUF 2
+#endif
+#ifndef DFL_ATTN_WPE
+#define DFL_ATTN_WPE 2
+#endif
 constexpr int kAttnWorkMax = 4096;     // attention split work items per call
-constexpr int kAttnTargetWG = 512;     // attention work-groups aimed for
-constexpr int kAttnMinChunk = 128;     // minimum context keys per split
-constexpr int kAttnNbuf = 2;           // attention K/V ring depth
-constexpr int kAttnStg = 32;           // attention keys per stage
-constexpr int kAttnWpe = 4;            // attention waves per SIMD the registers must allow
-constexpr int kAttnQw = 1;             // attention query fragments per wave
+constexpr int kAttnTargetWG = DFL_ATTN_TARGET_WG;  // attention work-groups aimed for
+constexpr int kAttnMinChunk = DFL_ATTN_MIN_CHUNK;  // minimum context keys per split
+constexpr int kAttnNbuf = DFL_ATTN_NBUF;           // attention K/V ring depth
+#ifndef DFL_ATTN_STG
+#define DFL_ATTN_STG 32
+#endif
+#ifndef DFL_ATTN_QW
+#define DFL_ATTN_QW 1
+#endif
+constexpr int kAttnStg = DFL_ATTN_STG;             // attention keys per stage
+constexpr int kAttnWpe = DFL_ATTN_WPE;             // attention waves per SIMD the registers must allow
+constexpr int kAttnQw = DFL_ATTN_QW;   // attention query fragments per wave
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
 constexpr int kNarrowMaxGroups = 64;   // weights of at most 1024 rows also take the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
@@ -114,9 +134,10 @@ int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
 // Few-token LM head: one 16-wave work-group per CU and 16-row block.
 int lm_chunks_small(int rowblocks) { return std::max(1, 256 / rowblocks); }
 constexpr int kLdsMax = 160 * 1024;  // LDS of one CU
-// LDS of the top-k LM head: 16 staged rows, reused for the 16 x 64 x 16 list merge.
+// LDS of the top-k LM head: 16 staged rows, reused for the 16 x 64 x 16 list
+// merge and its 16 x 64 list heads.
 int lm_small_lds(const dflash_dims& d) {
-  return std::max(16 * (d.D * elt_size(d.dtype) + 16), 16 * 64 * 16 * 8);
+  return std::max(16 * (d.D * elt_size(d.dtype) + 16), 16 * 64 * 16 * 8 + 16 * 64);
 }
 
 // Which GEMM engine serves M rows against a weight of ngroups 16-row groups:
@@ -624,8 +645,8 @@ void plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPla
 
 template <typename T, int KTOP>
 void launch_lm_small(const LmArgs<T>& la, int nchunk, int rowblocks, int* tile_ctr, hipStream_t st) {
-  // staged rows, reused afterwards for the 16 x 64 x KTOP list merge
-  const int lds = std::max(16 * (la.a.kseg * (int)sizeof(T) + 16), 16 * 64 * KTOP * 8);  // <= kLdsMax (checked)
+  // staged rows, reused afterwards for the 16 x 64 x KTOP list merge and its list heads
+  const int lds = std::max(16 * (la.a.kseg * (int)sizeof(T) + 16), 16 * 64 * KTOP * 8 + 16 * 64);  // <= kLdsMax (checked)
   auto kern = lmhead_lds_kernel<T, KTOP, kLmFN, kLmU>;
   static bool attr_set = false;
   if (!attr_set) {

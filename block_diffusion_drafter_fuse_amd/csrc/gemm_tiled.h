@@ -267,15 +267,42 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
     if (tid == 0) __hip_atomic_store(sk.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
+  // Row scales of the folded RMSNorm, once per work-group: the BM rows' sums
+  // of squares are reduced by TPR threads per row (fixed order) into LDS (the
+  // ring is idle after the stream; a barrier first lets every wave finish
+  // its last fragment reads).  Every wave of the work-group then reads its
+  // rows' scales from LDS instead of re-reducing the slots per fragment.
+  float* srow = reinterpret_cast<float*>(lds + 256);
+  if (nrm.ssq) {
+    constexpr int NT = 64 * NWV;
+    constexpr int TPR = NT / BM >= 1 ? NT / BM : 1;  // threads per row
+    static_assert(NT % BM == 0 || BM % NT == 0, "rows split evenly over the threads");
+    __syncthreads();
+    for (int r0 = 0; r0 < BM; r0 += NT / TPR) {
+      const int row = r0 + tid / TPR, sub = tid % TPR;
+      const int m = bm * BM + row;
+      const float* p = nrm.ssq + (size_t)a.row(m < a.M ? m : a.M - 1) * nrm.nslot;
+      float ssum = 0.f;
+      for (int j = sub * 4; j < nrm.nslot; j += TPR * 4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + j);
+        ssum += (v[0] + v[1]) + (v[2] + v[3]);
+      }
+#pragma unroll
+      for (int o = 1; o < TPR; o <<= 1) ssum += __shfl_xor(ssum, o);
+      if (sub == 0 && row < BM) srow[row] = 1.0f / sqrtf(ssum * nrm.inv_d + nrm.eps);
+    }
+    __syncthreads();
+  }
+
   const int g0 = ngroups_tile0 + wn * FN;
   int fb[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) fb[j] = g0 + j < w.ngroups ? w.feature_of_group(g0 + j) : 0;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = bm * BM + wm * FM * 16 + i * 16 + r16;
-    const int arow = a.row(m < a.M ? m : a.M - 1);
-    const float sc = norm_scale(nrm, arow, kg);
+    const int lrow = wm * FM * 16 + i * 16 + r16;
+    const int m = bm * BM + lrow;
+    const float sc = nrm.ssq ? srow[lrow] : 1.0f;
     run_epilogue<FN>(epi, m, m < a.M, w.ngroups - g0, fb, acc[i], sc, kg);
   }
 }

@@ -141,8 +141,9 @@ __global__ __launch_bounds__(1024) void lmhead_lds_kernel(const LmArgs<T> p, int
   __syncthreads();
   const int mr = m0 + tid;
   if (tid < 16 && mr < p.a.M) {
-    int head[NL];
-#pragma unroll
+    // list heads of this row in LDS (a per-thread array indexed at run time
+    // would live in scratch memory)
+    unsigned char* head = reinterpret_cast<unsigned char*>(lds + 16 * NL * KTOP * 8) + tid * NL;
     for (int l = 0; l < NL; ++l) head[l] = 0;
     float* ov = p.part_v + ((size_t)mr * gridDim.x + blockIdx.x) * KTOP;
     int* oi = p.part_i + ((size_t)mr * gridDim.x + blockIdx.x) * KTOP;
@@ -151,9 +152,10 @@ __global__ __launch_bounds__(1024) void lmhead_lds_kernel(const LmArgs<T> p, int
       float bv = -INFINITY;
       int bi = 0x7fffffff;
       for (int l = 0; l < NL; ++l) {
-        if (head[l] >= KTOP) continue;
-        const float v = sv[(tid * NL + l) * KTOP + head[l]];
-        const int id = si[(tid * NL + l) * KTOP + head[l]];
+        const int h = head[l];
+        if (h >= KTOP) continue;
+        const float v = sv[(tid * NL + l) * KTOP + h];
+        const int id = si[(tid * NL + l) * KTOP + h];
         if (best < 0 || tk_better(v, id, bv, bi)) {
           bv = v;
           bi = id;

@@ -166,13 +166,6 @@ __global__ __launch_bounds__(64 * (QF / QW), WPE) void attn_kernel(const AttnArg
   const int kend = min(ctx, kbeg + a.chunk);
   const int nctx = kend > kbeg ? (kend - kbeg + STG - 1) / STG : 0;
   const int nst = nctx + (s == S - 1 ? 1 : 0);
-#ifdef DFL_ATTN_ROT
-  // context stages taken in a rotated order (start offset per work-group)
-  const int rot = nctx > 0 ? (int)(((unsigned)w * 2654435761u) % (unsigned)nctx) : 0;
-  auto cst = [&](int i) { int x = i + rot; return x >= nctx ? x - nctx : x; };
-#else
-  auto cst = [&](int i) { return i; };
-#endif
   const T* hb = a.pool + (size_t)a.meta.slot[r] * a.slot_stride + (size_t)a.layer * a.layer_stride +
                 (size_t)g * a.head_stride;
   const T* bkb = a.kb + (size_t)(r * a.B) * kd + (size_t)g * HD;
@@ -182,7 +175,7 @@ __global__ __launch_bounds__(64 * (QF / QW), WPE) void attn_kernel(const AttnArg
   // (j < KI) or V^T rows; each lane one 16-byte chunk of one row.
   auto issue = [&](int i, int b) {
     const bool blk = i >= nctx;
-    const int k0 = blk ? 0 : kbeg + cst(i) * STG;  // multiple of STG
+    const int k0 = blk ? 0 : kbeg + i * STG;  // multiple of STG
     char* base = lds + b * SG::BUF;
 #pragma unroll
     for (int ii = 0; ii < SG::NIW; ++ii) {
@@ -233,7 +226,7 @@ __global__ __launch_bounds__(64 * (QF / QW), WPE) void attn_kernel(const AttnArg
       issue(i + NBUF - 1, nb);
     }
     const bool blk = i >= nctx;
-    const int klim = blk ? a.B : kend - (kbeg + cst(i) * STG);  // valid keys in this stage
+    const int klim = blk ? a.B : kend - (kbeg + i * STG);  // valid keys in this stage
     const char* kl = lds + buf * SG::BUF;
     const char* vl = kl + SG::KBYTES;
     // S^T for every key of the stage first (the MFMA chains interleave; one K

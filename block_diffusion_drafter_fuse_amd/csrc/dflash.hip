@@ -83,8 +83,18 @@ constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (L
 constexpr bool kGemvPF = false;        // prefetch the next tile's weights before the current MFMAs
 constexpr int kGemvWGs = 256;          // skinny GEMM work-groups per 16-token block
 constexpr int kGemvXcds = 8;           // XCDs; work-group i runs on XCD i mod 8
-constexpr int kRsNbuf = 6;             // row-streaming GEMV ring depth (stages of 16 KB)
-constexpr int kRsMaxSplit = 8;         // K ranges of the row-streaming GEMV
+#ifndef DFL_RS_NBUF
+#define DFL_RS_NBUF 6
+#endif
+#ifndef DFL_RS_MAX_SPLIT
+#define DFL_RS_MAX_SPLIT 8
+#endif
+#ifndef DFL_RS_SPLIT_COST
+#define DFL_RS_SPLIT_COST 0
+#endif
+constexpr int kRsNbuf = DFL_RS_NBUF;   // row-streaming GEMV ring depth (stages of 16 KB)
+constexpr int kRsMaxSplit = DFL_RS_MAX_SPLIT;  // K ranges of the row-streaming GEMV
+constexpr int kRsSplitCost = DFL_RS_SPLIT_COST;  // stage-equivalents charged per extra K range
 constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, unroll
 constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
 constexpr size_t kPartFloats = size_t(16) << 20;  // split-K partials (64 MB)
@@ -360,7 +370,7 @@ bool plan_rs(const WOperand<T>& w, const AOperand<T>& a, int mt, RsPlan* out) {
     const int lds = gemv_rs_lds(kRsNbuf, red2, tpw);
     if (lds > kRsLdsMax) continue;
     if (ks > 1 && ((long)mt * w.ngroups > kCounters - 64 || (size_t)mt * w.ngroups * ks * 256 > kPartFloats)) continue;
-    const long cost = (long)tpw * (nst + 2);
+    const long cost = (long)tpw * (nst + 2) + (long)(ks - 1) * kRsSplitCost;
     if (best < 0 || cost < best) {
       best = cost;
       *out = RsPlan{ceil_div(nst_all, nst), nst, red2, tpw, ceil_div(w.ngroups, tpw), lds};

@@ -146,6 +146,7 @@ def read_counter_csv(path, counter, reduce="sum"):
 
 
 SIMDS = 1024       # MI355X: 256 CUs x 4 SIMDs
+XCDS = 8           # GRBM_GUI_ACTIVE of a dispatch comes summed over the 8 XCDs
 GPU_CLOCK_HZ = 2.4e9
 
 
@@ -153,10 +154,12 @@ def counter_summary(paths):
     """Per kernel kind of the draft step: the median over dispatches of every
     counter in the given rocprofv3 counter_collection.csv files (SQ counters
     summed over the instances of a dispatch, GRBM_GUI_ACTIVE its maximum), and
-    where the counters are present the derived MFMA utilisation
-    SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x SIMDs) and the MFMA rate
-    512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 flops over GRBM_GUI_ACTIVE cycles at the
-    nominal 2.4 GHz clock."""
+    where the counters are present the derived figures: the dispatch's busy
+    cycles per XCD (GRBM_GUI_ACTIVE / 8, which includes the counter window's own
+    overhead, so the fractions below are lower bounds), the MFMA utilisation
+    SQ_VALU_MFMA_BUSY_CYCLES / (cycles per XCD x SIMDs), the executed bf16 MFMA
+    flops 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (padding of partial tiles
+    included), and their rate over those cycles at the nominal 2.4 GHz clock."""
     table = {}
     for path in paths:
         counters = set()
@@ -176,10 +179,14 @@ def counter_summary(paths):
         row = {c: float(np.median(v)) for c, v in cs.items()}
         row["dispatches"] = max(len(v) for v in cs.values())
         gui = row.get("GRBM_GUI_ACTIVE")
+        if gui:
+            gui /= XCDS
+            row["busy_us_per_xcd"] = round(gui / GPU_CLOCK_HZ * 1e6, 1)
         if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in row:
             row["mfma_busy_frac"] = round(row["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * SIMDS), 4)
         if gui and "SQ_INSTS_VALU_MFMA_MOPS_BF16" in row:
-            tf = 512.0 * row["SQ_INSTS_VALU_MFMA_MOPS_BF16"] / (gui / GPU_CLOCK_HZ) / 1e12
+            row["mfma_bf16_flops"] = 512.0 * row["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+            tf = row["mfma_bf16_flops"] / (gui / GPU_CLOCK_HZ) / 1e12
             row["mfma_bf16_tflops"] = round(tf, 1)
             row["mfma_bf16_frac_of_peak"] = round(tf / BF16_PEAK_TFLOPS, 4)
         out[kind] = row
@@ -673,6 +680,39 @@ def cpu_baseline(wl, w_np, n_sample=6):
             "single_thread": single}
 
 
+def blas_reference(wl, torch, reps=20):
+    """The vendor library's bf16 GEMM (torch.nn.functional.linear, which calls
+    hipBLASLt) on the projection shapes of the workload's draft step, with
+    weights cycled through enough copies (>= 600 MB) that each call reads its
+    weight from HBM as the step does.  Context for the MFMA fraction of the
+    library's own GEMM kernels; no part of the draft step."""
+    d = wl.dims
+    M, Mlm = wl.bs * d.B, wl.bs * (d.B - 1)
+    qkv = (d.Hq + 2 * d.Hkv) * d.hd
+    shapes = {"qkv_gemm": (M, qkv, d.D), "o_gemm": (M, d.D, d.Hq * d.hd), "gateup_gemm": (M, 2 * d.I, d.D),
+              "down_gemm": (M, d.D, d.I), "lm_head": (Mlm, d.V, d.D)}
+    out = {}
+    for kind, (m, n, k) in shapes.items():
+        a = torch.randn(m, k, device="cuda").to(torch.bfloat16)
+        w = (torch.randn(n, k, device="cuda") * 0.02).to(torch.bfloat16)
+        ws = [w] + [w.clone() for _ in range(max(0, -(-600_000_000 // (n * k * 2)) - 1))]
+        for i in range(3):
+            torch.nn.functional.linear(a, ws[i % len(ws)])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(reps):
+            torch.nn.functional.linear(a, ws[i % len(ws)])
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1000
+        tf = 2.0 * m * n * k / us / 1e6
+        out[kind] = {"shape_mnk": [m, n, k], "us_per_call": round(us, 1), "tflops": round(tf, 1),
+                     "mfma_roof_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        del ws, w, a
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -691,6 +731,8 @@ def main():
                          "measurements")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, copy one buffer of this many MiB (reference dispatch for byte counters)")
+    ap.add_argument("--blas-reference", action="store_true",
+                    help="also time torch's bf16 linear (hipBLASLt) on the step's projection shapes, cold weights")
     ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
                     help="print per-kind medians of the counters in rocprofv3 counter_collection.csv files "
                          "(and the derived MFMA utilisation); needs no GPU")
@@ -777,6 +819,7 @@ def main():
         torch.bitwise_not(src, out=dst)  # one elementwise kernel: n bytes in, n bytes out
         torch.cuda.synchronize()
         del src, dst
+    blas = blas_reference(wl, torch) if args.blas_reference else None
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -821,6 +864,8 @@ def main():
         line["select"] = select
     if spec:
         line["spec_sampling"] = spec
+    if blas:
+        line["blas_reference"] = blas
     print(json.dumps(line), flush=True)
 
 

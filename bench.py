@@ -362,7 +362,8 @@ def measure_conv(wb, steps, warmup, label):
     return {"workload": f"{label} step with the two-tap convolution",
             "ms_per_step": round(ms, 4), "conv_ms_per_step": round(kern[0] * kern[1] / steps, 4),
             "conv_launches_per_step": kern[1] // steps, "conv_weight_bytes": byts,
-            "note": "4 sites x N layers: tap-correction GEMM on the GEMV engine + tap mix; "
+            "note": "4 sites x N layers: tap-correction GEMM (64-token tiles, split K) + tap-mix kernel; with "
+                    "at most 64 token rows one launch per site (the mix in the GEMV's epilogue); "
                     "ms_per_step is the whole step with the convolution attached"}
 
 

@@ -4,13 +4,18 @@
 //   y_t = k_{t,0} * x_t + k_{t,1} * x_{t-1},  k_{t,j}[c] = kbase_j[c] + z_t[j][c / 16]
 //
 // over the block offsets t of one request (x_{-1} = 0: the anchor at offset 0
-// has no left neighbour; offset 1 reads the anchor).  z_t = [W_0; W_1] x_t
-// comes from the GEMM engine (one output per 16 channels and tap); this
-// kernel mixes the taps.  Two forms:
+// has no left neighbour; offset 1 reads the anchor).  The tap corrections
+// z_t = [W_0; W_1] x_t run on the GEMM engines with the two taps' rows paired
+// (group g of tap 0 beside group g of tap 1), and the tap mix is their epilogue (few token rows, on the GEMV engines).  A lane holds
+// the corrections of groups g..g+3 of both taps for token row m, i.e.
+// everything the 64 channels 16g..16g+63 of y_m need besides the inputs x_m
+// and x_{m-1}, which it reads.  With many token rows the corrections are
+// stored and conv_mix_kernel mixes the taps (two launches per site).
 //  * normed site (attention / FFN input): x is the RMSNorm output, held as
-//    T(h * g) with per-16-channel sums of squares of h; the row scales of
-//    rows t and t-1 are completed here, the convolved rows y are written in
-//    the storage type (the next GEMM's operand);
+//    T(h * g) with per-16-channel sums of squares of h; the engine passes the
+//    row scale of row m, and row m-1's is the one held by the lane a row up
+//    in the same 16-row fragment.  y is written in the storage type (the next
+//    GEMM's operand).
 //  * residual site (attention / FFN output before the residual add): x is
 //    the sub-layer output in the storage type; h += y on the fp32 residual
 //    stream, and the next RMSNorm's operand T(h * g) and per-16-channel sums
@@ -20,6 +25,72 @@
 
 namespace dfl {
 
+template <typename T, bool RESID>
+struct EpiConvMix {
+  static constexpr bool kPaired = true;
+  static constexpr bool kRow = false;
+  static constexpr bool kScaled = true;
+  const T* in;        // [M, D] site input (the GEMM's activation operand)
+  const float* ssq;   // normed site: [M, D/16] sums of squares of the unnormalised rows
+  float inv_d, eps;
+  const T* kbase;     // [2, D]
+  int B, D;
+  T* y;               // normed site output [M, D]
+  float* h;           // residual site: fp32 residual stream [M, D]
+  T* u;               // residual site: T(h * g) [M, D]
+  const T* g;         // residual site: gain of the next RMSNorm
+  float* ssq_out;     // residual site: [M, D/16]
+
+  __device__ __forceinline__ void apply2s(int m, bool valid, int f, f32x4_t z0, f32x4_t z1, float sc) const {
+    // row m - 1 sits one lane down in the same 16-row fragment (lane = row + 16 k)
+    const int lane = threadIdx.x & 63;
+    float scl = __shfl(sc, (lane & 15) ? lane - 1 : lane);
+    if (!valid) return;
+    const int t = m % B;
+    const int G = D >> 4;
+    if (!RESID && t > 0 && (lane & 15) == 0) {
+      // the fragment starts inside a block (B does not divide 16): reduce row m-1 here
+      float s = 0.f;
+      for (int j = 0; j < G; ++j) s += ssq[(size_t)(m - 1) * G + j];
+      scl = 1.0f / sqrtf(s * inv_d + eps);
+    }
+    z0 = z0 * sc;
+    z1 = z1 * sc;
+    const float sct = RESID ? 1.0f : sc;
+    const T* xt_row = in + (size_t)m * D;
+    const T* xl_row = in + (size_t)(m - 1) * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int grp = f + i;
+      float ss = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = grp * 16 + q * 4;
+        const f32x4_t xt = load4<T>(xt_row + c) * sct;
+        const f32x4_t xl = t > 0 ? load4<T>(xl_row + c) * (RESID ? 1.0f : scl) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const f32x4_t k0 = load4<T>(kbase + c), k1 = load4<T>(kbase + D + c);
+        f32x4_t yv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yv[e] = (k0[e] + z0[i]) * xt[e] + (k1[e] + z1[i]) * xl[e];
+        if constexpr (!RESID) {
+          store4<T>(y + (size_t)m * D + c, yv[0], yv[1], yv[2], yv[3]);
+        } else {
+          f32x4_t* hp = reinterpret_cast<f32x4_t*>(h + (size_t)m * D + c);
+          const f32x4_t hn = *hp + yv;
+          *hp = hn;
+          const f32x4_t gg = load4<T>(g + c);
+          store4<T>(u + (size_t)m * D + c, hn[0] * gg[0], hn[1] * gg[1], hn[2] * gg[2], hn[3] * gg[3]);
+          ss += (hn[0] * hn[0] + hn[1] * hn[1]) + (hn[2] * hn[2] + hn[3] * hn[3]);
+        }
+      }
+      if constexpr (RESID) ssq_out[(size_t)m * G + grp] = ss;
+    }
+  }
+};
+
+// The tap mix as a kernel of its own, after the corrections z were stored by
+// the GEMM (many token rows: there the corrections GEMM splits K, and a mix in
+// its epilogue would run in the one work-group per tile that sums the splits).
 template <typename T>
 struct ConvMixArgs {
   const T* in;        // [M, D] site input

@@ -137,6 +137,9 @@ using TileW192 = TileCfg<256, 192, 4, 2, 2>;  // same, 64 x 96 per wave, where i
 constexpr double kW192TileCost = 0.86;
 using TileLo = TileCfg<64, 128, 2, 4, 3>;     // activations as hi + lo planes
 using TileLoWide = TileCfg<128, 256, 2, 4, 2>;  // same, many tokens (every CU filled)
+using TileNarrow = TileCfg<64, 128, 2, 4, 3>;   // a narrow weight against many tokens (the
+                                                // convolution's tap corrections: 64-token
+                                                // tiles and split K keep every CU busy)
 constexpr int kWideMinFeatures = 16384;
 
 int elt_size(int dtype) { return dtype == DFLASH_BF16 ? 2 : 4; }
@@ -388,10 +391,10 @@ long tiled_cost(int M, int ngroups, int nst) {
   return (long)ceil_div(tiles * SK, kTiledSlots) * C::BM * C::BN / SK;
 }
 
+// The GEMV engines (few rows, or a narrow weight); false where neither applies.
 template <typename T, bool ALO = false, class Epi>
-void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
-                 hipStream_t st) {
-  if (a.M <= 0 || w.ngroups <= 0) return;
+bool launch_skinny(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
+                   hipStream_t st) {
   const int K = a.nk * a.kseg;
   {
     const int mt = ceil_div(a.M, 16);
@@ -407,7 +410,7 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
       }
       const RsSplit sp{rp.nsplit, rp.nst, rp.red2, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off)};
       hipLaunchKernelGGL(kern, dim3(rp.nwg, rp.nsplit * mt), dim3(1024), rp.lds, st, w, a, nrm, sp, epi, rp.tpw);
-      return;
+      return true;
     }
     if (uses_gemv(a.M, w.ngroups)) {
       // Activation-stationary GEMV: 16-row tiles, K split across the waves of
@@ -438,9 +441,18 @@ void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, cons
                dim3(kGemvXcds * nwg * ceil_div(mt, kGemvXcds)));
       else
         launch(gemv_as_kernel<T, KSW, ALO, kGemvTB, kGemvPF, false, Epi>, dim3(nwg, mt));
-      return;
+      return true;
     }
   }
+  return false;
+}
+
+template <typename T, bool ALO = false, class Epi>
+void launch_gemm(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, const NormIn& nrm, const Epi& epi,
+                 hipStream_t st) {
+  if (a.M <= 0 || w.ngroups <= 0) return;
+  if (launch_skinny<T, ALO>(c, w, a, nrm, epi, st)) return;
+  const int K = a.nk * a.kseg;
   if constexpr (ALO) {
     if ((long)ceil_div(a.M, TileLoWide::BM) * ceil_div(w.ngroups, TileLoWide::BN / 16) >= kTiledSlots)
       launch_tiled<TileLoWide, T, true>(c, w, a, nrm, epi, st);
@@ -761,15 +773,47 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
   T* cv = c->wsp<T>(p.cv_off);
   T* ob = c->wsp<T>(p.ob_off);
   float* zc = c->wsp<float>(p.zc_off);
-  // One convolution site: tap corrections z = [W_0; W_1] x on the GEMM engine
-  // (row-scaled for a normed site), then the tap mix.  Normed sites read the
-  // folded RMSNorm operand (u, ssq) and write the convolved operand cv;
-  // residual sites read the sub-layer output ob and update h, u and ssq.
+  // One convolution site.  Few token rows: one launch, the tap corrections
+  // [W_0; W_1] x on a GEMV engine (tap rows paired) with the tap mix in its
+  // epilogue.  Many rows: the corrections GEMM (K split over 64-token tiles)
+  // stores z, then conv_mix_kernel mixes the taps.  Normed sites read the
+  // folded RMSNorm operand (u with its row scale) and write the convolved
+  // operand cv; residual sites read the sub-layer output ob and update x, u
+  // and ssq.
   auto conv_site = [&](const dflash2_conv_site& cs, bool normed, const T* g_next_norm) {
     ProfScope ps(c, DFLASH_K_CONV, st);
     const T* in = normed ? u : ob;
-    launch_gemm<T>(c, wop<T>({{cs.w, d.D / 8}}, 0), aop<T>(in, M, d.D), normed ? nrm : none,
-                   EpiStore<float>{zc, d.D / 8}, st);
+    const AOperand<T> az = aop<T>(in, M, d.D);
+    const NormIn& n = normed ? nrm : none;
+    if (M <= kSkinnyMaxM) {
+      const WOperand<T> wz = wop<T>({{cs.w, d.D / 8}}, d.D / 16);
+      bool done;
+      if (normed) {
+        EpiConvMix<T, false> e{};
+        e.in = in;
+        e.ssq = ssq;
+        e.inv_d = 1.0f / (float)d.D;
+        e.eps = d.rms_eps;
+        e.kbase = static_cast<const T*>(cs.kbase);
+        e.B = d.B;
+        e.D = d.D;
+        e.y = cv;
+        done = launch_skinny<T>(c, wz, az, n, e, st);
+      } else {
+        EpiConvMix<T, true> e{};
+        e.in = in;
+        e.kbase = static_cast<const T*>(cs.kbase);
+        e.B = d.B;
+        e.D = d.D;
+        e.h = x;
+        e.u = u;
+        e.g = g_next_norm;
+        e.ssq_out = ssq;
+        done = launch_skinny<T>(c, wz, az, n, e, st);
+      }
+      if (done) return;
+    }
+    launch_tiled<TileNarrow, T, false>(c, wop<T>({{cs.w, d.D / 8}}, 0), az, n, EpiStore<float>{zc, d.D / 8}, st);
     ConvMixArgs<T> ca{};
     ca.in = in;
     ca.ssq = ssq;

@@ -18,6 +18,8 @@
 // lane: with a pair distance P, 16-feature groups 2i and 2i+1 map to features
 // (first half) and (first half + P).
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace dfl {
@@ -153,7 +155,23 @@ __device__ __forceinline__ float token_sum(float s) {
 // Unpaired: apply1(m, valid, f, v) - v holds features f..f+3 of row m (this
 // lane's part of one 16-feature fragment).  Paired: apply2(m, valid, f, a, b)
 // - a holds features f..f+3, b the partners f+P..f+P+3.  Every lane calls
-// the epilogue (shuffles inside); stores are guarded by `valid`.
+// the epilogue (shuffles inside); stores are guarded by `valid`.  A paired
+// epilogue with kScaled takes apply2s(m, valid, f, a, b, sc) instead: the raw
+// sums and the row scale of the folded RMSNorm (1 without a norm) apart.
+
+template <class E, class = void>
+struct EpiScaled : std::false_type {};
+template <class E>
+struct EpiScaled<E, std::void_t<decltype(E::kScaled)>> : std::integral_constant<bool, E::kScaled> {};
+
+template <class Epi>
+__device__ __forceinline__ void call_paired(const Epi& epi, int m, bool valid, int f, f32x4_t a, f32x4_t b,
+                                            float sc) {
+  if constexpr (EpiScaled<Epi>::value)
+    epi.apply2s(m, valid, f, a, b, sc);
+  else
+    epi.apply2(m, valid, f, a * sc, b * sc);
+}
 
 // Fusion output: u = T(z * g) (plus the low half z*g - u when lo != 0), and
 // per-16-feature sums of squares of z.
@@ -401,7 +419,7 @@ __device__ __forceinline__ void run_epilogue(const Epi& epi, int m, bool mvalid,
   } else if constexpr (Epi::kPaired) {
 #pragma unroll
     for (int j = 0; j < FN; j += 2)
-      epi.apply2(m, mvalid && j + 1 < nvalid, fb[j] + 4 * kg, acc[j] * sc, acc[j + 1] * sc);
+      call_paired(epi, m, mvalid && j + 1 < nvalid, fb[j] + 4 * kg, acc[j], acc[j + 1], sc);
   } else {
 #pragma unroll
     for (int j = 0; j < FN; ++j) epi.apply1(m, mvalid && j < nvalid, fb[j] + 4 * kg, acc[j] * sc);
@@ -574,7 +592,7 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
         const int fb1[1] = {w.feature_of_group(t)};
         epi.template apply_row<1>(m, m < a.M, 1, fb1, sum, sc, kg);
       } else if constexpr (Epi::kPaired) {
-        epi.apply2(m, m < a.M, w.feature_of_group(t) + 4 * kg, sum[0] * sc, sum[1] * sc);
+        call_paired(epi, m, m < a.M, w.feature_of_group(t) + 4 * kg, sum[0], sum[1], sc);
       } else {
         epi.apply1(m, m < a.M, w.feature_of_group(t) + 4 * kg, sum[0] * sc);
       }

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(1024) void gemv_rs_kernel(const WOperand<T> w, cons
       f32x4_t b;
 #pragma unroll
       for (int i = 0; i < 4; ++i) b[i] = __shfl_xor(v[i], 32);
-      epi.apply2(m, mvalid && kg < 2, feat(t, 4 * (kg & 1)), v * sc, b * sc);
+      call_paired(epi, m, mvalid && kg < 2, feat(t, 4 * (kg & 1)), v, b, sc);
     } else {
       epi.apply1(m, mvalid, t * 16 + 4 * kg, v * sc);
     }

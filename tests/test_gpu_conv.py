@@ -2,8 +2,9 @@
 + dflash_draft_block) against the float64 oracle.
 
 Workload: the selector configuration (tiny fp32 drafter, B 16), 16 requests
-with 64 context tokens, convolution weights from synth.make_conv_weights at
-all four sites of every layer.  Bars: logits rel <= 1e-4 (fp32), top-1 ids
+with 64 context tokens (the two-launch form: corrections GEMM, then the tap
+mix), and 1, 3 or 4 requests (the one-launch form, B 16 and B 6), convolution
+weights from synth.make_conv_weights at all four sites of every layer.  Bars: logits rel <= 1e-4 (fp32), top-1 ids
 where the oracle's margin exceeds 0.05; bf16 at the Qwen3-4B shape: logits
 within 2e-2 of max |logit|.  An identity convolution (W = 0, kbase = (1, 0))
 reproduces the plain draft, and detaching restores it bit for bit."""
@@ -62,6 +63,29 @@ def test_gpu_conv_matches_oracle():
         plain_diff = max(plain_diff, rel_inf(ref, o.draft(r, int(anchors[r]))["logits"]))
     # the convolution changes the draft (the comparison is not vacuous)
     assert plain_diff > 1e-2
+    g.close()
+
+
+@pytest.mark.parametrize("bs,B", [(1, 16), (4, 16), (3, 6)])
+def test_gpu_conv_few_rows_matches_oracle(bs, B):
+    """Few token rows take the one-launch form (tap mix in the corrections
+    GEMM's epilogue on a GEMV engine); B = 6 puts a block boundary inside a
+    16-row fragment, so row m - 1's scale is reduced by the epilogue itself."""
+    wl = synth.get_config("dflash2_select")
+    d = dataclasses.replace(wl.dims, B=B)
+    log(f"case dflash2 conv, few rows: bs {bs}, B {B}")
+    g, o, w32, slots = _setup(d, wl.seed, bs, 40)
+    cw = synth.make_conv_weights(d, wl.seed)
+    g.dr.conv_attach(_dev_conv(cw))
+    cw32 = synth.conv_weights_as_f32(cw)
+    anchors = synth.make_anchors(d, wl.seed, bs)
+    ids, _, lg = g.draft(slots, anchors, top_k=1, logits=True)
+    for r in slots:
+        ref = ds.draft_block_conv(w32, d, o.cache(r), int(anchors[r]), cw32)["logits"]
+        err = rel_inf(lg[r], ref)
+        assert err <= 1e-4, f"req {r}: logits rel err {err}"
+        _, bad = check_top1(ids[r][:, 0], ref)
+        assert len(bad) == 0, f"req {r}: top-1 mismatch at {bad}"
     g.close()
 
 

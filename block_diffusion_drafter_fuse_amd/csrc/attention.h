@@ -32,13 +32,43 @@ namespace dfl {
 constexpr int kAttnStage = 64;  // split lengths are multiples of this (and of every stage size)
 constexpr float kAttnSlack = 8.f;  // log2 headroom before a query's reference maximum moves
 
+// Work items (request r, KV head g, split s) are numbered canonically, r-major
+// (work0[r] + g * nsplit[r] + s: where the split's partial is stored and the
+// combine reads it), but launched longest first so that the short splits of
+// a ragged batch fill the gaps at the end: the last splits (rest of the
+// context plus the block) of the `nbig` requests at least a full split long,
+// in rorder; then every full split, r-major; then the other last splits in
+// rorder (requests by descending last-split length, ties by index).
 struct AttnMeta {
   int n_req;
+  int nbig;
   int ctx[kMaxReq];
   int slot[kMaxReq];
   int nsplit[kMaxReq];     // splits of request r (>= 1; the last one takes the block keys)
   int work0[kMaxReq + 1];  // first work item of request r; Hkv*nsplit items each
+  int rorder[kMaxReq];
 };
+
+// (request, KV head, split) of launched work-group w, in the order above.
+__device__ __forceinline__ void attn_item(const AttnMeta& m, int Hkv, int w, int& r, int& g, int& s) {
+  const int nbigw = m.nbig * Hkv;
+  const int nfull = m.work0[m.n_req] - m.n_req * Hkv;  // full (non-last) splits of all requests
+  if (w < nbigw || w >= nbigw + nfull) {
+    const int i = w < nbigw ? w : w - nfull;
+    r = m.rorder[i / Hkv];
+    g = i - (i / Hkv) * Hkv;
+    s = m.nsplit[r] - 1;
+  } else {
+    // full splits before request r: work0[r] - r * Hkv
+    const int j = w - nbigw;
+    r = 0;
+    while (r + 1 < m.n_req && j >= m.work0[r + 1] - (r + 1) * Hkv) ++r;
+    const int nf = m.nsplit[r] - 1;
+    const int local = j - (m.work0[r] - r * Hkv);
+    g = local / nf;
+    s = local - g * nf;
+  }
+}
 
 template <typename T>
 struct AttnArgs {
@@ -125,12 +155,10 @@ __global__ __launch_bounds__(64 * (QF / QW), WPE) void attn_kernel(const AttnArg
   const int tid = threadIdx.x;
   const int lane = tid & 63, f = tid >> 6;
   const int r16 = lane & 15, kg = lane >> 4;
-  const int w = blockIdx.x;
-  int r = 0;
-  while (r + 1 < a.meta.n_req && w >= a.meta.work0[r + 1]) ++r;
+  int r, g, s;
+  attn_item(a.meta, a.Hkv, blockIdx.x, r, g, s);
   const int S = a.meta.nsplit[r];
-  const int local = w - a.meta.work0[r];
-  const int g = local / S, s = local - g * S;
+  const int w = a.meta.work0[r] + g * S + s;  // canonical index of this split's partial
   const int ctx = a.meta.ctx[r];
   const int qd = a.Hq * HD, kd = a.Hkv * HD;
   const int GB = a.G * a.B;

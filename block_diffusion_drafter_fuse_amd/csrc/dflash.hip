@@ -661,6 +661,17 @@ void plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPla
     w += d.Hkv * m.nsplit[r];
   }
   m.work0[n_req] = w;
+  // Launch order (see AttnMeta): last splits by descending stage count (the
+  // rest of the context plus one stage for the block), ties by request.
+  int last[kMaxReq];
+  for (int r = 0; r < n_req; ++r) {
+    last[r] = ceil_div(m.ctx[r] - (m.nsplit[r] - 1) * ap->chunk, kAttnStg) + 1;
+    m.rorder[r] = r;
+  }
+  std::stable_sort(m.rorder, m.rorder + n_req, [&](int x, int y) { return last[x] > last[y]; });
+  const int full = ap->chunk / kAttnStg;
+  m.nbig = 0;
+  while (m.nbig < n_req && last[m.rorder[m.nbig]] >= full) ++m.nbig;
 }
 
 // ------------------------------------------------------------------ LM head

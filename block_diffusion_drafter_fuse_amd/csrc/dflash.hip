@@ -68,12 +68,12 @@ constexpr int kAttnTargetWG = DFL_ATTN_TARGET_WG;  // attention work-groups aime
 constexpr int kAttnMinChunk = DFL_ATTN_MIN_CHUNK;  // minimum context keys per split
 constexpr int kAttnNbuf = DFL_ATTN_NBUF;           // attention K/V ring depth
 #ifndef DFL_ATTN_STG
-#define DFL_ATTN_STG 32
+#define DFL_ATTN_STG 64
 #endif
 #ifndef DFL_ATTN_QW
 #define DFL_ATTN_QW 1
 #endif
-constexpr int kAttnStg = DFL_ATTN_STG;             // attention keys per stage
+constexpr int kAttnStg = DFL_ATTN_STG;             // attention keys per stage (bf16, head dim 128, G*B 64)
 constexpr int kAttnWpe = DFL_ATTN_WPE;             // attention waves per SIMD the registers must allow
 constexpr int kAttnQw = DFL_ATTN_QW;   // attention query fragments per wave
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
@@ -595,15 +595,18 @@ void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
     return;
   }
   // A ring of NBUF stages of K/V per work-group (fewer where a stage takes
-  // many copy instructions per wave); QW query fragments per wave.
-  constexpr int STG = kAttnStg;
+  // many copy instructions per wave); QW query fragments per wave.  The
+  // Qwen3-shaped instance (bf16, head dim 128, four query fragments) takes
+  // kAttnStg keys per stage (64: half the barriers of 32-key stages, measured
+  // faster there) and a register cap for kAttnWpe waves per SIMD; the others
+  // keep 32-key stages, whose fewer copies per wave keep them out of spills.
+  constexpr bool kMain = std::is_same<T, bf16_t>::value && HD == 128 && QF == 4;
+  constexpr int STG = kMain ? kAttnStg : 32;
   constexpr int QW = QF % kAttnQw == 0 ? kAttnQw : 1;
   constexpr int NIW = AttnStage<T, HD, QF / QW, 2, STG>::NIW;
   constexpr int NBUF = std::min(kAttnNbuf, 2 + 63 / NIW);
   const int lds = AttnStage<T, HD, QF / QW, NBUF, STG>::LDS;
-  // register cap for four work-groups per CU only where the kernel still fits
-  // without spilling much (bf16, head dim 128, four query fragments)
-  constexpr int WPE = std::is_same<T, bf16_t>::value && HD == 128 && QF == 4 ? kAttnWpe : 1;
+  constexpr int WPE = kMain ? kAttnWpe : 1;
   auto kern = attn_kernel<T, HD, QF, QW, NBUF, STG, WPE>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -661,15 +664,15 @@ void plan_attention(const dflash_ctx* c, int n_req, const int32_t* slot, AttnPla
     w += d.Hkv * m.nsplit[r];
   }
   m.work0[n_req] = w;
-  // Launch order (see AttnMeta): last splits by descending stage count (the
-  // rest of the context plus one stage for the block), ties by request.
+  // Launch order (see AttnMeta): last splits by descending length in 64-key
+  // units (the rest of the context plus one unit for the block), ties by request.
   int last[kMaxReq];
   for (int r = 0; r < n_req; ++r) {
-    last[r] = ceil_div(m.ctx[r] - (m.nsplit[r] - 1) * ap->chunk, kAttnStg) + 1;
+    last[r] = ceil_div(m.ctx[r] - (m.nsplit[r] - 1) * ap->chunk, kAttnStage) + 1;
     m.rorder[r] = r;
   }
   std::stable_sort(m.rorder, m.rorder + n_req, [&](int x, int y) { return last[x] > last[y]; });
-  const int full = ap->chunk / kAttnStg;
+  const int full = ap->chunk / kAttnStage;
   m.nbig = 0;
   while (m.nbig < n_req && last[m.rorder[m.nbig]] >= full) ++m.nbig;
 }

@@ -3,16 +3,21 @@
 Tolerances: fp32 storage paths rel <= 1e-4 (max-norm); bf16 logits
 max|diff| <= 2e-2 * max|logit| against the plain float64 oracle; token ids
 compared wherever the oracle's top-1 minus top-2 logit margin exceeds 0.05
-(top-k: both gaps around a rank); acceptance bit-exact.
+(top-k: both gaps around a rank; for bf16 drafters ranks after the first at
+tests._gpu.BF16_RANK_MARGIN); acceptance bit-exact.
 
 bf16 drafters: token-id and tau decisions are compared against the oracle
 taken in the kernel's storage precision (oracle.round_bf16 at every activation
 a bf16 drafter stores between projections; sums and the residual stream stay
 float64).  The plain oracle differs from any bf16 drafter by about 0.02 rms in
 the logits at the 8B shape (a float emulation of the storage roundings alone
-gives the same figure), which exceeds half the 0.05 margin on some rows; in
-the storage precision the remaining difference (the softmax weights inside the
-attention kernel, accumulation order) stays well inside it."""
+gives the same figure), which exceeds half the 0.05 margin on some rows.  In
+the storage precision about 0.015 rms remains (the softmax weights inside the
+attention kernel, accumulation order, and roundings of slightly different
+values that land on different bf16 neighbours): enough for a top-1 decision at
+the 0.05 margin, but among the ~130 inner ranks of a 16-long list compared per
+request an occasional pair whose gap just clears 0.05 trades places, so those
+ranks use a margin of about five times the spread of a logit difference."""
 import dataclasses
 
 import numpy as np
@@ -21,7 +26,7 @@ import pytest
 import oracle
 import synth
 from synth.configs import QWEN3_4B, QWEN3_8B
-from tests._gpu import GpuDraft, check_top1, check_topk, hidden_rows, log, margin_mask, rel_inf
+from tests._gpu import BF16_RANK_MARGIN, GpuDraft, check_top1, check_topk, hidden_rows, log, margin_mask, rel_inf
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -303,7 +308,7 @@ def _full_size_case(wl, sample_reqs, label, tau_kind, repeat=False):
         ref = o.draft(r, int(anchors[r]))["logits"]
         ref_s = o.draft(r, int(anchors[r]), store=_store(d))["logits"]
         err, mask = _compare_request(lg[r], ids[r], ref, d, 2e-2, f"{label} r{r}", ref_s)
-        _, bad = check_topk(ids16[r], ref_s)
+        _, bad = check_topk(ids16[r], ref_s, thr_rest=BF16_RANK_MARGIN)
         assert len(bad) == 0, f"{label} r{r}: top-16 mismatch at (row, rank) {bad[:5].tolist()}"
         plain_mask, plain_bad = check_top1(ids[r][:, 0], ref)
         plain_agree.append((int(plain_mask.sum()) - len(plain_bad), int(plain_mask.sum())))
@@ -379,7 +384,7 @@ def test_gpu_topk_width_not_a_multiple_of_the_unroll(dtype):
             ref_s = o.draft(r, int(anchors[r]), store=_store(d))["logits"]
             tol = 1e-4 if dtype == "f32" else 2e-2
             _compare_request(lg[r], ids1[r], ref, d, tol, f"D=320 {dtype} r{r}", ref_s)
-            _, bad = check_topk(ids[r], ref_s)
+            _, bad = check_topk(ids[r], ref_s, thr_rest=None if dtype == "f32" else BF16_RANK_MARGIN)
             assert len(bad) == 0, f"D=320 {dtype} r{r} top-{k}: mismatch at {bad[:5].tolist()}"
             # values are the logits of the listed ids
             got = np.take_along_axis(lg[r], ids[r].astype(np.int64), 1)

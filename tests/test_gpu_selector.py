@@ -20,7 +20,7 @@ import oracle
 import synth
 from oracle import dflash2 as ds
 from synth.configs import QWEN3_4B
-from tests._gpu import GpuDraft, check_topk, hidden_rows, log, rel_inf
+from tests._gpu import BF16_RANK_MARGIN, GpuDraft, check_topk, hidden_rows, log, rel_inf
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -54,7 +54,7 @@ def _run(d, seed, bs, ctx, tables_np, zero_a=False, check_top16=True):
     for r in slots:
         out = o.draft(r, int(anchors[r]), store=store)
         if check_top16:
-            _, bad = check_topk(ids[r], out["logits"])
+            _, bad = check_topk(ids[r], out["logits"], thr_rest=BF16_RANK_MARGIN if d.dtype == "bf16" else None)
             assert len(bad) == 0, f"req {r}: top-16 mismatch at {bad[:5]}"
         c, v = oracle.topk(out["logits"], K)
         cand[r], u[r] = c, v

@@ -403,6 +403,39 @@ def measure(wl, w_dev, torch, steps, warmup, label, conv=False):
     return out
 
 
+def measure_lm_shard(workloads, w_dev, torch, steps, warmup, shards=8):
+    """The LM head as one GPU of a vocabulary-sharded deployment would run it:
+    the same step with the vocabulary cut to its first ceil(V/shards) rows,
+    rounded up to whole 64-row groups (the
+    embedding stays tied, anchors drawn inside the shard), the LM-head kernel
+    timed with events.  Each GPU would then all-gather bs*(B-1)*k (value, id)
+    pairs and merge them; that exchange is not part of this single-GPU run."""
+    import dataclasses
+    out = {}
+    for wl in workloads:
+        d = dataclasses.replace(wl.dims, V=-(-wl.dims.V // (shards * 64)) * 64)  # rows kept whole 64-row groups
+        wls = dataclasses.replace(wl, dims=d)
+        w = dict(w_dev)
+        w["embed"] = w_dev["embed"][:d.V]
+        w["w_lm"] = w_dev["w_lm"][:d.V]
+        wb = Workbench(wls, w, torch)
+        wb.prepare_targets()
+        ms, _, kern = wb.timed(steps, warmup, "lm_head")
+        us = kern[0] * 1000
+        rows = wl.bs * (d.B - 1)
+        byts = d.V * d.D * (2 if d.dtype == "bf16" else 4)
+        flops = 2.0 * rows * d.V * d.D
+        ent = {"vocab_rows": d.V, "token_rows": rows, "us_per_launch": round(us, 1),
+               "hbm_GBs": round(byts / us / 1e3, 1), "hbm_roof_frac": round(byts / us / 1e3 / HBM_PEAK_GBS, 4),
+               "mfma_TFLOPs": round(flops / us / 1e6, 1),
+               "mfma_roof_frac": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4),
+               "allgather_bytes_top16": rows * 16 * 8}
+        out[f"{wl.dims.name}_bs{wl.bs}"] = ent
+        del wb
+        torch.cuda.synchronize()
+    return out
+
+
 def measure_prefill(d, w_dev, torch, n_tok, seed, reps=3):
     """Context prefill: one dflash_fuse_ctx call that fuses `n_tok` verifier
     rows of one request (fusion GEMM, RMSNorm and the per-layer context K/V
@@ -804,7 +837,11 @@ def main():
         prefill.insert(0, measure_prefill(w4.dims, w4_dev, torch, 2048, w4.seed))
         del w4_dev
         torch.cuda.synchronize()
-    relay = select = spec = None
+    relay = select = spec = shard = None
+    if not args.no_extras:
+        print(f"[bench] measuring the LM head on one of 8 vocabulary shards", file=sys.stderr, flush=True)
+        shard = measure_lm_shard([wl] + ([synth.get_config(args.companion)] if args.companion else []), w_dev,
+                                 torch, args.steps, args.warmup)
     if not args.no_relay:
         print(f"[bench] measuring the DFlow relay at {args.workload}", file=sys.stderr, flush=True)
         relay = measure_relay(wl, w_dev, torch, args.steps, args.warmup)
@@ -867,6 +904,8 @@ def main():
         line["spec_sampling"] = spec
     if blas:
         line["blas_reference"] = blas
+    if shard:
+        line["lm_head_vocab_shard"] = shard
     print(json.dumps(line), flush=True)
 
 

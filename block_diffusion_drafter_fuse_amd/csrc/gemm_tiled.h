@@ -275,8 +275,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
   float* srow = reinterpret_cast<float*>(lds + 256);
   if (nrm.ssq) {
     constexpr int NT = 64 * NWV;
-    constexpr int TPR = NT / BM >= 1 ? NT / BM : 1;  // threads per row
-    static_assert(NT % BM == 0 || BM % NT == 0, "rows split evenly over the threads");
+    // threads per row: the largest power of two with TPR * BM <= NT (at least 1)
+    constexpr int TPR = NT >= 8 * BM ? 8 : NT >= 4 * BM ? 4 : NT >= 2 * BM ? 2 : 1;
     __syncthreads();
     for (int r0 = 0; r0 < BM; r0 += NT / TPR) {
       const int row = r0 + tid / TPR, sub = tid % TPR;

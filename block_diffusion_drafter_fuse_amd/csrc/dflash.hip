@@ -74,6 +74,7 @@ constexpr int kAttnNbuf = DFL_ATTN_NBUF;           // attention K/V ring depth
 #define DFL_ATTN_QW 1
 #endif
 constexpr int kAttnStg = DFL_ATTN_STG;             // attention keys per stage (bf16, head dim 128, G*B 64)
+constexpr int kAttnShortSplit = 256;               // splits up to this many keys take 32-key stages
 constexpr int kAttnWpe = DFL_ATTN_WPE;             // attention waves per SIMD the registers must allow
 constexpr int kAttnQw = DFL_ATTN_QW;   // attention query fragments per wave
 constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
@@ -597,23 +598,32 @@ void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
   // A ring of NBUF stages of K/V per work-group (fewer where a stage takes
   // many copy instructions per wave); QW query fragments per wave.  The
   // Qwen3-shaped instance (bf16, head dim 128, four query fragments) takes
-  // kAttnStg keys per stage (64: half the barriers of 32-key stages, measured
-  // faster there) and a register cap for kAttnWpe waves per SIMD; the others
-  // keep 32-key stages, whose fewer copies per wave keep them out of spills.
+  // kAttnStg keys per stage on long splits (64: half the barriers of 32-key
+  // stages, measured faster at bs 32) and 32 on splits of at most
+  // kAttnShortSplit keys (bs 1: more stages in flight per split), with a
+  // register cap for kAttnWpe waves per SIMD; the others keep 32-key stages,
+  // whose fewer copies per wave keep them out of spills.
   constexpr bool kMain = std::is_same<T, bf16_t>::value && HD == 128 && QF == 4;
-  constexpr int STG = kMain ? kAttnStg : 32;
   constexpr int QW = QF % kAttnQw == 0 ? kAttnQw : 1;
-  constexpr int NIW = AttnStage<T, HD, QF / QW, 2, STG>::NIW;
-  constexpr int NBUF = std::min(kAttnNbuf, 2 + 63 / NIW);
-  const int lds = AttnStage<T, HD, QF / QW, NBUF, STG>::LDS;
   constexpr int WPE = kMain ? kAttnWpe : 1;
-  auto kern = attn_kernel<T, HD, QF, QW, NBUF, STG, WPE>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr_set = true;
-  }
-  hipLaunchKernelGGL(kern, dim3(work), dim3(64 * (QF / QW)), lds, st, a);
+  auto go = [&](auto stg) {
+    constexpr int STG = decltype(stg)::value;
+    constexpr int NIW = AttnStage<T, HD, QF / QW, 2, STG>::NIW;
+    constexpr int NBUF = std::min(kAttnNbuf, 2 + 63 / NIW);
+    const int lds = AttnStage<T, HD, QF / QW, NBUF, STG>::LDS;
+    auto kern = attn_kernel<T, HD, QF, QW, NBUF, STG, WPE>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                lds);
+      attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(work), dim3(64 * (QF / QW)), lds, st, a);
+  };
+  if (kMain && a.chunk > kAttnShortSplit)
+    go(std::integral_constant<int, kMain ? kAttnStg : 32>{});
+  else
+    go(std::integral_constant<int, 32>{});
 }
 
 template <typename T>

@@ -142,6 +142,26 @@ def test_gpu_tiny_ragged_batch_and_rewind(tiny):
     g.close()
 
 
+def test_gpu_tiny_multi_split_ragged(tiny):
+    """Contexts from empty to 1000 keys in one batch: 128-key attention splits,
+    one to eight per request, last splits shorter and longer than a full one
+    (launched longest first, merged in split order), fp32 against the oracle."""
+    wl, d, w_np = tiny
+    ctxs = [0, 1, 127, 128, 129, 300, 513, 1000]
+    n = len(ctxs)
+    log(f"case tiny multi-split ragged, ctx {ctxs}")
+    slots = list(range(n))
+    g = GpuDraft(d, w_np, max_ctx=max(ctxs) + d.B, max_slots=n, max_batch=n)
+    g.fuse(slots, ctxs, hidden_rows(d, wl.seed, [(r, 0, ctxs[r]) for r in range(n)]))
+    o = _oracle_for(d, w_np, wl.seed, list(enumerate(ctxs)))
+    anchors = synth.make_anchors(d, wl.seed, n)
+    ids, _, lg = g.draft(slots, anchors, top_k=1, logits=True)
+    for r in range(n):
+        ref = o.draft(r, int(anchors[r]))["logits"]
+        _compare_request(lg[r], ids[r], ref, d, 0, f"tiny multi-split r{r} ctx {ctxs[r]}")
+    g.close()
+
+
 def test_gpu_tiny_deterministic(tiny):
     wl, d, w_np = tiny
     log("case tiny determinism")

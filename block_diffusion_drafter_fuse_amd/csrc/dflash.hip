@@ -52,7 +52,7 @@ constexpr int kFuseChunk = 4096;       // rows per fusion launch pair
 // Tuning constants of the attention launch (overridable at build time for
 // sweeps: -DDFL_ATTN_TARGET_WG=... etc.).
 #ifndef DFL_ATTN_TARGET_WG
-#define DFL_ATTN_TARGET_WG 512
+#define DFL_ATTN_TARGET_WG 480
 #endif
 #ifndef DFL_ATTN_MIN_CHUNK
 #define DFL_ATTN_MIN_CHUNK 128

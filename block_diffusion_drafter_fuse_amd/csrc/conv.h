@@ -6,11 +6,12 @@
 // over the block offsets t of one request (x_{-1} = 0: the anchor at offset 0
 // has no left neighbour; offset 1 reads the anchor).  The tap corrections
 // z_t = [W_0; W_1] x_t run on the GEMM engines with the two taps' rows paired
-// (group g of tap 0 beside group g of tap 1), and the tap mix is their epilogue (few token rows, on the GEMV engines).  A lane holds
-// the corrections of groups g..g+3 of both taps for token row m, i.e.
-// everything the 64 channels 16g..16g+63 of y_m need besides the inputs x_m
-// and x_{m-1}, which it reads.  With many token rows the corrections are
-// stored and conv_mix_kernel mixes the taps (two launches per site).
+// (group g of tap 0 beside group g of tap 1).  With few token rows (GEMV
+// engines) the tap mix is their epilogue: a lane holds the corrections of
+// groups g..g+3 of both taps for token row m, i.e. everything the 64 channels
+// 16g..16g+63 of y_m need besides the inputs x_m and x_{m-1}, which it reads.
+// With many token rows the corrections are stored and conv_mix_kernel mixes
+// the taps (two launches per site).
 //  * normed site (attention / FFN input): x is the RMSNorm output, held as
 //    T(h * g) with per-16-channel sums of squares of h; the engine passes the
 //    row scale of row m, and row m-1's is the one held by the lane a row up

@@ -126,6 +126,56 @@ def test_gpu_relay_rounds():
     rig.g.close()
 
 
+def test_gpu_relay_with_conv():
+    """The relay and the DFlash 2 two-tap convolution in the same drafts: the
+    relayed rows enter the block as its inputs and the convolution then runs at
+    all four sites of every layer (oracle: the convolution forward over the
+    relayed block inputs).  Eight rounds of the relay workload."""
+    from oracle import dflash2 as ds
+    wl = synth.get_config("dflow_relay")
+    d, bs, B = wl.dims, wl.bs, wl.dims.B
+    rounds = 8
+    log(f"case dflow relay + dflash2 conv: bs {bs}, B {B}, {rounds} rounds")
+    rig = RelayRig(d, wl.seed, bs, max_ctx=wl.ctx[0] + rounds * B + B)
+    cw = synth.make_conv_weights(d, wl.seed)
+    rig.g.dr.conv_attach([{s: {k: rig.dfa.to_device(v) for k, v in t.items()} for s, t in layer.items()}
+                          for layer in cw])
+    cw32 = synth.conv_weights_as_f32(cw)
+    slots = list(range(bs))
+    rig.g.fuse(slots, wl.n_new, hidden_rows(d, wl.seed, [(r, 0, wl.n_new[r]) for r in range(bs)]))
+    for r in range(bs):
+        rig.o.fuse(r, synth.as_f32(synth.make_hidden(d, wl.seed, r, 0, wl.n_new[r])))
+    anchors = synth.make_anchors(d, wl.seed, bs)
+    nacc = synth.draw_accepted(bs, rounds, B, wl.seed)
+    relayed = 0
+    for t in range(rounds):
+        ids, _, lg = rig.g.draft(slots, anchors, top_k=1, logits=True)
+        cand = np.zeros((bs, B - 1), np.int32)
+        for r in slots:
+            relay_rows = rig.state.take(r)
+            relayed += len(relay_rows)
+            x0 = ofl.block_inputs(rig.w32, d, int(anchors[r]), relay_rows)
+            ref = ds.draft_block_conv(rig.w32, d, rig.o.cache(r), int(anchors[r]), cw32, x0)["logits"]
+            err = rel_inf(lg[r], ref)
+            assert err <= 1e-4, f"round {t} req {r}: logits rel err {err}"
+            _, bad = check_top1(ids[r][:, 0], ref)
+            assert len(bad) == 0, f"round {t} req {r}: top-1 mismatch at {bad}"
+            cand[r] = oracle.topk(ref, 1)[0][:, 0]
+        m = nacc[t]
+        tgt = synth.make_targets(cand, m, d.V, wl.seed * 1000 + t)
+        tau, bonus = rig.g.accept(cand, 1, tgt)
+        pos0 = [rig.o.cache(r).length for r in slots]
+        rig.g.fuse(slots, [int(x) for x in tau], hidden_rows(d, wl.seed, [(r, pos0[r], int(tau[r])) for r in slots]))
+        for r in slots:
+            rig.o.fuse(r, synth.as_f32(synth.make_hidden(d, wl.seed, r, pos0[r], int(tau[r]))))
+        suffix = [synth.make_suffix_hidden(d, wl.seed, r, t, max(0, B - 2 - int(m[r]))) for r in slots]
+        rig.relay(slots, m, cand, bonus, suffix)
+        anchors = bonus.astype(np.int32)
+    log(f"relayed rows used: {relayed}")
+    assert relayed > 10
+    rig.g.close()
+
+
 def test_gpu_relay_dropped_when_length_changes_or_reset():
     wl = synth.get_config("dflow_relay")
     d = wl.dims

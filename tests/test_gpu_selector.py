@@ -31,10 +31,16 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 K = 16
 
 
-def _run(d, seed, bs, ctx, tables_np, zero_a=False, check_top16=True):
+def _run(d, seed, bs, ctx, tables_np, zero_a=False, check_top16=True, conv=False):
     import block_diffusion_drafter_fuse_amd as dfa
     w_np = synth.make_weights(d, seed)
     g = GpuDraft(d, w_np, max_ctx=ctx + d.B, max_slots=bs, max_batch=bs)
+    cw32 = None
+    if conv:
+        cw = synth.make_conv_weights(d, seed)
+        g.dr.conv_attach([{st: {k: dfa.to_device(v) for k, v in t.items()} for st, t in layer.items()}
+                          for layer in cw])
+        cw32 = synth.conv_weights_as_f32(cw)
     slots = list(range(bs))
     g.fuse(slots, [ctx] * bs, hidden_rows(d, seed, [(r, 0, ctx) for r in slots]))
     w32 = synth.weights_as_f32(w_np)
@@ -52,7 +58,10 @@ def _run(d, seed, bs, ctx, tables_np, zero_a=False, check_top16=True):
     # bf16: candidate decisions in the drafter's storage precision
     store = oracle.round_bf16 if d.dtype == "bf16" else None
     for r in slots:
-        out = o.draft(r, int(anchors[r]), store=store)
+        if conv:
+            out = ds.draft_block_conv(w32, d, o.cache(r), int(anchors[r]), cw32)
+        else:
+            out = o.draft(r, int(anchors[r]), store=store)
         if check_top16:
             _, bad = check_topk(ids[r], out["logits"], thr_rest=BF16_RANK_MARGIN if d.dtype == "bf16" else None)
             assert len(bad) == 0, f"req {r}: top-16 mismatch at {bad[:5]}"
@@ -106,6 +115,19 @@ def test_gpu_selector_matches_oracle():
     assert compared >= wl.bs * (d.B - 1) // 2
     # the walk is not simply the per-position argmax on this workload
     assert np.any(path != cand[:, :, 0])
+
+
+def test_gpu_selector_with_conv():
+    """The selector over a draft made with the two-tap convolution attached:
+    the gates read the convolved drafter's final hidden states."""
+    wl = synth.get_config("dflash2_select")
+    d = wl.dims
+    log(f"case dflash2 selector with the convolution: bs {wl.bs}, B {d.B}")
+    tables = synth.make_selector_weights(d, wl.seed)
+    cand, u, path, scores, ref = _run(d, wl.seed, wl.bs, wl.ctx[0], tables, conv=True)
+    compared = _compare(d, wl.bs, path, scores, ref, 1e-4)
+    log(f"path positions compared: {compared} of {wl.bs * (d.B - 1)}")
+    assert compared >= wl.bs * (d.B - 1) // 2
 
 
 def test_gpu_selector_zero_a_is_per_position_argmax():

@@ -9,7 +9,8 @@ copies to or from the host, or clears memory; kernel arguments (slot lengths,
 split plans) are fixed at capture, so the host-side slot lengths are rewound
 after capture exactly as after an eager step.  The graph is replayed several
 times with eager library work and synchronisations in between, and every
-replay is compared with the eager result."""
+replay is compared with the eager result.  The DFlash 2 convolution is
+captured the same way at both of its launch forms."""
 import numpy as np
 import pytest
 
@@ -24,11 +25,15 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
     pytest.skip("needs a GPU", allow_module_level=True)
 
 
-def _run(d, w_np, seed, ctxs, news, top_k, replays=4):
+def _run(d, w_np, seed, ctxs, news, top_k, replays=4, conv=False):
     bs = len(ctxs)
     slots = list(range(bs))
     g = GpuDraft(d, w_np, max_ctx=max(ctxs) + max(news) + d.B, max_slots=bs, max_batch=bs)
     dr, dfa = g.dr, g.dfa
+    if conv:
+        cw = synth.make_conv_weights(d, seed)
+        dr.conv_attach([{st: {k: dfa.to_device(v) for k, v in t.items()} for st, t in layer.items()}
+                        for layer in cw])
     g.fuse(slots, ctxs, hidden_rows(d, seed, [(r, 0, ctxs[r]) for r in slots]))
     hid = [dfa.to_device(h) for h in hidden_rows(d, seed, [(r, ctxs[r], news[r]) for r in slots])]
     anchor = torch.tensor(synth.make_anchors(d, seed, bs), device="cuda")
@@ -88,6 +93,18 @@ def test_gpu_graph_replay_tiny_ragged():
     d = wl.dims
     log("[graph] tiny fp32, bs 4 ragged")
     _run(d, synth.make_weights(d, wl.seed), wl.seed, ctxs=[0, 17, 64, 100], news=[3, 0, 8, 1], top_k=4)
+
+
+@pytest.mark.parametrize("bs", [4, 16])
+def test_gpu_graph_replay_with_conv(bs):
+    """The same with the DFlash 2 convolution attached (4 requests: one launch
+    per site; 16: the corrections GEMM with split K, then the tap mix)."""
+    wl = synth.get_config("dflash2_select")
+    d = wl.dims
+    log(f"[graph] dflash2 conv, fp32, bs {bs}")
+    ctxs = [(7 * r + 5) % 70 for r in range(bs)]
+    news = [(3 * r) % 9 for r in range(bs)]
+    _run(d, synth.make_weights(d, wl.seed), wl.seed, ctxs=ctxs, news=news, top_k=1, conv=True)
 
 
 def test_gpu_graph_replay_qwen3_8b_bs4():

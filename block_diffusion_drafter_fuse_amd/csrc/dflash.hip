@@ -81,7 +81,6 @@ constexpr int kSkinnyMaxM = 64;        // rows handled by the skinny GEMM
 constexpr int kNarrowMaxGroups = 64;   // weights of at most 1024 rows also take the skinny GEMM
 constexpr int kGemvKSW = 8;            // k-steps (activation fragments) per wave in the skinny GEMM
 constexpr int kGemvTB = 8;             // skinny GEMM tiles per barrier batch (LDS: TB x waves x 1 KB)
-constexpr bool kGemvPF = false;        // prefetch the next tile's weights before the current MFMAs
 constexpr int kGemvWGs = 256;          // skinny GEMM work-groups per 16-token block
 constexpr int kGemvXcds = 8;           // XCDs; work-group i runs on XCD i mod 8
 #ifndef DFL_RS_NBUF
@@ -438,10 +437,10 @@ bool launch_skinny(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, co
         hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, st, w, a, nrm, epi, tpw);
       };
       if (xr)
-        launch(gemv_as_kernel<T, KSW, ALO, kGemvTB, kGemvPF, true, Epi>,
+        launch(gemv_as_kernel<T, KSW, ALO, kGemvTB, true, Epi>,
                dim3(kGemvXcds * nwg * ceil_div(mt, kGemvXcds)));
       else
-        launch(gemv_as_kernel<T, KSW, ALO, kGemvTB, kGemvPF, false, Epi>, dim3(nwg, mt));
+        launch(gemv_as_kernel<T, KSW, ALO, kGemvTB, false, Epi>, dim3(nwg, mt));
       return true;
     }
   }

@@ -434,10 +434,10 @@ __device__ __forceinline__ void run_epilogue(const Epi& epi, int m, bool mvalid,
 // activation fragments in registers, so the vector-memory path carries only
 // the weight stream (re-reading activations from L2 costs a third of the
 // bandwidth).  Tiles are processed in batches of up to TB: inside a batch the
-// waves never synchronise (each writes its partial tile to LDS and the next
-// tile's weight loads are issued before the current MFMAs); one barrier per
-// batch, then the partial tiles are summed in wave order and the epilogues
-// run spread over the waves (a paired epilogue takes two consecutive tiles).
+// waves never synchronise (each writes its partial tile to LDS); one barrier
+// per batch, then the partial tiles are summed in wave order and the
+// epilogues run spread over the waves (a paired epilogue takes two
+// consecutive tiles).
 // When K spans several chunks the activations are reloaded per chunk (such
 // GEMMs have one or two tiles per work-group).
 //
@@ -449,7 +449,7 @@ __device__ __forceinline__ void run_epilogue(const Epi& epi, int m, bool mvalid,
 // into one L2 only; the weight, which every XCD then reads, is loaded with
 // ordinary caching.
 
-template <typename T, int KSW, bool ALO, int TB, bool PF, bool XR, class Epi>
+template <typename T, int KSW, bool ALO, int TB, bool XR, class Epi>
 __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, const AOperand<T> a,
                                                         const NormIn nrm, const Epi epi, int tiles_per_wg) {
   using MM = Mma<T>;
@@ -530,25 +530,12 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
     const int items = bt * nchunks;  // (tile, chunk) in order
     const T* wp = wrow(b0);
     uint4 wcur[KSW];
-    if constexpr (PF) load_w(wp, 0, wcur);
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < items; ++it) {
       const int tl = it / nchunks, c = it - tl * nchunks;
       if (nchunks > 1) load_a(c);
-      if constexpr (!PF) {
-        if (c == 0) wp = wrow(b0 + tl);
-        load_w(wp, c, wcur);
-      }
-      uint4 wnext[PF ? KSW : 1];
-      const bool more = it + 1 < items;
-      const T* wpn = wp;
-      if constexpr (PF) {
-        if (more) {
-          const int tn = (it + 1) / nchunks, cn = (it + 1) - tn * nchunks;
-          if (tn != tl) wpn = wrow(b0 + tn);
-          load_w(wpn, cn, wnext);
-        }
-      }
+      if (c == 0) wp = wrow(b0 + tl);
+      load_w(wp, c, wcur);
 #pragma unroll
       for (int j = 0; j < KSW; ++j) {
         acc = MM::step(wcur[j], areg[j], acc);
@@ -557,13 +544,6 @@ __global__ __launch_bounds__(1024) void gemv_as_kernel(const WOperand<T> w, cons
       if (c == nchunks - 1) {
         red[(tl * NW + wave) * 64 + lane] = acc;
         acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
-      if constexpr (PF) {
-        if (more) {
-          wp = wpn;
-#pragma unroll
-          for (int j = 0; j < KSW; ++j) wcur[j] = wnext[j];
-        }
       }
     }
     const bool first = b0 == t_begin;

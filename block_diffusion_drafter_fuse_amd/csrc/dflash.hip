@@ -732,8 +732,8 @@ void run_lmhead(dflash_ctx* c, hipStream_t st, int n_req, int top_k, int32_t* ou
     hipLaunchKernelGGL(top1_merge_kernel, dim3(Mlm), dim3(1024), 0, st, pv, pi, nchunk, out_ids, out_vals, tile_ctr,
                        64);
   else
-    hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, Mlm, top_k,
-                       out_ids, out_vals, tile_ctr, 64);
+    hipLaunchKernelGGL((topk_merge_kernel<16>), dim3(Mlm), dim3(256), 0, st, pv, pi, nchunk, top_k, out_ids,
+                       out_vals, tile_ctr, 64);
 }
 
 // ------------------------------------------------------------------ draft

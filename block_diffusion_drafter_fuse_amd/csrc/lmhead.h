@@ -217,10 +217,10 @@ struct EpiTop1 {
 // KTOP rounds of a block-wide (value, id) maximum over the list heads.
 template <int KTOP>
 __global__ __launch_bounds__(256) void topk_merge_kernel(const float* part_v, const int* part_i,
-                                                         int nchunk, int M, int top_k, int* out_ids,
+                                                         int nchunk, int top_k, int* out_ids,
                                                          float* out_vals, int* tile_ctr, int nctr) {
   const int m = blockIdx.x;
-  if (m == 0 && threadIdx.x < nctr) tile_ctr[threadIdx.x] = 0;  // LM-head tile counters for the next call
+  if (m == 0 && (int)threadIdx.x < nctr) tile_ctr[threadIdx.x] = 0;  // LM-head tile counters for the next call
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   float lv[KTOP];
   int li[KTOP];
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(1024) void top1_merge_kernel(const float* part_v, c
                                                           int* out_ids, float* out_vals, int* tile_ctr,
                                                           int nctr) {
   const int m = blockIdx.x;
-  if (m == 0 && threadIdx.x < nctr) tile_ctr[threadIdx.x] = 0;  // small LM-head tile counters, next call
+  if (m == 0 && (int)threadIdx.x < nctr) tile_ctr[threadIdx.x] = 0;  // small LM-head tile counters, next call
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* pv = part_v + (size_t)m * nchunk;
   const int* pi = part_i + (size_t)m * nchunk;

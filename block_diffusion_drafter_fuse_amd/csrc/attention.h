@@ -14,7 +14,9 @@
 // wave computes S^T = K Q^T and O^T += V^T P^T with MFMA and keeps an online
 // softmax per query column, then stores its partial (max, sum, O).  The
 // combine kernel merges the splits of every (r, g) in split order, so results
-// are deterministic.
+// are deterministic.  Work-groups are launched longest split first (AttnMeta),
+// which packs a ragged batch's splits onto the CUs; the partials keep their
+// request-major index.
 //
 // Layouts: Q, K_b rows [M, heads*hd]; V_b transposed vbT[(r*Hkv+g)*hd + d][64]
 // (zero padded past B); cache keys [pos][hd] and values in kVTile-key tiles

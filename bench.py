@@ -20,7 +20,10 @@ comes from an event after every timed step.
 events recorded by the library on the launch stream over a second pass of the
 timed steps (the step time itself comes from an uninstrumented pass);
 its achieved rate is the kernel's algorithmic bytes (HBM-bound kernels) or
-flops (MFMA-bound) per launch divided by its mean launch time.
+flops (MFMA-bound) per launch divided by its mean launch time, against the
+nominal MI355X peak; `achievable_peaks` adds what standard operations reach
+on the same GPU (a plain 1 GiB device copy, a reduction over 1 GiB, an 8192^3
+bf16 GEMM of the vendor library) as context for those fractions.
 `cpu_baseline` times the float64 CPU oracle on a sample of the same workload's
 requests (evenly spaced context quantiles) and scales it to the whole batch
 step; it records the host CPU count, the BLAS vendor and threads, and one
@@ -714,6 +717,58 @@ def cpu_baseline(wl, w_np, n_sample=6):
             "single_thread": single}
 
 
+def achievable_peaks(torch, reps=10):
+    """Measured ceilings beside the nominal peaks: HBM read+write rate of a
+    plain device-to-device copy of 1 GiB (torch's copy kernel), HBM read rate of
+    a reduction over 1 GiB (torch's sum), and the bf16 rate of one large square
+    GEMM (torch.mm, i.e. the vendor library, 8192^3).  Context for the roofline
+    fractions, which stay against the nominal peaks."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del dst
+    x = src.view(torch.float32)  # 1 GiB read by a reduction (the read-only ceiling)
+    for _ in range(2):
+        x.sum()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    read_gbs = 1.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, x
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    for _ in range(2):
+        torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    tflops = 2.0 * m ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b
+    torch.cuda.synchronize()
+    return {"hbm_copy_GBs": round(copy_gbs, 1), "hbm_copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "hbm_read_GBs": round(read_gbs, 1), "hbm_read_frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4),
+            "bf16_gemm_8192_TFLOPs": round(tflops, 1),
+            "bf16_gemm_frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4)}
+
+
 def blas_reference(wl, torch, reps=20):
     """The vendor library's bf16 GEMM (torch.nn.functional.linear, which calls
     hipBLASLt) on the projection shapes of the workload's draft step, with
@@ -858,6 +913,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     blas = blas_reference(wl, torch) if args.blas_reference else None
+    peaks = None if args.no_extras else achievable_peaks(torch)
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -906,6 +962,8 @@ def main():
         line["blas_reference"] = blas
     if shard:
         line["lm_head_vocab_shard"] = shard
+    if peaks:
+        line["achievable_peaks"] = peaks
     print(json.dumps(line), flush=True)
 
 

@@ -234,6 +234,36 @@ def test_gpu_tiny_max_batch_and_full_slots(tiny):
     g.close()
 
 
+def test_gpu_empty_calls_are_no_ops(tiny):
+    """Zero requests, and requests with no new rows, launch nothing: slot
+    lengths, the caches and the next draft are unchanged, and the caller's
+    output buffers are not written."""
+    wl, d, w_np = tiny
+    log("case empty calls")
+    g = GpuDraft(d, w_np, max_ctx=64, max_slots=2, max_batch=2)
+    g.fuse([0, 1], [5, 9], hidden_rows(d, wl.seed, [(0, 0, 5), (1, 0, 9)]))
+    anchors = synth.make_anchors(d, wl.seed, 2)
+    ids, _, lg = g.draft([0, 1], anchors, top_k=2, logits=True)
+    k0, v0 = g.read_cache(1, 0, 0, 9)
+    # fusion: no requests; requests with zero rows (no hidden-state pointers needed)
+    g.dr.fuse_ctx([], [], [])
+    g.dr.fuse_ctx([0, 1], [0, 0], [])
+    # draft: no requests, with sentinel outputs that must stay untouched
+    out = torch.full((1, d.B - 1, 2), 7, dtype=torch.int32, device="cuda")
+    g.dr.draft_block([], None, 2, out)
+    torch.cuda.synchronize()
+    assert int((out != 7).sum()) == 0
+    assert g.dr.slot_len(0) == 5 and g.dr.slot_len(1) == 9
+    k1, v1 = g.read_cache(1, 0, 0, 9)
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
+    ids2, _, lg2 = g.draft([0, 1], anchors, top_k=2, logits=True)
+    assert np.array_equal(ids2, ids) and np.array_equal(lg2, lg)
+    # an empty acceptance scan is a no-op too
+    dfa = g.dfa
+    dfa.accept(0, d.B, None, d.B - 1, None, None, None)
+    g.close()
+
+
 def test_gpu_capacity_errors_leave_state(tiny):
     import block_diffusion_drafter_fuse_amd as dfa
     wl, d, w_np = tiny

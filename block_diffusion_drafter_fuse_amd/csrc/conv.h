@@ -107,44 +107,50 @@ struct ConvMixArgs {
   float* ssq_out;     // residual site: [M, D/16]
 };
 
-// Row scale 1/sqrt(mean + eps) of row m from its per-16-channel sums of squares.
-template <int NT>
-__device__ __forceinline__ float conv_row_scale(const float* ssq, int m, int nslot, float inv_d, float eps,
-                                                float* red) {
+// Row scale 1/sqrt(mean + eps) of row m from its per-16-channel sums of
+// squares, reduced by one wave in a fixed order (lane-strided partial sums,
+// then a butterfly): no work-group barrier, every wave holds the result.
+__device__ __forceinline__ float conv_row_scale(const float* ssq, int m, int nslot, float inv_d, float eps) {
+  const float* p = ssq + (size_t)m * nslot;
   float s = 0.f;
-  for (int i = threadIdx.x; i < nslot; i += NT) s += ssq[(size_t)m * nslot + i];
+  for (int i = threadIdx.x & 63; i < nslot; i += 64) s += p[i];
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  float t = 0.f;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) t += red[w];
-  __syncthreads();
-  return 1.0f / sqrtf(t * inv_d + eps);
+  return 1.0f / sqrtf(s * inv_d + eps);
 }
 
-// One 256-thread work-group per block row m = r * B + t; thread i handles the
-// 4-channel vectors c = 4 i + 1024 p (a 16-channel slot is 4 adjacent lanes).
+// One work-group per block row m = r * B + t (blockDim a multiple of 64, up
+// to 1024), one 4-channel vector c = 4 i + 4 blockDim p per thread and pass (a
+// 16-channel slot is 4 adjacent lanes).  The first pass's inputs are loaded
+// before the row scales are reduced, so the two memory round trips overlap.
 template <typename T, bool RESID>
-__global__ __launch_bounds__(256) void conv_mix_kernel(const ConvMixArgs<T> a) {
-  __shared__ float red[4];
+__global__ __launch_bounds__(1024) void conv_mix_kernel(const ConvMixArgs<T> a) {
   const int m = blockIdx.x, t = m % a.B;
   const int D = a.D, G = D >> 4;
+  const int step = (int)blockDim.x * 4;
+  int c = threadIdx.x * 4;
+  f32x4_t xt = {0.f, 0.f, 0.f, 0.f}, xl = {0.f, 0.f, 0.f, 0.f};
+  if (c < D) {
+    xt = load4<T>(a.in + (size_t)m * D + c);
+    if (t > 0) xl = load4<T>(a.in + (size_t)(m - 1) * D + c);
+  }
   float sc = 1.0f, scl = 1.0f;
   if (!RESID) {
-    sc = conv_row_scale<256>(a.ssq, m, G, a.inv_d, a.eps, red);
-    if (t > 0) scl = conv_row_scale<256>(a.ssq, m - 1, G, a.inv_d, a.eps, red);
+    sc = conv_row_scale(a.ssq, m, G, a.inv_d, a.eps);
+    if (t > 0) scl = conv_row_scale(a.ssq, m - 1, G, a.inv_d, a.eps);
   }
   const float* z = a.z + (size_t)m * 2 * G;
-  for (int c = threadIdx.x * 4; c < D; c += 1024) {
-    const f32x4_t xt = load4<T>(a.in + (size_t)m * D + c) * sc;
-    const f32x4_t xl = t > 0 ? load4<T>(a.in + (size_t)(m - 1) * D + c) * scl : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (; c < D; c += step) {
+    if (c >= step) {  // later passes (D > 4 blockDim)
+      xt = load4<T>(a.in + (size_t)m * D + c);
+      if (t > 0) xl = load4<T>(a.in + (size_t)(m - 1) * D + c);
+    }
+    const f32x4_t xs = xt * sc, xls = xl * scl;
     const float z0 = z[c >> 4], z1 = z[G + (c >> 4)];
     const f32x4_t k0 = load4<T>(a.kbase + c), k1 = load4<T>(a.kbase + D + c);
     f32x4_t y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[i] = (k0[i] + z0) * xt[i] + (k1[i] + z1) * xl[i];
+    for (int i = 0; i < 4; ++i) y[i] = (k0[i] + z0) * xs[i] + (k1[i] + z1) * xls[i];
     if constexpr (!RESID) {
       store4<T>(a.y + (size_t)m * D + c, y[0], y[1], y[2], y[3]);
     } else {

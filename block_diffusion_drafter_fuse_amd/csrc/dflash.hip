@@ -851,10 +851,11 @@ void run_draft(dflash_ctx* c, hipStream_t st, int n_req, const int32_t* slot, co
     ca.u = u;
     ca.g = g_next_norm;
     ca.ssq_out = ssq;
+    const int nt = std::min(1024, round_up(d.D / 4, 64));  // one 4-channel vector per thread (D <= 4096)
     if (normed)
-      hipLaunchKernelGGL((conv_mix_kernel<T, false>), dim3(M), dim3(256), 0, st, ca);
+      hipLaunchKernelGGL((conv_mix_kernel<T, false>), dim3(M), dim3(nt), 0, st, ca);
     else
-      hipLaunchKernelGGL((conv_mix_kernel<T, true>), dim3(M), dim3(256), 0, st, ca);
+      hipLaunchKernelGGL((conv_mix_kernel<T, true>), dim3(M), dim3(nt), 0, st, ca);
   };
   for (int l = 0; l < d.N; ++l) {
     const dflash_layer_weights& lw = c->layers[l];

@@ -18,6 +18,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -99,6 +100,19 @@ constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, 
 constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
 constexpr size_t kPartFloats = size_t(16) << 20;  // split-K partials (64 MB)
 constexpr int kCounters = 1 << 16;
+
+// Raises a kernel's dynamic-LDS limit to `bytes`, once per device: the
+// attribute belongs to the kernel on the device current when it is set, so a
+// process driving several GPUs sets it on each.  `done` is the call site's own
+// bitmask of devices already set (one per kernel instance).
+void set_lds_limit(std::atomic<uint64_t>& done, const void* kern, int bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  const uint64_t bit = uint64_t(1) << dev;
+  if (done.load(std::memory_order_acquire) & bit) return;
+  (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  done.fetch_or(bit, std::memory_order_acq_rel);
+}
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -336,11 +350,8 @@ void launch_tiled(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, con
   const int nblocks = tiles * SK;
   const int lds = C::NBUF * ((ALO ? 2 : 1) * C::BM + C::BN) * 128;
   auto kern = gemm_tiled_kernel<T, C::BM, C::BN, C::WM, C::WN, C::NBUF, ALO, Epi>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  set_lds_limit(lds_set, reinterpret_cast<const void*>(kern), lds);
   hipLaunchKernelGGL(kern, dim3(round_up(nblocks, 8)), dim3(64 * C::WM * C::WN), lds, st, w, a, nrm, sk, epi,
                      nblocks);
 }
@@ -402,12 +413,8 @@ bool launch_skinny(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, co
     if (uses_gemv(a.M, w.ngroups) && mt < kGemvXcds && plan_rs<T, ALO, Epi>(w, a, mt, &rp)) {
       // Row-streaming GEMV (few token blocks against a wide weight).
       auto kern = gemv_rs_kernel<T, kRsNbuf, ALO, Epi::kPaired, Epi>;
-      static bool attr_set = false;
-      if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  kRsLdsMax);
-        attr_set = true;
-      }
+      static std::atomic<uint64_t> lds_set{0};
+      set_lds_limit(lds_set, reinterpret_cast<const void*>(kern), kRsLdsMax);
       const RsSplit sp{rp.nsplit, rp.nst, rp.red2, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off)};
       hipLaunchKernelGGL(kern, dim3(rp.nwg, rp.nsplit * mt), dim3(1024), rp.lds, st, w, a, nrm, sp, epi, rp.tpw);
       return true;
@@ -428,12 +435,8 @@ bool launch_skinny(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, co
       // row blocks kept on one XCD each once there are enough to go round
       const bool xr = mt >= kGemvXcds;
       auto launch = [&](auto kern, dim3 grid) {
-        static bool attr_set = false;
-        if (!attr_set) {
-          (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kGemvTB * 16 * 64 * 16);
-          attr_set = true;
-        }
+        static std::atomic<uint64_t> lds_set{0};
+        set_lds_limit(lds_set, reinterpret_cast<const void*>(kern), kGemvTB * 16 * 64 * 16);
         hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, st, w, a, nrm, epi, tpw);
       };
       if (xr)
@@ -611,12 +614,8 @@ void launch_attn(const AttnArgs<T>& a, int work, bool combine, hipStream_t st) {
     constexpr int NBUF = std::min(kAttnNbuf, 2 + 63 / NIW);
     const int lds = AttnStage<T, HD, QF / QW, NBUF, STG>::LDS;
     auto kern = attn_kernel<T, HD, QF, QW, NBUF, STG, WPE>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                lds);
-      attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};
+    set_lds_limit(lds_set, reinterpret_cast<const void*>(kern), lds);
     hipLaunchKernelGGL(kern, dim3(work), dim3(64 * (QF / QW)), lds, st, a);
   };
   if (kMain && a.chunk > kAttnShortSplit)
@@ -693,12 +692,8 @@ void launch_lm_small(const LmArgs<T>& la, int nchunk, int rowblocks, int* tile_c
   // staged rows, reused afterwards for the 16 x 64 x KTOP list merge and its list heads
   const int lds = std::max(16 * (la.a.kseg * (int)sizeof(T) + 16), 16 * 64 * KTOP * 8 + 16 * 64);  // <= kLdsMax (checked)
   auto kern = lmhead_lds_kernel<T, KTOP, kLmFN, kLmU>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                              160 * 1024);
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  set_lds_limit(lds_set, reinterpret_cast<const void*>(kern), 160 * 1024);
   hipLaunchKernelGGL(kern, dim3(nchunk, rowblocks), dim3(1024), lds, st, la, tile_ctr);
 }
 

@@ -264,6 +264,46 @@ def test_gpu_empty_calls_are_no_ops(tiny):
     g.close()
 
 
+# Head-dim / dtype pairs the other cases leave out (fp32 runs head dim 64 and
+# bf16 head dim 128 elsewhere): each attention instance with its query
+# fragments per work-group, over ragged multi-split contexts and more than
+# 64 token rows.
+CROSS_CASES = [
+    # dtype, hd, Hq, Hkv, B
+    ("f32", 128, 8, 2, 16),    # four query fragments (G*B = 64)
+    ("bf16", 64, 8, 2, 16),    # four query fragments
+    ("bf16", 64, 4, 4, 8),     # one query fragment (G*B = 8)
+    ("bf16", 128, 8, 4, 16),   # two query fragments (G*B = 32)
+]
+
+
+@pytest.mark.parametrize("dtype,hd,Hq,Hkv,B", CROSS_CASES)
+def test_gpu_head_dim_dtype_cross(dtype, hd, Hq, Hkv, B):
+    d = dataclasses.replace(synth.get_config("tiny").dims, dtype=dtype, D=512, Dt=256, L=3, Hq=Hq, Hkv=Hkv,
+                            hd=hd, I=1024, V=2048, B=B)
+    seed = 31
+    ctxs = [0, 37, 300, 700, 1000]
+    n = len(ctxs)
+    log(f"case cross {dtype} hd {hd} Hq {Hq} Hkv {Hkv} B {B}, ctx {ctxs}")
+    w_np = synth.make_weights(d, seed)
+    g = GpuDraft(d, w_np, max_ctx=1024, max_slots=n, max_batch=n)
+    g.fuse(list(range(n)), ctxs, hidden_rows(d, seed, [(r, 0, ctxs[r]) for r in range(n)]))
+    anchors = synth.make_anchors(d, seed, n)
+    ids, _, lg = g.draft(list(range(n)), anchors, top_k=4, logits=True)
+    o = _oracle_for(d, w_np, seed, list(enumerate(ctxs)))
+    n_cmp = 0
+    for r in range(n):
+        ref = o.draft(r, int(anchors[r]))["logits"]
+        ref_s = None if dtype == "f32" else o.draft(r, int(anchors[r]), store=_store(d))["logits"]
+        _, mask = _compare_request(lg[r], ids[r], ref, d, 2e-2, f"cross {dtype} hd {hd} r{r}", ref_s)
+        _, bad = check_topk(ids[r], ref if ref_s is None else ref_s,
+                            thr_rest=None if ref_s is None else BF16_RANK_MARGIN)
+        assert len(bad) == 0, f"cross {dtype} hd {hd} r{r}: top-4 mismatch at {bad[:5].tolist()}"
+        n_cmp += int(mask.sum())
+    assert n_cmp > 0, "no row cleared the top-1 margin"
+    g.close()
+
+
 def test_gpu_capacity_errors_leave_state(tiny):
     import block_diffusion_drafter_fuse_amd as dfa
     wl, d, w_np = tiny

@@ -110,3 +110,11 @@ def test_traffic_summary_scales_by_the_reference_copy():
     k = t["kernels"]["wl:qkv_gemm"]
     assert k["fetch_bytes"] == 2 * 1000 * 1024 and k["write_bytes"] == 100 * 1024
     assert k["bytes_per_launch"] == k["fetch_bytes"] + k["write_bytes"]
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import subprocess, sys, os
+    r = subprocess.run([sys.executable, os.path.join(os.path.dirname(bench.__file__), "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""

@@ -1247,6 +1247,7 @@ int dflow_relay(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slo
   }
   rm.row0[n_req] = row;
   if (total > 0) {
+    if (ctx->d.D > 4 * 256 * kRelayMaxPass) return fail(DFLASH_EUNSUPPORTED, "the relay needs D <= 16384");
     if (!cand || !bonus) return fail(DFLASH_EINVAL, "cand and bonus must not be NULL");
     if (cand_stride < 1) return fail(DFLASH_EINVAL, "cand_stride must be >= 1");
     if (!rw || !rw->w1 || !rw->w2) return fail(DFLASH_EINVAL, "relay weights must not be NULL");

@@ -2,6 +2,7 @@
 // read-back.
 #pragma once
 #include "common.h"
+#include "gemm.h"
 
 namespace dfl {
 
@@ -110,7 +111,11 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* embed, const T* e_m
 // shared fusion projection (hc holds T(z * g_c), fssq the per-16-feature sums
 // of squares of z), then writes the relay MLP input row
 // [E(bonus); E(first rejection); h] (K = 3D, storage dtype) and LN(h) in fp32
-// (population variance, eps 1e-5, no affine).
+// (population variance, eps 1e-5, no affine).  The row of T(z * g_c) is read
+// once, 4 features per thread and pass, and held in registers for the mean,
+// the variance and the writes (D <= 4 * 256 * kRelayMaxPass).
+constexpr int kRelayMaxPass = 16;
+
 template <typename T>
 __global__ __launch_bounds__(256) void relay_assemble_kernel(const T* hc, const float* fssq, int D, float eps,
                                                              const T* embed, int V, const int* bonus,
@@ -119,8 +124,14 @@ __global__ __launch_bounds__(256) void relay_assemble_kernel(const T* hc, const 
   const int m = blockIdx.x;
   const int r = relay_req_of_row(rm, m);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ float red[2][4];
+  __shared__ float red[3][4];
   const int nslot = D >> 4;
+  f32x4_t hv[kRelayMaxPass];
+#pragma unroll
+  for (int p = 0; p < kRelayMaxPass; ++p) {
+    const int c = (tid + 256 * p) * 4;
+    hv[p] = c < D ? load4<T>(hc + (size_t)m * D + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
   // mean of z^2 from the slot sums
   float ss = 0.f;
   for (int i = tid; i < nslot; i += 256) ss += fssq[(size_t)m * nslot + i];
@@ -128,33 +139,45 @@ __global__ __launch_bounds__(256) void relay_assemble_kernel(const T* hc, const 
   if (lane == 0) red[0][wave] = ss;
   __syncthreads();
   const float rs = rsqrtf((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)D + eps);
-  // mean and variance of h = T(z*g) * rs
+  // mean and variance of h = T(z*g) * rs (padding lanes hold zeros and are
+  // left out of the variance)
   float s1 = 0.f;
-  for (int c = tid; c < D; c += 256) s1 += to_f<T>(hc[(size_t)m * D + c]) * rs;
+#pragma unroll
+  for (int p = 0; p < kRelayMaxPass; ++p) {
+    hv[p] = hv[p] * rs;
+    s1 += (hv[p][0] + hv[p][1]) + (hv[p][2] + hv[p][3]);
+  }
   s1 = wave_sum(s1);
   if (lane == 0) red[1][wave] = s1;
   __syncthreads();
   const float mu = (red[1][0] + red[1][1] + red[1][2] + red[1][3]) / (float)D;
   float s2 = 0.f;
-  for (int c = tid; c < D; c += 256) {
-    const float dv = to_f<T>(hc[(size_t)m * D + c]) * rs - mu;
-    s2 += dv * dv;
+#pragma unroll
+  for (int p = 0; p < kRelayMaxPass; ++p) {
+    if ((tid + 256 * p) * 4 >= D) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float dv = hv[p][e] - mu;
+      s2 += dv * dv;
+    }
   }
   s2 = wave_sum(s2);
+  if (lane == 0) red[2][wave] = s2;
   __syncthreads();
-  if (lane == 0) red[0][wave] = s2;
-  __syncthreads();
-  const float rstd = rsqrtf((red[0][0] + red[0][1] + red[0][2] + red[0][3]) / (float)D + 1e-5f);
+  const float rstd = rsqrtf((red[2][0] + red[2][1] + red[2][2] + red[2][3]) / (float)D + 1e-5f);
   int b = bonus[r], y = cand[((size_t)r * Bm1 + rm.nacc[r]) * cand_stride];
   b = b < 0 ? 0 : (b >= V ? V - 1 : b);
   y = y < 0 ? 0 : (y >= V ? V - 1 : y);
   T* row = in + (size_t)m * 3 * D;
-  for (int c = tid; c < D; c += 256) {
-    const float h = to_f<T>(hc[(size_t)m * D + c]) * rs;
-    row[c] = embed[(size_t)b * D + c];
-    row[D + c] = embed[(size_t)y * D + c];
-    row[2 * D + c] = from_f<T>(h);
-    lnh[(size_t)m * D + c] = (h - mu) * rstd;
+#pragma unroll
+  for (int p = 0; p < kRelayMaxPass; ++p) {
+    const int c = (tid + 256 * p) * 4;
+    if (c >= D) continue;
+    const f32x4_t eb = load4<T>(embed + (size_t)b * D + c), ey = load4<T>(embed + (size_t)y * D + c);
+    store4<T>(row + c, eb[0], eb[1], eb[2], eb[3]);
+    store4<T>(row + D + c, ey[0], ey[1], ey[2], ey[3]);
+    store4<T>(row + 2 * D + c, hv[p][0], hv[p][1], hv[p][2], hv[p][3]);
+    *reinterpret_cast<f32x4_t*>(lnh + (size_t)m * D + c) = (hv[p] - mu) * rstd;
   }
 }
 
@@ -170,33 +193,33 @@ template <typename T>
 __global__ __launch_bounds__(256) void select_tables_kernel(const int* anchor, const int* cand, const float* ul,
                                                             int k, int Tn, const T* ta, const T* tb, int R,
                                                             const float* gates, int V, float* tables) {
-  __shared__ float sa[kSelMaxK][kSelMaxR + 1];
-  __shared__ float sb[kSelMaxK][kSelMaxR + 1];
-  __shared__ float sg[kSelMaxR];
+  // rows of A * g_t and of B, 16-byte aligned, read back 4 features at a time
+  __shared__ __align__(16) float sa[kSelMaxK][kSelMaxR + 4];
+  __shared__ __align__(16) float sb[kSelMaxK][kSelMaxR + 4];
   const int r = blockIdx.x, t = blockIdx.y;
   const int na = t == 0 ? 1 : k;
   const float* g = gates + ((size_t)r * Tn + t) * R;
-  for (int c = threadIdx.x; c < R; c += blockDim.x) sg[c] = g[c];
-  constexpr int EPV = 16 / (int)sizeof(T);  // table elements per 16-byte load
-  const int cpr = R / EPV;                   // 16-byte chunks per row
+  const int cpr = R / 4;  // 4-feature chunks per row
   for (int e = threadIdx.x; e < (na + k) * cpr; e += blockDim.x) {
-    const int row = e / cpr, c = (e - row * cpr) * EPV;
+    const int row = e / cpr, c = (e - row * cpr) * 4;
     int id;
     if (row < na) id = t == 0 ? anchor[r] : cand[((size_t)r * Tn + t - 1) * k + row];
     else id = cand[((size_t)r * Tn + t) * k + row - na];
     id = id < 0 ? 0 : (id >= V ? V - 1 : id);
-    const uint4 v = ld16((row < na ? ta : tb) + (size_t)id * R + c);
-    const T* ev = reinterpret_cast<const T*>(&v);
-    float* dst = row < na ? &sa[row][c] : &sb[row - na][c];
-#pragma unroll
-    for (int x = 0; x < EPV; ++x) dst[x] = to_f<T>(ev[x]);
+    f32x4_t v = load4<T>((row < na ? ta : tb) + (size_t)id * R + c);
+    if (row < na) v = v * *reinterpret_cast<const f32x4_t*>(g + c);
+    *reinterpret_cast<f32x4_t*>(row < na ? &sa[row][c] : &sb[row - na][c]) = v;
   }
   __syncthreads();
   const int i = threadIdx.x / k, j = threadIdx.x - i * k;
   if (i >= k) return;
   const int ia = t == 0 ? 0 : i;
   float s = 0.f;
-  for (int c = 0; c < R; ++c) s += sa[ia][c] * sg[c] * sb[j][c];
+  for (int c = 0; c < R; c += 4) {
+    const f32x4_t a4 = *reinterpret_cast<const f32x4_t*>(&sa[ia][c]);
+    const f32x4_t b4 = *reinterpret_cast<const f32x4_t*>(&sb[j][c]);
+    s += ((a4[0] * b4[0] + a4[1] * b4[1]) + (a4[2] * b4[2] + a4[3] * b4[3]));
+  }
   tables[(((size_t)r * Tn + t) * k + i) * k + j] = ul[((size_t)r * Tn + t) * k + j] + s;
 }
 

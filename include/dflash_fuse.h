@@ -235,7 +235,7 @@ typedef struct dflow_relay_weights {
  * Stored rows are bound to the slot and its current length: the next
  * dflash_draft_block on the slot at that length uses them; a draft at another
  * length, dflash_slot_reset or the next dflow_relay drops them.  Uses the
- * workspace. */
+ * workspace.  Requires D <= 16384 (EUNSUPPORTED otherwise). */
 int dflow_relay(dflash_ctx* ctx, void* stream, int32_t n_req, const int32_t* slot, const int32_t* n_acc,
                 const int32_t* cand, int32_t cand_stride, const int32_t* bonus,
                 const void* const* tgt_hidden, const dflow_relay_weights* rw);

@@ -148,3 +148,45 @@ def test_spec_draft_static_rejects_bad_sizes_before_any_launch():
     assert f(None, 1, 1024, 16, None, 0.0, 0, None, None, None) == -1        # temperature
     assert f(None, 0, 1024, 16, None, 1.0, 0, None, None, None) == 0         # nothing to do
     assert f(None, 1, 1024, 16, None, 1.0, 0, None, None, None) == -1        # NULL logits
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """A C99 caller: the header is valid C, the library links by name, and the
+    sizes it reports for the Qwen3-8B bs 32 shape equal the ctypes binding's."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "caller.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "dflash_fuse.h"
+int main(void) {
+  dflash_dims d;
+  size_t kv = 0, ws = 0;
+  int rc;
+  d.dtype = DFLASH_BF16; d.D = 4096; d.L = 5; d.Dt = 4096; d.N = 5; d.Hq = 32; d.Hkv = 8; d.hd = 128;
+  d.I = 12288; d.V = 151936; d.B = 16; d.max_ctx = 8208; d.max_slots = 32; d.max_batch = 32;
+  d.rope_base = 10000.0f; d.rms_eps = 1e-6f; d.use_rope = 1;
+  rc = dflash_query_sizes(&d, &kv, &ws);
+  printf("%d %zu %zu\n", rc, kv, ws);
+  d.hd = 96;
+  printf("%d %s\n", dflash_query_sizes(&d, &kv, &ws), dflash_strerror(DFLASH_EUNSUPPORTED));
+  return rc;
+}
+''')
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(dfa.LIB_PATH)
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src),
+                        "-L", libdir, "-ldflash_fuse", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    first, second = out.stdout.splitlines()[:2]
+    rc, kv, ws = (int(x) for x in first.split())
+    d = synth.get_config("qwen3_8b_bs32").dims
+    kv_py, ws_py = dfa.query_sizes(dfa.make_dims(d, 8208, 32, 32))
+    assert rc == 0 and (kv, ws) == (kv_py, ws_py)
+    assert second.split()[0] == "-2"

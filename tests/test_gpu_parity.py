@@ -441,6 +441,58 @@ def test_gpu_qwen3_4b_bs1():
     _full_size_case(synth.get_config("qwen3_4b_bs1"), [0], "qwen3_4b_bs1", "uniform")
 
 
+def test_gpu_qwen3_4b_bs1_decode_loop():
+    """Six steady-state steps at the Qwen3-4B bs1 shape: each step drafts on the
+    GPU and in the oracle, compares logits and top-1, draws the verifier targets
+    from the oracle's candidates (tau ~ U{1..16}), takes tau and the bonus from
+    the oracle's scan (the GPU scan is checked on its own candidates), fuses
+    the tau committed rows into both and anchors the next block at the bonus
+    token; both sides therefore see the same history even where bf16 rounding
+    would pick another token on a near tie."""
+    wl = synth.get_config("qwen3_4b_bs1")
+    d = wl.dims
+    steps = 6
+    log("case qwen3_4b_bs1 decode loop: generating weights")
+    w_np = synth.make_weights(d, wl.seed)
+    ctx = wl.ctx[0]
+    g = GpuDraft(d, w_np, max_ctx=ctx + 16 * steps + 16, max_slots=1, max_batch=1)
+    hid0 = synth.make_hidden(d, wl.seed, 0, 0, ctx)
+    g.fuse([0], [ctx], hid0)
+    o = oracle.OracleDrafter(synth.weights_as_f32(w_np), d)
+    o.fuse(0, synth.as_f32(hid0))
+    del hid0
+    anchor = int(synth.make_anchors(d, wl.seed, 1)[0])
+    taus = []
+    for k in range(steps):
+        log(f"case qwen3_4b_bs1 decode loop: step {k}, ctx {ctx}")
+        ids, _, lg = g.draft([0], [anchor], top_k=1, logits=True)
+        ref = o.draft(0, anchor)["logits"]
+        ref_s = o.draft(0, anchor, store=_store(d))["logits"]
+        _compare_request(lg[0], ids[0], ref, d, 2e-2, f"4B loop step {k}", ref_s)
+        cand_o = oracle.topk(ref_s, 1)[0][:, 0]
+        m = synth.draw_first_mismatch("uniform", 1, d.B, wl.seed + 7 * k)
+        tgt = synth.make_targets(cand_o[None], m, d.V, wl.seed + 7 * k)
+        tau, bonus = oracle.accept(cand_o, tgt[0])
+        tau_g, bonus_g = g.accept(ids, 1, tgt)
+        assert (int(tau_g[0]), int(bonus_g[0])) == oracle.accept(ids[0, :, 0], tgt[0]), f"step {k}: scan"
+        # the committed rows: the anchor and the accepted candidates, whose
+        # verifier states are the synthetic rows at positions ctx .. ctx + tau - 1
+        hid = synth.make_hidden(d, wl.seed, 0, ctx, tau)
+        g.fuse([0], [tau], hid)
+        o.fuse(0, synth.as_f32(hid))
+        ctx += tau
+        taus.append(tau)
+        assert g.dr.slot_len(0) == ctx
+        anchor = int(bonus)
+    n = min(32, ctx)
+    for l in (0, d.N - 1):
+        kc, vc = g.read_cache(0, l, ctx - n, n)
+        assert rel_inf(kc, o.cache(0).K[l][:, ctx - n:ctx]) <= 2e-2, f"layer {l} K after the loop"
+        assert rel_inf(vc, o.cache(0).V[l][:, ctx - n:ctx]) <= 2e-2, f"layer {l} V after the loop"
+    log(f"case qwen3_4b_bs1 decode loop: taus {taus}")
+    g.close()
+
+
 def test_gpu_qwen3_8b_bs1():
     _full_size_case(synth.get_config("qwen3_8b_bs1"), [0], "qwen3_8b_bs1", "geometric")
 

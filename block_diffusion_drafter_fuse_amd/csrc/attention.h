@@ -215,7 +215,7 @@ __global__ __launch_bounds__(64 * (QF / QW), WPE) void attn_kernel(const AttnArg
         const int row = j * RPI + lane / KCH;
         const int chunk = (lane % KCH) ^ attn_kswz<NT, KCH>(row);
         const T* src = blk ? bkb + (size_t)min(row, a.B - 1) * kd : hb + (size_t)(k0 + row) * HD;
-        dma16(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
+        dma16<true>(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
       } else {
         constexpr int RPI = 1024 / SG::VRB;
         const int row = (j - SG::KI) * RPI + lane / VCH;  // tile-major V^T row: tile row / HD, d row % HD
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * (QF / QW), WPE) void attn_kernel(const AttnArg
         // the block has one V^T tile (B <= 16 keys); later tiles of its stage
         // re-read it (their keys are masked)
         const T* src = blk ? bvt + (size_t)d * a.BP : hb + a.kv_stride + ((size_t)(k0 / kVTile) * HD + row) * kVTile;
-        dma16(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
+        dma16<true>(reinterpret_cast<const char*>(src) + chunk * 16, base + j * 1024);
       }
     }
   };

@@ -98,6 +98,7 @@ constexpr int kRsMaxSplit = DFL_RS_MAX_SPLIT;  // K ranges of the row-streaming 
 constexpr int kRsSplitCost = DFL_RS_SPLIT_COST;  // stage-equivalents charged per extra K range
 constexpr int kLmFN = 1, kLmU = 8;     // few-token LM head fragments per wave, unroll
 constexpr int kTiledSlots = 256;       // concurrent tiled work-groups (one per CU)
+constexpr int kStreamMaxShare = 4;     // token tiles sharing a weight tile that still take streamed copies
 constexpr size_t kPartFloats = size_t(16) << 20;  // split-K partials (64 MB)
 constexpr int kCounters = 1 << 16;
 
@@ -346,7 +347,7 @@ void launch_tiled(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, con
   while (SK > 1 && ((size_t)tiles * SK * C::BM * C::BN > kPartFloats || tiles > kCounters - 64)) --SK;
   const int kps = ceil_div(nst, SK);
   SK = ceil_div(nst, kps);
-  const SplitK sk{SK, kps, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off)};
+  const SplitK sk{SK, kps, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off), MT <= kStreamMaxShare};
   const int nblocks = tiles * SK;
   const int lds = C::NBUF * ((ALO ? 2 : 1) * C::BM + C::BN) * 128;
   auto kern = gemm_tiled_kernel<T, C::BM, C::BN, C::WM, C::WN, C::NBUF, ALO, Epi>;
@@ -415,7 +416,8 @@ bool launch_skinny(dflash_ctx* c, const WOperand<T>& w, const AOperand<T>& a, co
       auto kern = gemv_rs_kernel<T, kRsNbuf, ALO, Epi::kPaired, Epi>;
       static std::atomic<uint64_t> lds_set{0};
       set_lds_limit(lds_set, reinterpret_cast<const void*>(kern), kRsLdsMax);
-      const RsSplit sp{rp.nsplit, rp.nst, rp.red2, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off)};
+      const RsSplit sp{rp.nsplit, rp.nst, rp.red2, c->wsp<float>(c->p.part_off), c->wsp<int>(c->p.ctr_off),
+                       mt <= kStreamMaxShare};
       hipLaunchKernelGGL(kern, dim3(rp.nwg, rp.nsplit * mt), dim3(1024), rp.lds, st, w, a, nrm, sp, epi, rp.tpw);
       return true;
     }

@@ -107,6 +107,7 @@ struct SplitK {
   int kps;      // K stages per split
   float* part;  // [tiles][SK][waves][FM * FN * 256]
   int* ctr;     // [tiles] tickets, zero between launches (reset by the last arriver)
+  int wstream;  // copy weights with the non-temporal hint (few token tiles share each weight tile)
 };
 
 // ---------------------------------------------------------------- helpers

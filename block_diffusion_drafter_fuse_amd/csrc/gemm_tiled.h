@@ -32,11 +32,21 @@ typedef __attribute__((address_space(3))) void* lds_dst_t;
 // assembly so that the compiler does not put a full vmcnt(0) in front of every
 // LDS read that might alias a copy still in flight, which would serialise the
 // stage ring.  Nothing else in the kernels that use it keeps a value in m0.
+// STREAM: data that few work-groups read (the context K/V; weights shared by at
+// most kStreamMaxShare token tiles) is copied with the non-temporal hint, so
+// that lines read once do not hold the caches (attention at bs 32: 128 ->
+// 107 us per layer; the bs 1 step 0.86 -> 0.80 ms).  Activations, re-read by
+// many work-groups from L2, and weights shared by more token tiles (prefill)
+// are copied without it: there the hint cost re-reads.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(const void* g, char* wave_base) {
   const unsigned m0v = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_dst_t)wave_base);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory", "m0");
+  if constexpr (STREAM)
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(m0v) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0v) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -142,8 +152,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
     char* base = lds + buf * SBYTES + wave * 1024;
     const long ao = a_off(st);
     const long wo = (long)st * 128;
+    if (sk.wstream) {  // one uniform branch per stage, each copy sequence unrolled
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16(src[i] + (i < NIA ? ao : wo), base + i * NWV * 1024);
+      for (int i = 0; i < NI; ++i) {
+        if (i < NIA)
+          dma16(src[i] + ao, base + i * NWV * 1024);
+        else
+          dma16<true>(src[i] + wo, base + i * NWV * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) dma16(src[i] + (i < NIA ? ao : wo), base + i * NWV * 1024);
+    }
   };
 
   // Fragment read offsets within a stage: row r16 of a 16-row block, chunk kk*4+kg.

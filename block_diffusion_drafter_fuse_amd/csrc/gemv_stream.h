@@ -57,6 +57,7 @@ struct RsSplit {
   int red2;     // some K range is a single stage: two partial buffers
   float* part;  // [token blocks][ngroups][nsplit][256] tile sums
   int* ctr;     // [token blocks][ngroups] tickets, zero between launches
+  int wstream;  // copy weights with the non-temporal hint (few token blocks share them)
 };
 
 // NBUF: ring depth.  ALO: activations as hi + lo planes.  PAIR8: 8 + 8 row
@@ -120,7 +121,10 @@ __global__ __launch_bounds__(1024) void gemv_rs_kernel(const WOperand<T> w, cons
   const char* c_src = row_src(0);
   char* const c_dst = ring + wave * SB;
   auto issue = [&]() {
-    dma16(c_src + c_s * SB + (swz << 4), c_dst + c_buf * TILE);
+    if (sp.wstream)
+      dma16<true>(c_src + c_s * SB + (swz << 4), c_dst + c_buf * TILE);
+    else
+      dma16(c_src + c_s * SB + (swz << 4), c_dst + c_buf * TILE);
     c_buf = c_buf + 1 == NBUF ? 0 : c_buf + 1;
     if (++c_s == nst) {
       c_s = 0;

@@ -2,11 +2,13 @@
 + dflash_draft_block) against the float64 oracle.
 
 Workload: the selector configuration (tiny fp32 drafter, B 16), 16 requests
-with 64 context tokens (the two-launch form: corrections GEMM, then the tap
-mix), and 1, 3 or 4 requests (the one-launch form, B 16 and B 6), convolution
-weights from synth.make_conv_weights at all four sites of every layer.  Bars: logits rel <= 1e-4 (fp32), top-1 ids
-where the oracle's margin exceeds 0.05; bf16 at the Qwen3-4B shape: logits
-within 2e-2 of max |logit|.  An identity convolution (W = 0, kbase = (1, 0))
+with 64 context tokens, 5 requests (a partial last row tile) and 11 requests
+with B 6 — the many-row form: corrections GEMM on 64-token tiles with split
+K, then the tap-mix kernel — and 1, 3 or 4 requests (the few-row form, the
+tap mix in a GEMV epilogue, B 16 and B 6), convolution weights from synth.make_conv_weights at all four sites of
+every layer.  Bars: logits rel <= 1e-4 (fp32), top-1 ids where the oracle's
+margin exceeds 0.05; bf16 at the Qwen3-4B shape (2 requests: few rows; 5
+requests: many rows): logits within 2e-2 of max |logit|.  An identity convolution (W = 0, kbase = (1, 0))
 reproduces the plain draft, and detaching restores it bit for bit."""
 import dataclasses
 
@@ -89,6 +91,30 @@ def test_gpu_conv_few_rows_matches_oracle(bs, B):
     g.close()
 
 
+@pytest.mark.parametrize("bs,B", [(5, 16), (11, 6)])
+def test_gpu_conv_many_rows_ragged_matches_oracle(bs, B):
+    """More than 64 token rows take the many-row form: 80 rows leave the
+    last 64-token tile of the corrections GEMM part empty; with B = 6 (66
+    rows) blocks straddle its tiles and the tap mix reads left neighbours
+    across them."""
+    wl = synth.get_config("dflash2_select")
+    d = dataclasses.replace(wl.dims, B=B)
+    log(f"case dflash2 conv, many rows: bs {bs}, B {B}, rows {bs * B}")
+    g, o, w32, slots = _setup(d, wl.seed, bs, 40)
+    cw = synth.make_conv_weights(d, wl.seed)
+    g.dr.conv_attach(_dev_conv(cw))
+    cw32 = synth.conv_weights_as_f32(cw)
+    anchors = synth.make_anchors(d, wl.seed, bs)
+    ids, _, lg = g.draft(slots, anchors, top_k=1, logits=True)
+    for r in slots:
+        ref = ds.draft_block_conv(w32, d, o.cache(r), int(anchors[r]), cw32)["logits"]
+        err = rel_inf(lg[r], ref)
+        assert err <= 1e-4, f"req {r}: logits rel err {err}"
+        _, bad = check_top1(ids[r][:, 0], ref)
+        assert len(bad) == 0, f"req {r}: top-1 mismatch at {bad}"
+    g.close()
+
+
 def test_gpu_conv_identity_and_detach():
     wl = synth.get_config("dflash2_select")
     d = wl.dims
@@ -121,16 +147,20 @@ def test_gpu_conv_rejects_unsupported_width():
     g.close()
 
 
-def test_gpu_conv_bf16_qwen3_4b_shape():
+@pytest.mark.parametrize("bs", [2, 5])
+def test_gpu_conv_bf16_qwen3_4b_shape(bs):
+    """bf16 at the Qwen3-4B shape: 32 token rows (few-row form) and 80 rows
+    (many-row form, a part-empty last token tile; the first, middle and last
+    requests are compared)."""
     d = QWEN3_4B
-    log("case dflash2 conv, Qwen3-4B shape bf16")
-    g, o, w32, slots = _setup(d, 8, 2, 96)
+    log(f"case dflash2 conv, Qwen3-4B shape bf16, bs {bs}")
+    g, o, w32, slots = _setup(d, 8, bs, 96)
     cw = synth.make_conv_weights(d, 8)
     g.dr.conv_attach(_dev_conv(cw))
-    anchors = synth.make_anchors(d, 8, 2)
+    anchors = synth.make_anchors(d, 8, bs)
     ids, _, lg = g.draft(slots, anchors, top_k=1, logits=True)
     cw32 = synth.conv_weights_as_f32(cw)
-    for r in slots:
+    for r in sorted({slots[0], slots[len(slots) // 2], slots[-1]}):
         ref = ds.draft_block_conv(w32, d, o.cache(r), int(anchors[r]), cw32)["logits"]
         err = np.abs(lg[r] - ref).max() / np.abs(ref).max()
         assert err <= 2e-2, f"req {r}: logits err {err}"

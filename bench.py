@@ -872,8 +872,8 @@ def main():
         print(json.dumps(doc["kernels"], indent=1))
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the draft step shards by request across GPUs with no exchange; see DESIGN.md)",
+        print(f"bench.py: the library runs on one GPU per process; --gpus {args.gpus} is not supported "
+              "(the draft step would shard by request across GPUs with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     import torch

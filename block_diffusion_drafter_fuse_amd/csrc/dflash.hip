@@ -108,7 +108,10 @@ constexpr int kCounters = 1 << 16;
 // bitmask of devices already set (one per kernel instance).
 void set_lds_limit(std::atomic<uint64_t>& done, const void* kern, int bytes) {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);  // no bit to remember it by
+    return;
+  }
   const uint64_t bit = uint64_t(1) << dev;
   if (done.load(std::memory_order_acquire) & bit) return;
   (void)hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);

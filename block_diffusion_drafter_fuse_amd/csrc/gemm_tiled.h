@@ -267,14 +267,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
     if (tid == 0) *ticket = __hip_atomic_fetch_add(sk.ctr + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     if (*ticket != sk.SK - 1) return;
-    // the sum runs over every split in index order (the own partial is read
-    // back too), so the result does not depend on which split arrived last
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int x = 0; x < sk.SK; ++x) {
-      const float* px = pt + (size_t)x * (NWV * WTILE);
+    if (sk.SK == 2) {
+      // two splits: own + other is the same sum whichever arrived last
+      // (addition commutes), so only the other split's partial is read
+      const float* px = pt + (size_t)(1 - s) * (NWV * WTILE);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -283,6 +279,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
           for (int c = 0; c < 4; ++c)
             acc[i][j][c] += __hip_atomic_load(px + (i * FN + j) * 256 + c * 64 + lane, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      // the sum runs over every split in index order (the own partial is read
+      // back too), so the result does not depend on which split arrived last
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int x = 0; x < sk.SK; ++x) {
+        const float* px = pt + (size_t)x * (NWV * WTILE);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              acc[i][j][c] += __hip_atomic_load(px + (i * FN + j) * 256 + c * 64 + lane, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     if (tid == 0) __hip_atomic_store(sk.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

@@ -24,7 +24,8 @@
 //
 // K may be split over work-groups (grid.y = splits x token blocks): each split
 // publishes its tile sums with agent-scope stores, takes a ticket, and the
-// last one to arrive adds the splits in index order and runs the epilogue.
+// last one to arrive adds the splits in index order (with two splits, the
+// other one to its own) and runs the epilogue.
 //
 // Paired epilogues (RoPE, SwiGLU, the relay's beta/gamma) use tiles of 8 + 8
 // rows: rows 0-7 are features f0..f0+7 and rows 8-15 their partners
@@ -272,12 +273,20 @@ __global__ __launch_bounds__(1024) void gemv_rs_kernel(const WOperand<T> w, cons
         if (lane == 0) ticket = __hip_atomic_fetch_add(sp.ctr + ti, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ticket = __shfl(ticket, 0);
         if (ticket != sp.nsplit - 1) continue;
-        // the sum runs over every split in index order (the own one read back too)
-        v = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int x = 0; x < sp.nsplit; ++x)
+        if (sp.nsplit == 2) {
+          // own + other is the same sum whichever arrived last (addition commutes)
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            v[c] += __hip_atomic_load(pt + x * 256 + c * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v[c] += __hip_atomic_load(pt + (1 - ks_id) * 256 + c * 64 + lane, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          // the sum runs over every split in index order (the own one read back too)
+          v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int x = 0; x < sp.nsplit; ++x)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              v[c] += __hip_atomic_load(pt + x * 256 + c * 64 + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         if (lane == 0) __hip_atomic_store(sp.ctr + ti, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       epilogue(tl, v);

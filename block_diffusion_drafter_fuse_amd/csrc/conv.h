@@ -113,7 +113,14 @@ struct ConvMixArgs {
 __device__ __forceinline__ float conv_row_scale(const float* ssq, int m, int nslot, float inv_d, float eps) {
   const float* p = ssq + (size_t)m * nslot;
   float s = 0.f;
-  for (int i = threadIdx.x & 63; i < nslot; i += 64) s += p[i];
+  for (int i0 = threadIdx.x & 63; i0 < nslot; i0 += 64 * 8) {  // eight loads in flight, then the sums in order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i0 + 64 * u < nslot ? p[i0 + 64 * u] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + 64 * u < nslot) s += v[u];
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
   return 1.0f / sqrtf(s * inv_d + eps);

@@ -171,15 +171,44 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
 #pragma unroll
   for (int kk = 0; kk < KPS; ++kk) offk[kk] = r16 * 128 + (((kk * 4 + kg) ^ (r16 & 7)) << 4);
 
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nst) issue(st0 + p, p);
+
+  // Sum of squares of this thread's row of the folded RMSNorm (TPR threads
+  // per row, slots in a fixed order), read while the first stages are in
+  // flight, the loads four at a time: as a dependent loop after the stream
+  // it cost one memory round trip per 16-byte load at the end of every
+  // work-group.  The scale goes to LDS after the stream.
+  constexpr int NT = 64 * NWV;
+  // threads per row: the largest power of two with TPR * BM <= NT (at least 1)
+  constexpr int TPR = NT >= 8 * BM ? 8 : NT >= 4 * BM ? 4 : NT >= 2 * BM ? 2 : 1;
+  static_assert(NT / TPR >= BM, "one row per thread group");
+  const int srow_row = tid / TPR, srow_sub = tid % TPR;
+  float ssum = 0.f;
+  if (nrm.ssq) {
+    const int m = bm * BM + (srow_row < BM ? srow_row : 0);
+    const float* p = nrm.ssq + (size_t)a.row(m < a.M ? m : a.M - 1) * nrm.nslot;
+    for (int j0 = srow_sub * 4; j0 < nrm.nslot; j0 += TPR * 4 * 4) {
+      f32x4_t v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = j0 + u * TPR * 4;
+        v[u] = j < nrm.nslot ? *reinterpret_cast<const f32x4_t*>(p + j) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (j0 + u * TPR * 4 < nrm.nslot) ssum += (v[u][0] + v[u][1]) + (v[u][2] + v[u][3]);
+    }
+#pragma unroll
+    for (int o = 1; o < TPR; o <<= 1) ssum += __shfl_xor(ssum, o);
+  }
+
   f32x4_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int p = 0; p < NBUF - 1; ++p)
-    if (p < nst) issue(st0 + p, p);
 
   int buf = 0;
   for (int k = 0; k < nst; ++k) {
@@ -301,30 +330,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(const WOperand
     if (tid == 0) __hip_atomic_store(sk.ctr + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // Row scales of the folded RMSNorm, once per work-group: the BM rows' sums
-  // of squares are reduced by TPR threads per row (fixed order) into LDS (the
+  // Row scales of the folded RMSNorm, once per work-group: the sums of
+  // squares reduced before the stream become the BM rows' scales in LDS (the
   // ring is idle after the stream; a barrier first lets every wave finish
   // its last fragment reads).  Every wave of the work-group then reads its
   // rows' scales from LDS instead of re-reducing the slots per fragment.
   float* srow = reinterpret_cast<float*>(lds + 256);
   if (nrm.ssq) {
-    constexpr int NT = 64 * NWV;
-    // threads per row: the largest power of two with TPR * BM <= NT (at least 1)
-    constexpr int TPR = NT >= 8 * BM ? 8 : NT >= 4 * BM ? 4 : NT >= 2 * BM ? 2 : 1;
     __syncthreads();
-    for (int r0 = 0; r0 < BM; r0 += NT / TPR) {
-      const int row = r0 + tid / TPR, sub = tid % TPR;
-      const int m = bm * BM + row;
-      const float* p = nrm.ssq + (size_t)a.row(m < a.M ? m : a.M - 1) * nrm.nslot;
-      float ssum = 0.f;
-      for (int j = sub * 4; j < nrm.nslot; j += TPR * 4) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(p + j);
-        ssum += (v[0] + v[1]) + (v[2] + v[3]);
-      }
-#pragma unroll
-      for (int o = 1; o < TPR; o <<= 1) ssum += __shfl_xor(ssum, o);
-      if (sub == 0 && row < BM) srow[row] = 1.0f / sqrtf(ssum * nrm.inv_d + nrm.eps);
-    }
+    if (srow_sub == 0 && srow_row < BM) srow[srow_row] = 1.0f / sqrtf(ssum * nrm.inv_d + nrm.eps);
     __syncthreads();
   }
 

@@ -290,11 +290,24 @@ __global__ __launch_bounds__(1024) void top1_merge_kernel(const float* part_v, c
   const int* pi = part_i + (size_t)m * nchunk;
   float bv = -INFINITY;
   int bi = 0x7fffffff;
-  for (int c = tid; c < nchunk; c += 1024)
-    if (tk_better(pv[c], pi[c], bv, bi)) {
-      bv = pv[c];
-      bi = pi[c];
+  // eight entries loaded at a time (one memory round trip per eight, not per
+  // entry); the winner does not depend on the order of the comparisons
+  for (int c0 = tid; c0 < nchunk; c0 += 1024 * 8) {
+    float v[8];
+    int ix[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * 1024;
+      v[u] = c < nchunk ? pv[c] : -INFINITY;
+      ix[u] = c < nchunk ? pi[c] : 0x7fffffff;
     }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (tk_better(v[u], ix[u], bv, bi)) {
+        bv = v[u];
+        bi = ix[u];
+      }
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float v2 = __shfl_xor(bv, o);
